@@ -1,0 +1,179 @@
+/*
+ * oracle.c -- plain fp64 CPU reference of the block-sparse linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The product path never
+ * calls it, and it shares no code, header or table with the HIP library.
+ *
+ * What is computed (pytorch/ao sparsity README, workflow section: sparse and
+ * dense matmul with the zero-filled weight are numerically equivalent; Table
+ * 4.1: BSR stores dense blocks plus their block coordinates, CSR/CSC store an
+ * index pointer, indices and data):
+ *
+ *   W~ [N,K] is zero except block (r, col_idx[i]) = V[i] for i in
+ *   row_ptr[r] .. row_ptr[r+1]-1, with V[i][p][q] = W~[r*b+p][col_idx[i]*b+q].
+ *
+ *   forward       Y  = X . W~^T + 1 . bias^T                 (nn.Linear layout)
+ *   input grad    dX = dY . W~
+ *   weight grad   dV[i] = block (r, col_idx[i]) of dY^T . X  (the dense weight
+ *                 gradient masked to the pattern, "dW' = dW (Mask)" of the
+ *                 README's out-of-place mask update)
+ *   bias grad     db = sum over rows of dY
+ *
+ * Alongside every output element o the oracle returns S(o), the sum of the
+ * absolute values of the products summed into o (plus |bias| where a bias is
+ * added). The tolerance of a bf16 result g is |g - o| <= 4e-3 * S(o).
+ *
+ * Every sum runs in a fixed order (stated per function), so the result does
+ * not depend on the OpenMP thread count: threads only split independent
+ * outputs (rows m, or blocks i).
+ *
+ * All matrices are dense row-major fp64. M is the number of rows of X / dY.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Forward. For each output Y[m][r*b+p]: sum over the blocks i of row r in
+ * ascending i, then over q ascending, of X[m][col_idx[i]*b+q] * V[i][p][q];
+ * then + bias. Empty block rows give bias (or 0). S may be NULL. */
+void oracle_fwd(int64_t M, int32_t N, int32_t K, int32_t b,
+                const int32_t *row_ptr, const int32_t *col_idx,
+                const double *X, const double *V, const double *bias,
+                double *Y, double *S)
+{
+    const int32_t R = N / b;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const double *x = X + m * (int64_t)K;
+        for (int32_t r = 0; r < R; ++r) {
+            for (int32_t p = 0; p < b; ++p) {
+                double acc = 0.0, s = 0.0;
+                for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
+                    const double *v = V + ((int64_t)i * b + p) * b;
+                    const double *xc = x + (int64_t)col_idx[i] * b;
+                    for (int32_t q = 0; q < b; ++q) {
+                        double t = xc[q] * v[q];
+                        acc += t;
+                        s += fabs(t);
+                    }
+                }
+                const int64_t n = (int64_t)r * b + p;
+                if (bias) {
+                    acc += bias[n];
+                    s += fabs(bias[n]);
+                }
+                Y[m * (int64_t)N + n] = acc;
+                if (S) S[m * (int64_t)N + n] = s;
+            }
+        }
+    }
+}
+
+/* Input gradient, walking the CSR order on purpose (not the transposed
+ * metadata): dX[m][col_idx[i]*b+q] += dY[m][r*b+p] * V[i][p][q] over rows r
+ * ascending, blocks i ascending, p ascending. Columns of dX that no block
+ * touches stay 0. S may be NULL. */
+void oracle_dx(int64_t M, int32_t N, int32_t K, int32_t b,
+               const int32_t *row_ptr, const int32_t *col_idx,
+               const double *dY, const double *V,
+               double *dX, double *S)
+{
+    const int32_t R = N / b;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const double *dy = dY + m * (int64_t)N;
+        double *dx = dX + m * (int64_t)K;
+        double *s = S ? S + m * (int64_t)K : NULL;
+        for (int32_t k = 0; k < K; ++k) {
+            dx[k] = 0.0;
+            if (s) s[k] = 0.0;
+        }
+        for (int32_t r = 0; r < R; ++r) {
+            for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
+                const int64_t c0 = (int64_t)col_idx[i] * b;
+                for (int32_t p = 0; p < b; ++p) {
+                    const double g = dy[(int64_t)r * b + p];
+                    const double *v = V + ((int64_t)i * b + p) * b;
+                    for (int32_t q = 0; q < b; ++q) {
+                        double t = g * v[q];
+                        dx[c0 + q] += t;
+                        if (s) s[c0 + q] += fabs(t);
+                    }
+                }
+            }
+        }
+    }
+}
+
+/* Weight gradient on the pattern only. For block i of row r, column c:
+ * dV[i][p][q] = sum over m ascending of dY[m][r*b+p] * X[m][c*b+q].
+ * `blocks` lists which block indices to compute (NULL = all nnzb, in order);
+ * output slot j of dV (and S) holds block blocks[j]. */
+void oracle_dw(int64_t M, int32_t N, int32_t K, int32_t b,
+               const int32_t *row_ptr, const int32_t *col_idx,
+               const double *dY, const double *X,
+               const int32_t *blocks, int32_t nblocks,
+               double *dV, double *S)
+{
+    const int32_t R = N / b;
+    const int32_t nnzb = row_ptr[R];
+    if (!blocks) nblocks = nnzb;
+    /* row of every block, from the row pointer */
+    int32_t *row_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nnzb > 0 ? nnzb : 1));
+    for (int32_t r = 0; r < R; ++r)
+        for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) row_of[i] = r;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t j = 0; j < nblocks; ++j) {
+        const int32_t i = blocks ? blocks[j] : j;
+        const int64_t n0 = (int64_t)row_of[i] * b;
+        const int64_t k0 = (int64_t)col_idx[i] * b;
+        double *acc = dV + (int64_t)j * b * b;
+        double *s = S ? S + (int64_t)j * b * b : NULL;
+        for (int32_t e = 0; e < b * b; ++e) {
+            acc[e] = 0.0;
+            if (s) s[e] = 0.0;
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            const double *dy = dY + m * (int64_t)N + n0;
+            const double *x = X + m * (int64_t)K + k0;
+            for (int32_t p = 0; p < b; ++p) {
+                for (int32_t q = 0; q < b; ++q) {
+                    double t = dy[p] * x[q];
+                    acc[p * b + q] += t;
+                    if (s) s[p * b + q] += fabs(t);
+                }
+            }
+        }
+    }
+    free(row_of);
+}
+
+/* Bias gradient: db[n] = sum over m ascending of dY[m][n]; S = sum |dY|. */
+void oracle_db(int64_t M, int32_t N, const double *dY, double *db, double *S)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t n = 0; n < N; ++n) {
+        double acc = 0.0, s = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            acc += dY[m * (int64_t)N + n];
+            s += fabs(dY[m * (int64_t)N + n]);
+        }
+        db[n] = acc;
+        if (S) S[n] = s;
+    }
+}
+
+/* Threads the OpenMP runtime will use for the loops above. */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
