@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse linear layer (forward + input grad + weight grad) on one MI355X.
+
+One step = one pass of the whole hot path over one batch: bsr_linear_fwd, then
+bsr_linear_bwd_input and bsr_linear_bwd_weight (the ops the workload lists), on seeded
+synthetic bf16 inputs already resident in HBM. Useful FLOPs per op are 2*M*b^2*nnzb (work
+on zero blocks is never counted).
+
+Default workload: BERT-base FFN-up, X[4096,768] -> Y[4096,3072], 32x32 blocks at density
+0.25. By default every step uses the next of several distinct buffer sets, together at least
+512 MB (twice the 256 MB Infinity Cache), so each step reads its inputs from HBM; --warm
+reuses one set.
+
+Prints ONE JSON line. Extra legs: the same kernels on the density-1.0 pattern of the same
+shape, hipBLASLt dense (torch.matmul) as context, and the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+METRIC = "useful TFLOP/s (2·M·b²·nnzb) fwd+bwd and % bf16 MFMA peak; GB/s at small M"
+ROTATE_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def op_bytes(w, nnzb: int, op: str, bias: bool) -> int:
+    """Algorithmic bytes of one op: each input read once, each output written once, metadata."""
+    M, N, K, b = w.M, w.N, w.K, w.b
+    R, C = N // b, K // b
+    act_x, act_y, vals = 2 * M * K, 2 * M * N, 2 * nnzb * b * b
+    csr = 4 * (R + 1) + 4 * nnzb
+    csc = 4 * (C + 1) + 8 * nnzb
+    if op == "fwd":
+        return act_x + vals + act_y + csr + (2 * N if bias else 0)
+    if op == "dx":
+        return act_y + vals + act_x + csc
+    if op == "dw":
+        return act_y + act_x + vals + csr
+    raise ValueError(op)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _sleep_cycles_per_ms() -> float:
+    """Rate of the spin kernel torch.cuda._sleep, measured with HIP events."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    a.record()
+    torch.cuda._sleep(2_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(1e-3, a.elapsed_time(b))
+
+
+def time_ops(run_step, nsteps: int, warmup: int, ops, hold_ms: float):
+    """Per-op GPU durations with HIP events on the launch stream (torch's current stream).
+
+    A spin kernel holds the GPU while the host enqueues all timed steps, so back-to-back
+    kernels run with no host gaps and each event pair brackets GPU execution only (what
+    rocprofv3's kernel trace reports). Returns (GPU ms per step, {op: avg ms}, enqueue s)."""
+    import torch
+    for k in range(warmup):
+        run_step(k, None)
+    torch.cuda.synchronize()
+    evs = {op: [] for op in ops}
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(hold_ms * _CYC_PER_MS))
+    first.record()
+    t = time.perf_counter()
+    for k in range(nsteps):
+        run_step(warmup + k, evs)
+    last.record()
+    enqueue_s = time.perf_counter() - t
+    torch.cuda.synchronize()
+    step_ms = first.elapsed_time(last) / nsteps
+    op_ms = {op: sum(a.elapsed_time(b) for a, b in evs[op]) / max(1, len(evs[op])) for op in ops}
+    if enqueue_s * 1e3 > hold_ms:
+        log(f"[bench] warning: host enqueue took {enqueue_s * 1e3:.1f} ms > hold {hold_ms:.1f} ms; "
+            "op times may include host gaps")
+    return step_ms, op_ms, enqueue_s
+
+
+def time_graph(run_step, nsets: int, reps: int):
+    """Whole-step throughput: the steps over all buffer sets captured once as a HIP graph,
+    replayed `reps` times; wall clock and HIP events bracketed by synchronize."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(nsets):            # one eager pass on the capture stream first
+            run_step(k, None)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for k in range(nsets):
+            run_step(k, None)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    steps = reps * nsets
+    return a.elapsed_time(b) / steps, wall / steps * 1e3, steps
+
+
+_CYC_PER_MS = 1.0
+
+
+def build_sets(w, host, nsets: int, dev):
+    import torch
+    from sparse_gemm_amd import binding
+    sets = []
+    for k in range(nsets):
+        s = {}
+        for key in ("X", "V", "dY"):
+            if host.get(key) is not None:
+                s[key] = host[key].to(dev) if k == 0 else host[key].to(dev).clone()
+        s["bias"] = host["bias"].to(dev) if host.get("bias") is not None else None
+        s["Y"] = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        if "dx" in w.ops:
+            s["dX"] = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+        if "dw" in w.ops:
+            s["dV"] = torch.empty_like(s["V"])
+        sets.append(s)
+    return sets
+
+
+def make_runner(p, w, sets, ws):
+    import torch
+    from sparse_gemm_amd import binding
+
+    def run_step(k, evs):
+        s = sets[k % len(sets)]
+        for op in w.ops:
+            if evs is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+            if op == "fwd":
+                binding.linear_fwd(p, s["X"], s["V"], s["bias"], out=s["Y"])
+            elif op == "dx":
+                binding.linear_bwd_input(p, s["dY"], s["V"], out=s["dX"])
+            elif op == "dw":
+                binding.linear_bwd_weight(p, s["dY"], s["X"], out=s["dV"], workspace=ws)
+            if evs is not None:
+                b.record()
+                evs[op].append((a, b))
+    return run_step
+
+
+def cpu_baseline(w, host, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, on the same workload and the host's cores."""
+    import oracle
+    from oracle import meta
+    md = meta.scan(host["mask"])
+    nnzb = md["nnzb"]
+    # bounded sample: the first rows of the workload, sized to about `seconds` of CPU work
+    F_row = 2.0 * w.b * w.b * nnzb * len(w.ops)
+    X64 = oracle._f64(host["X"])
+    dY64 = oracle._f64(host["dY"]) if host.get("dY") is not None else None
+    probe_rows = min(w.M, 64)
+    t = time.perf_counter()
+    _run_oracle(w, md, host, X64, dY64, probe_rows)
+    per_row = max(1e-6, (time.perf_counter() - t) / probe_rows)
+    rows = int(min(w.M, max(probe_rows, seconds / per_row)))
+    reps = max(1, int(round(seconds / (per_row * rows)))) if rows == w.M else 1
+    t = time.perf_counter()
+    for _ in range(reps):
+        _run_oracle(w, md, host, X64, dY64, rows)
+    dt = time.perf_counter() - t
+    flops = F_row * rows * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{reps} pass(es) over the first {rows} of {w.M} rows of the workload, ops "
+                      f"{'+'.join(w.ops)}, fp64 with no tolerance sums, {dt:.1f} s wall, "
+                      f"{flops / dt / 1e9:.2f} GFLOP/s",
+            "cpu_model": cpu_model(), "seconds": dt}
+
+
+def _run_oracle(w, md, host, X64, dY64, rows):
+    import oracle
+    for op in w.ops:
+        if op == "fwd":
+            oracle.fwd(X64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.N, w.b,
+                       bias=host["bias"], want_s=False)
+        elif op == "dx":
+            oracle.dx(dY64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.K, w.b, want_s=False)
+        elif op == "dw":
+            oracle.dw(dY64[:rows], X64[:rows], md["row_ptr"], md["col_idx"], w.b, want_s=False)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="reference workload 1..5 (default 2)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the density-1.0 and hipBLASLt legs")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_gemm_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}; generating inputs")
+    host = synth.make_inputs(w, args.seed)
+    nnzb = int(host["mask"].sum())
+    p = binding.Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    F = 2.0 * w.M * w.b * w.b * nnzb
+    set_bytes = sum(op_bytes(w, nnzb, op, w.bias) for op in w.ops)
+    nsets = 1 if args.warm else max(1, -(-ROTATE_BYTES // max(1, set_bytes)))
+    sets = build_sets(w, host, nsets, dev)
+    ws_bytes = binding.bwd_weight_workspace_bytes(p, w.M) if "dw" in w.ops else 0
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    log(f"[bench] nnzb {nnzb}, {nsets} buffer set(s), timing {args.steps} steps after {args.warmup} warmup")
+    global _CYC_PER_MS
+    _CYC_PER_MS = _sleep_cycles_per_ms()
+    run = make_runner(p, w, sets, ws)
+    gpu_step_ms, op_ms, enq = time_ops(run, args.steps, args.warmup, w.ops, hold_ms=50.0 + 2.0 * args.steps)
+    reps = max(1, -(-args.steps // nsets))
+    step_ms, wall_ms, nsteps_graph = time_graph(run, nsets, reps)
+    log(f"[bench] graph step {step_ms * 1e3:.1f} us (wall {wall_ms * 1e3:.1f} us); eager GPU step "
+        f"{gpu_step_ms * 1e3:.1f} us; " + ", ".join(f"{o} {t * 1e3:.1f} us" for o, t in op_ms.items()))
+
+    nops = len(w.ops)
+    value = nops * F / (step_ms * 1e-3) / 1e12
+    per_op = {}
+    for op in w.ops:
+        t = op_ms[op] * 1e-3
+        by = op_bytes(w, nnzb, op, w.bias)
+        t_roof = max(F / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        per_op[op] = {"us": op_ms[op] * 1e3, "tflops": F / t / 1e12, "pct_mfma_peak": 100 * F / t / 1e12 / PEAK_BF16_TFLOPS,
+                      "gbs": by / t / 1e9, "pct_hbm_peak": 100 * by / t / 1e9 / PEAK_HBM_GBS, "bytes": by,
+                      "pct_roofline": 100 * t_roof / t}
+    dom = max(w.ops, key=lambda o: op_ms[o])
+    dom_bytes = op_bytes(w, nnzb, dom, w.bias)
+    t_dom = op_ms[dom] * 1e-3
+    ai = F / dom_bytes
+    if ai < RIDGE:
+        roofline = {"bound": "hbm", "achieved": dom_bytes / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roofline = {"bound": "mfma", "achieved": F / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+    roofline["traffic"] = None
+    roofline["kernel"] = {"fwd": "bsr_linear_fwd", "dx": "bsr_linear_bwd_input", "dw": "bsr_linear_bwd_weight"}[dom]
+    roofline["per_launch"] = {"flops": F, "algorithmic_bytes": dom_bytes, "avg_us": op_ms[dom] * 1e3}
+
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": nsteps_graph,
+           "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02) blocks)",
+           "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.b, "density": w.density,
+                      "nnzb": nnzb, "pattern": w.pattern, "ops": "+".join(w.ops),
+                      "buffers": "warm (1 set)" if nsets == 1 else f"cold ({nsets} rotated sets)",
+                      "pattern_sha256": synth.mask_digest(host["mask"]), "rows": synth.row_histogram(host["mask"])},
+           "pct_bf16_mfma_peak": 100 * value / PEAK_BF16_TFLOPS,
+           "ops": per_op, "roofline": roofline,
+           "timing": {"ms_per_step": "HIP-graph replay of the step over the rotated buffer sets, HIP events",
+                      "graph_wall_ms_per_step": wall_ms, "eager_gpu_ms_per_step": gpu_step_ms,
+                      "eager_host_enqueue_ms_per_step": enq * 1e3 / args.steps,
+                      "ops": "HIP events around each call, host queue pre-filled behind a spin kernel"}}
+
+    # the same step with one buffer set (cache-warm), for reference
+    warm_ms, _, _ = time_graph(make_runner(p, w, sets[:1], ws), 1, max(5, args.steps))
+    out["warm_ms_per_step"] = warm_ms
+
+    if not args.no_extras:
+        # the same kernels on the density-1.0 pattern of the same shape, same buffer rotation
+        full = np.ones_like(host["mask"])
+        host_d = dict(host)
+        host_d["mask"] = full
+        host_d["V"] = synth.block_values(int(full.sum()), w.b, args.seed)
+        pd = binding.Pattern.from_mask(full, w.N, w.K, w.b)
+        bytes_d = sum(op_bytes(w, int(full.sum()), op, w.bias) for op in w.ops)
+        nsets_d = 1 if args.warm else max(1, -(-ROTATE_BYTES // bytes_d))
+        del sets
+        sets_d = build_sets(w, host_d, nsets_d, dev)
+        wsd_b = binding.bwd_weight_workspace_bytes(pd, w.M) if "dw" in w.ops else 0
+        wsd = torch.empty((wsd_b,), dtype=torch.uint8, device=dev) if wsd_b else None
+        run_d = make_runner(pd, w, sets_d, wsd)
+        _, d_ops, _ = time_ops(run_d, max(10, args.steps // 2), 3, w.ops, hold_ms=60.0)
+        d_ms, _, _ = time_graph(run_d, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
+        out["density_1.0_same_kernels"] = {"ms_per_step": d_ms, "speedup_of_sparse": d_ms / step_ms,
+                                           "ops_us": {o: t * 1e3 for o, t in d_ops.items()},
+                                           "buffers": f"{nsets_d} rotated sets" if nsets_d > 1 else "warm"}
+
+        # hipBLASLt dense GEMMs of the same shapes (torch.matmul; context only)
+        dense_w = [s_["V"].new_empty((w.N, w.K)).normal_() for s_ in sets_d]
+
+        def dense_step(k, evs):
+            s_ = sets_d[k % len(sets_d)]
+            Wd = dense_w[k % len(sets_d)]
+            torch.matmul(s_["X"], Wd.t(), out=s_["Y"])
+            if "dx" in w.ops:
+                torch.matmul(s_["dY"], Wd, out=s_["dX"])
+            if "dw" in w.ops:
+                torch.matmul(s_["dY"].t(), s_["X"])
+        for k in range(3):
+            dense_step(k, None)
+        h_ms, _, _ = time_graph(dense_step, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
+        out["hipblaslt_dense_context"] = {"ms_per_step": h_ms, "speedup_of_sparse": h_ms / step_ms}
+        del sets_d, dense_w, pd
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+"""Python face of the C ABI: a Pattern handle and the three compute calls on torch tensors.
+
+PyTorch supplies device memory and the current stream; the arithmetic runs in the
+library's HIP kernels. Names follow include/bsr_linear.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch  # imported before the library so the process maps a single HIP runtime
+
+from . import _lib
+
+
+def _single_hip_runtime() -> None:
+    """Refuse to run with two different libamdhip64 images mapped (two HIP runtimes)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return
+    import os
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped in this process: {sorted(real)}")
+
+
+_checked = None
+
+
+def lib() -> ctypes.CDLL:
+    global _checked
+    if _checked is None:
+        L = _lib.load()
+        _single_hip_runtime()
+        _checked = L
+    return _checked
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+class Pattern:
+    """A block pattern owned by the library: CSR, transposed CSC + perm, and work lists.
+
+    Created from a block mask [N/b, K/b] (nonzero = kept block) or from CSR arrays. With
+    upload=True (default) the metadata is copied to the current device; with False the
+    pattern is host-only (export / info only)."""
+
+    def __init__(self, handle: ctypes.c_void_p, upload: bool, device: Optional[int]):
+        self._h = handle
+        self.uploaded = upload
+        self.device = device
+        N, K, b, nnzb = (ctypes.c_int32() for _ in range(4))
+        _lib.check(lib().bsr_pattern_info(self._h, ctypes.byref(N), ctypes.byref(K), ctypes.byref(b),
+                                          ctypes.byref(nnzb)), "bsr_pattern_info")
+        self.N, self.K, self.b, self.nnzb = N.value, K.value, b.value, nnzb.value
+        self.R, self.C = self.N // self.b, self.K // self.b
+
+    @staticmethod
+    def _device(upload: bool) -> Optional[int]:
+        if not upload:
+            return None
+        if not torch.cuda.is_available():
+            raise RuntimeError("uploading a pattern needs a GPU")
+        torch.cuda.init()
+        return torch.cuda.current_device()
+
+    @classmethod
+    def from_mask(cls, mask, N: int, K: int, b: int, upload: bool = True) -> "Pattern":
+        m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        if m.shape != (N // b, K // b) or N % b or K % b:
+            raise ValueError(f"mask shape {m.shape} does not match N={N}, K={K}, b={b}")
+        dev = cls._device(upload)
+        h = ctypes.c_void_p()
+        _lib.check(lib().bsr_pattern_create_from_mask(N, K, b, m.ctypes.data_as(ctypes.c_void_p), int(upload),
+                                                      ctypes.byref(h)), "bsr_pattern_create_from_mask")
+        return cls(h, upload, dev)
+
+    @classmethod
+    def from_csr(cls, N: int, K: int, b: int, row_ptr, col_idx, upload: bool = True) -> "Pattern":
+        rp, ci = _i32(row_ptr), _i32(col_idx)
+        dev = cls._device(upload)
+        h = ctypes.c_void_p()
+        _lib.check(lib().bsr_pattern_create_from_csr(N, K, b, int(ci.size), rp.ctypes.data_as(ctypes.c_void_p),
+                                                     ci.ctypes.data_as(ctypes.c_void_p) if ci.size else None,
+                                                     int(upload), ctypes.byref(h)), "bsr_pattern_create_from_csr")
+        return cls(h, upload, dev)
+
+    def export(self) -> dict:
+        out = dict(row_ptr=np.empty(self.R + 1, np.int32), col_idx=np.empty(self.nnzb, np.int32),
+                   col_ptr=np.empty(self.C + 1, np.int32), row_idx=np.empty(self.nnzb, np.int32),
+                   perm=np.empty(self.nnzb, np.int32))
+        p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+        _lib.check(lib().bsr_pattern_export(self._h, p(out["row_ptr"]), p(out["col_idx"]), p(out["col_ptr"]),
+                                            p(out["row_idx"]), p(out["perm"])), "bsr_pattern_export")
+        return out
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            if self.uploaded and torch.cuda.is_available():
+                torch.cuda.synchronize(self.device)  # no queued kernel may still read the metadata
+            _lib.load().bsr_pattern_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _check_tensor(t: torch.Tensor, name: str, shape, device) -> None:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda or t.device.index != device:
+        raise ValueError(f"{name} must be on cuda:{device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: int):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def linear_fwd(p: Pattern, X: torch.Tensor, V: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W~^T + bias via bsr_linear_fwd; X [M, K], V [nnzb, b, b], bias [N] or None."""
+    M = X.shape[0]
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_tensor(V, "V", (p.nnzb, p.b, p.b), p.device)
+    if bias is not None:
+        _check_tensor(bias, "bias", (p.N,), p.device)
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, p.N), p.device)
+    _lib.check(lib().bsr_linear_fwd(p.handle, _ptr(X), M, _ptr(V), _ptr(bias), _ptr(out), _stream(p.device)),
+               "bsr_linear_fwd")
+    return out
+
+
+def linear_bwd_input(p: Pattern, dY: torch.Tensor, V: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = dY . W~ via bsr_linear_bwd_input; dY [M, N]."""
+    M = dY.shape[0]
+    _check_tensor(dY, "dY", (M, p.N), p.device)
+    _check_tensor(V, "V", (p.nnzb, p.b, p.b), p.device)
+    if out is None:
+        out = torch.empty((M, p.K), dtype=torch.bfloat16, device=dY.device)
+    _check_tensor(out, "out", (M, p.K), p.device)
+    _lib.check(lib().bsr_linear_bwd_input(p.handle, _ptr(dY), M, _ptr(V), _ptr(out), _stream(p.device)),
+               "bsr_linear_bwd_input")
+    return out
+
+
+def bwd_weight_workspace_bytes(p: Pattern, M: int) -> int:
+    return int(lib().bsr_linear_bwd_weight_workspace(p.handle, int(M)))
+
+
+def linear_bwd_weight(p: Pattern, dY: torch.Tensor, X: torch.Tensor, want_dbias: bool = False,
+                      out: Optional[torch.Tensor] = None, dbias: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """(dV, dbias or None) via bsr_linear_bwd_weight; dV [nnzb, b, b] on the pattern only."""
+    M = dY.shape[0]
+    _check_tensor(dY, "dY", (M, p.N), p.device)
+    _check_tensor(X, "X", (M, p.K), p.device)
+    if out is None:
+        out = torch.empty((p.nnzb, p.b, p.b), dtype=torch.bfloat16, device=dY.device)
+    _check_tensor(out, "out", (p.nnzb, p.b, p.b), p.device)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((p.N,), dtype=torch.bfloat16, device=dY.device)
+    if dbias is not None:
+        _check_tensor(dbias, "dbias", (p.N,), p.device)
+    need = bwd_weight_workspace_bytes(p, M)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dY.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.check(lib().bsr_linear_bwd_weight(p.handle, _ptr(dY), _ptr(X), M, _ptr(out), _ptr(dbias), _ptr(workspace),
+                                           ws_bytes, _stream(p.device)), "bsr_linear_bwd_weight")
+    return out, dbias

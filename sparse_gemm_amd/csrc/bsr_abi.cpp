@@ -1,0 +1,297 @@
+// bsr_abi.cpp -- the extern "C" entry points: argument checks, pattern life cycle, dispatch.
+// Nothing is enqueued before every argument has been checked; no C++ exception escapes.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "bsr_internal.hpp"
+
+namespace bsr {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int32_t check_shape(int32_t N, int32_t K, int32_t b) {
+    if (b != 32 && b != 64) return fail(BSR_ERR_UNSUPPORTED, "block size must be 32 or 64, got " + std::to_string(b));
+    if (N <= 0 || K <= 0) return fail(BSR_ERR_INVALID_ARG, "N and K must be positive");
+    if (N % b || K % b) return fail(BSR_ERR_INVALID_ARG, "N and K must be multiples of the block size");
+    return BSR_OK;
+}
+
+// Copies every metadata array to the current device in one allocation.
+int32_t upload(bsr_pattern &p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BSR_ERR_HIP, "hipGetDevice failed (no usable GPU?)");
+    struct Part {
+        const std::vector<int32_t> *v;
+        const int32_t **dst;
+    };
+    DeviceMeta &d = p.dev;
+    const Part parts[] = {
+        {&p.row_ptr, &d.row_ptr},         {&p.col_idx, &d.col_idx},       {&p.col_ptr, &d.col_ptr},
+        {&p.row_idx, &d.row_idx},         {&p.perm, &d.perm},             {&p.blk_row, &d.blk_row},
+        {&p.fwd.order, &d.f_order},       {&p.fwd.step_ptr, &d.f_step_ptr}, {&p.fwd.out, &d.f_out},
+        {&p.fwd.step_in, &d.f_step_in},   {&p.fwd.step_blk, &d.f_step_blk},
+        {&p.bwd.order, &d.t_order},       {&p.bwd.step_ptr, &d.t_step_ptr}, {&p.bwd.out, &d.t_out},
+        {&p.bwd.step_in, &d.t_step_in},   {&p.bwd.step_blk, &d.t_step_blk},
+        {&p.rows_by_nnz, &d.rows_by_nnz},
+    };
+    size_t total = 0;
+    for (const Part &q : parts) total += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);
+    if (total == 0) total = 256;
+    std::vector<char> host(total, 0);
+    size_t off = 0;
+    std::vector<size_t> offs;
+    for (const Part &q : parts) {
+        offs.push_back(off);
+        if (!q.v->empty()) std::memcpy(host.data() + off, q.v->data(), q.v->size() * sizeof(int32_t));
+        off += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);
+    }
+    void *base = nullptr;
+    hipError_t e = hipMalloc(&base, total);
+    if (e == hipErrorOutOfMemory) return fail(BSR_ERR_OUT_OF_MEMORY, "hipMalloc of pattern metadata failed");
+    if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("hipMalloc: ") + hipGetErrorString(e));
+    e = hipMemcpy(base, host.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        return fail(BSR_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    }
+    for (size_t k = 0; k < sizeof(parts) / sizeof(parts[0]); ++k)
+        *parts[k].dst = reinterpret_cast<const int32_t *>(static_cast<char *>(base) + offs[k]);
+    d.base = base;
+    d.bytes = total;
+    d.device = dev;
+    p.uploaded = true;
+    return BSR_OK;
+}
+
+int32_t finish_create(bsr_pattern *p, int32_t upload_flag, bsr_pattern **out) {
+    try {
+        build_pattern(*p);
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return fail(BSR_ERR_OUT_OF_MEMORY, "host allocation failed while building the pattern");
+    }
+    if (upload_flag) {
+        int32_t st = upload(*p);
+        if (st != BSR_OK) {
+            delete p;
+            return st;
+        }
+    }
+    *out = p;
+    return BSR_OK;
+}
+
+// Common checks of a compute call.
+int32_t check_call(const bsr_pattern *p, int64_t M) {
+    if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    if (!p->uploaded) return fail(BSR_ERR_NO_DEVICE_DATA, "pattern was created without upload");
+    if (M < 0) return fail(BSR_ERR_INVALID_ARG, "M must be >= 0");
+    if (M > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "M must fit in int32");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BSR_ERR_HIP, "hipGetDevice failed");
+    if (dev != p->dev.device)
+        return fail(BSR_ERR_INVALID_ARG, "current device " + std::to_string(dev) + " differs from the pattern's device " +
+                                             std::to_string(p->dev.device));
+    return BSR_OK;
+}
+
+int32_t check_ptr(const void *ptr, const char *name, bool nullable = false) {
+    if (!ptr) return nullable ? BSR_OK : fail(BSR_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (!aligned16(ptr)) return fail(BSR_ERR_MISALIGNED, std::string(name) + " is not 16-byte aligned");
+    return BSR_OK;
+}
+
+}  // namespace
+
+int32_t fail(int32_t status, const std::string &msg) {
+    g_last_error = msg;
+    return status;
+}
+
+}  // namespace bsr
+
+using namespace bsr;
+
+#define BSR_TRY_BEGIN try {
+#define BSR_TRY_END                                                             \
+    }                                                                           \
+    catch (const std::bad_alloc &) {                                            \
+        return fail(BSR_ERR_OUT_OF_MEMORY, "host allocation failed");           \
+    }                                                                           \
+    catch (...) {                                                               \
+        return fail(BSR_ERR_INVALID_ARG, "unexpected internal exception");      \
+    }
+
+#define BSR_CHECK(expr)             \
+    do {                            \
+        int32_t _st = (expr);       \
+        if (_st != BSR_OK) return _st; \
+    } while (0)
+
+extern "C" {
+
+int32_t bsr_abi_version(void) { return BSR_ABI_VERSION; }
+
+int32_t bsr_pattern_create_from_mask(int32_t N, int32_t K, int32_t b, const uint8_t *mask, int32_t upload_flag,
+                                     bsr_pattern **out) {
+    BSR_TRY_BEGIN
+    if (!out) return fail(BSR_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    BSR_CHECK(check_shape(N, K, b));
+    if (!mask) return fail(BSR_ERR_INVALID_ARG, "mask is NULL");
+    auto *p = new bsr_pattern();
+    p->N = N;
+    p->K = K;
+    p->b = b;
+    p->R = N / b;
+    p->C = K / b;
+    p->row_ptr.assign(p->R + 1, 0);
+    for (int32_t r = 0; r < p->R; ++r) {
+        for (int32_t c = 0; c < p->C; ++c)
+            if (mask[(size_t)r * p->C + c]) p->col_idx.push_back(c);
+        p->row_ptr[r + 1] = (int32_t)p->col_idx.size();
+    }
+    p->nnzb = (int32_t)p->col_idx.size();
+    return finish_create(p, upload_flag, out);
+    BSR_TRY_END
+}
+
+int32_t bsr_pattern_create_from_csr(int32_t N, int32_t K, int32_t b, int32_t nnzb, const int32_t *row_ptr,
+                                    const int32_t *col_idx, int32_t upload_flag, bsr_pattern **out) {
+    BSR_TRY_BEGIN
+    if (!out) return fail(BSR_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    BSR_CHECK(check_shape(N, K, b));
+    const int32_t R = N / b, C = K / b;
+    if (nnzb < 0 || (int64_t)nnzb > (int64_t)R * C) return fail(BSR_ERR_INVALID_ARG, "nnzb out of range");
+    if (!row_ptr) return fail(BSR_ERR_INVALID_ARG, "row_ptr is NULL");
+    if (nnzb > 0 && !col_idx) return fail(BSR_ERR_INVALID_ARG, "col_idx is NULL");
+    if (row_ptr[0] != 0) return fail(BSR_ERR_INVALID_ARG, "row_ptr[0] must be 0");
+    if (row_ptr[R] != nnzb) return fail(BSR_ERR_INVALID_ARG, "row_ptr[R] must equal nnzb");
+    for (int32_t r = 0; r < R; ++r) {
+        if (row_ptr[r + 1] < row_ptr[r]) return fail(BSR_ERR_INVALID_ARG, "row_ptr must be non-decreasing");
+        if (row_ptr[r + 1] > nnzb) return fail(BSR_ERR_INVALID_ARG, "row_ptr exceeds nnzb");
+        for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
+            if (col_idx[i] < 0 || col_idx[i] >= C) return fail(BSR_ERR_INVALID_ARG, "col_idx out of range");
+            if (i > row_ptr[r] && col_idx[i] <= col_idx[i - 1])
+                return fail(BSR_ERR_INVALID_ARG, "col_idx must be strictly increasing inside a row");
+        }
+    }
+    auto *p = new bsr_pattern();
+    p->N = N;
+    p->K = K;
+    p->b = b;
+    p->R = R;
+    p->C = C;
+    p->nnzb = nnzb;
+    p->row_ptr.assign(row_ptr, row_ptr + R + 1);
+    p->col_idx.assign(col_idx, col_idx + nnzb);
+    return finish_create(p, upload_flag, out);
+    BSR_TRY_END
+}
+
+int32_t bsr_pattern_info(const bsr_pattern *p, int32_t *N, int32_t *K, int32_t *b, int32_t *nnzb) {
+    if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    if (N) *N = p->N;
+    if (K) *K = p->K;
+    if (b) *b = p->b;
+    if (nnzb) *nnzb = p->nnzb;
+    return BSR_OK;
+}
+
+int32_t bsr_pattern_export(const bsr_pattern *p, int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
+                           int32_t *row_idx, int32_t *perm) {
+    if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    auto put = [](int32_t *dst, const std::vector<int32_t> &v) {
+        if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(int32_t));
+    };
+    put(row_ptr, p->row_ptr);
+    put(col_idx, p->col_idx);
+    put(col_ptr, p->col_ptr);
+    put(row_idx, p->row_idx);
+    put(perm, p->perm);
+    return BSR_OK;
+}
+
+void bsr_pattern_destroy(bsr_pattern *p) {
+    if (!p) return;
+    if (p->dev.base) (void)hipFree(p->dev.base);
+    delete p;
+}
+
+int32_t bsr_linear_fwd(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *V, const bsr_bf16 *bias,
+                       bsr_bf16 *Y, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M == 0) return BSR_OK;
+    FwdArgs a{X, M, p->K, V, bias, Y, p->N};
+    if (M <= kSmallM) return launch_small_m_fwd(*p, a, stream);
+    return launch_group_gemm(*p, false, a, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_linear_bwd_input(const bsr_pattern *p, const bsr_bf16 *dY, int64_t M, const bsr_bf16 *V, bsr_bf16 *dX,
+                             void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(dY, "dY", M == 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    BSR_CHECK(check_ptr(dX, "dX", M == 0));
+    if (M == 0) return BSR_OK;
+    FwdArgs a{dY, M, p->N, V, nullptr, dX, p->K};
+    return launch_group_gemm(*p, true, a, stream);
+    BSR_TRY_END
+}
+
+size_t bsr_linear_bwd_weight_workspace(const bsr_pattern *p, int64_t M) {
+    if (!p || M < 0) return 0;
+    return dw_workspace_bytes(*p, M);
+}
+
+int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bsr_bf16 *X, int64_t M, bsr_bf16 *dV,
+                              bsr_bf16 *dbias, void *workspace, size_t ws_bytes, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(dY, "dY", M == 0));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(dV, "dV", p->nnzb == 0));
+    BSR_CHECK(check_ptr(dbias, "dbias", true));
+    const size_t need = dw_workspace_bytes(*p, M);
+    if (need > 0) {
+        if (ws_bytes < need)
+            return fail(BSR_ERR_WORKSPACE_TOO_SMALL,
+                        "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(need));
+        BSR_CHECK(check_ptr(workspace, "workspace"));
+    }
+    DwArgs a{dY, X, M, dV, dbias, workspace, ws_bytes};
+    return launch_dw(*p, a, stream);
+    BSR_TRY_END
+}
+
+const char *bsr_status_string(int32_t status) {
+    switch (status) {
+        case BSR_OK: return "BSR_OK";
+        case BSR_ERR_INVALID_ARG: return "BSR_ERR_INVALID_ARG";
+        case BSR_ERR_UNSUPPORTED: return "BSR_ERR_UNSUPPORTED";
+        case BSR_ERR_MISALIGNED: return "BSR_ERR_MISALIGNED";
+        case BSR_ERR_WORKSPACE_TOO_SMALL: return "BSR_ERR_WORKSPACE_TOO_SMALL";
+        case BSR_ERR_HIP: return "BSR_ERR_HIP";
+        case BSR_ERR_OUT_OF_MEMORY: return "BSR_ERR_OUT_OF_MEMORY";
+        case BSR_ERR_NO_DEVICE_DATA: return "BSR_ERR_NO_DEVICE_DATA";
+        default: return "BSR_ERR_UNKNOWN";
+    }
+}
+
+const char *bsr_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

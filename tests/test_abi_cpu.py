@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads and exports every symbol the header
+declares; host-only patterns give metadata bit-identical to the oracle's independent scan;
+malformed input is rejected with the documented status codes. No compute call is made."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import meta
+from sparse_gemm_amd import _lib, synth
+from sparse_gemm_amd.binding import Pattern
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsr_linear.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(bsr_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declarations_are_exported():
+    L = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+    assert L.bsr_abi_version() == 1
+
+
+def test_status_strings():
+    L = _lib.load()
+    for code, name in _lib.STATUS.items():
+        assert L.bsr_status_string(code).decode() == name
+    assert L.bsr_status_string(99).decode() == "BSR_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("N,K,b,d,seed", [(256, 256, 32, 0.5, 0), (3072, 768, 32, 0.25, 1), (512, 256, 64, 0.3, 2),
+                                          (64, 2048, 32, 0.05, 3), (2048, 64, 32, 1.0, 4), (128, 128, 32, 0.0, 5)])
+def test_host_pattern_matches_oracle_scan(N, K, b, d, seed):
+    mask = synth.uniform_mask(N // b, K // b, d, np.random.default_rng(seed))
+    p = Pattern.from_mask(mask, N, K, b, upload=False)
+    got = p.export()
+    ref = meta.scan(mask)
+    assert p.nnzb == ref["nnzb"]
+    for k in ("row_ptr", "col_idx", "col_ptr", "row_idx", "perm"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_workload_patterns_match_oracle_scan(k):
+    w = synth.WORKLOADS[k]
+    mask = synth.block_mask(w, 0)
+    p = Pattern.from_mask(mask, w.N, w.K, w.b, upload=False)
+    got, ref = p.export(), meta.scan(mask)
+    for key in ("row_ptr", "col_idx", "col_ptr", "row_idx", "perm"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+def test_csr_round_trip():
+    mask = synth.uniform_mask(12, 9, 0.4, np.random.default_rng(7))
+    ref = meta.scan(mask)
+    p = Pattern.from_csr(12 * 32, 9 * 32, 32, ref["row_ptr"], ref["col_idx"], upload=False)
+    got = p.export()
+    for k in ("row_ptr", "col_idx", "col_ptr", "row_idx", "perm"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def _csr_status(N, K, b, row_ptr, col_idx):
+    L = _lib.load()
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    h = ctypes.c_void_p()
+    st = L.bsr_pattern_create_from_csr(N, K, b, int(ci.size), rp.ctypes.data_as(ctypes.c_void_p),
+                                       ci.ctypes.data_as(ctypes.c_void_p), 0, ctypes.byref(h))
+    if st == 0:
+        L.bsr_pattern_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("row_ptr,col_idx", [
+    ([1, 2, 3], [0, 1, 0]),          # row_ptr[0] != 0
+    ([0, 2, 1], [0, 1]),             # decreasing
+    ([0, 2, 3], [1, 0, 0]),          # unsorted in a row
+    ([0, 2, 3], [1, 1, 0]),          # duplicate in a row
+    ([0, 1, 2], [0, 5]),             # column out of range
+    ([0, 1, 3], [0, 1]),             # row_ptr[R] != nnzb
+    ([0, 1, 2], [-1, 0]),            # negative column
+])
+def test_malformed_csr_rejected(row_ptr, col_idx):
+    assert _csr_status(64, 128, 32, row_ptr, col_idx) == 1
+
+
+def test_bad_shapes_rejected():
+    L = _lib.load()
+    mask = np.ones(16, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    mk = lambda N, K, b: L.bsr_pattern_create_from_mask(N, K, b, mask.ctypes.data_as(ctypes.c_void_p), 0,
+                                                        ctypes.byref(h))
+    assert mk(128, 128, 16) == 2      # unsupported block size
+    assert mk(100, 128, 32) == 1      # N not a multiple of b
+    assert mk(0, 128, 32) == 1
+    assert L.bsr_pattern_create_from_mask(64, 64, 32, None, 0, ctypes.byref(h)) == 1
+    assert "mask" in L.bsr_last_error().decode()
+    assert mk(128, 128, 32) == 0
+    L.bsr_pattern_destroy(h)
+
+
+def test_compute_on_host_only_pattern_is_refused():
+    L = _lib.load()
+    mask = np.ones((2, 2), dtype=np.uint8)
+    p = Pattern.from_mask(mask, 64, 64, 32, upload=False)
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.bsr_linear_fwd(p.handle, fake, 4, fake, None, fake, None) == 7
+    assert L.bsr_linear_bwd_input(p.handle, fake, 4, fake, fake, None) == 7
+    assert L.bsr_linear_bwd_weight(p.handle, fake, fake, 4, fake, None, None, 0, None) == 7
+    assert L.bsr_linear_fwd(None, fake, 4, fake, None, fake, None) == 1
+
+
+def test_workspace_query_is_host_only():
+    w = synth.WORKLOADS[2]
+    p = Pattern.from_mask(synth.block_mask(w, 0), w.N, w.K, w.b, upload=False)
+    L = _lib.load()
+    assert L.bsr_linear_bwd_weight_workspace(p.handle, 0) == 0
+    assert L.bsr_linear_bwd_weight_workspace(p.handle, w.M) > 0
+    assert L.bsr_linear_bwd_weight_workspace(None, w.M) == 0
