@@ -9,7 +9,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsr_linear.so")
+# BSR_LIB_PATH selects another build of the same library (tuning experiments).
+LIB_PATH = os.environ.get("BSR_LIB_PATH") or os.path.join(_HERE, "libbsr_linear.so")
 
 # Names and codes of include/bsr_linear.h.
 STATUS = {0: "BSR_OK", 1: "BSR_ERR_INVALID_ARG", 2: "BSR_ERR_UNSUPPORTED", 3: "BSR_ERR_MISALIGNED",

@@ -5,6 +5,8 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "bsr_internal.hpp"
 
@@ -31,15 +33,20 @@ int32_t upload(bsr_pattern &p) {
         const int32_t **dst;
     };
     DeviceMeta &d = p.dev;
-    const Part parts[] = {
-        {&p.row_ptr, &d.row_ptr},         {&p.col_idx, &d.col_idx},       {&p.col_ptr, &d.col_ptr},
-        {&p.row_idx, &d.row_idx},         {&p.perm, &d.perm},             {&p.blk_row, &d.blk_row},
-        {&p.fwd.order, &d.f_order},       {&p.fwd.step_ptr, &d.f_step_ptr}, {&p.fwd.out, &d.f_out},
-        {&p.fwd.step_in, &d.f_step_in},   {&p.fwd.step_blk, &d.f_step_blk},
-        {&p.bwd.order, &d.t_order},       {&p.bwd.step_ptr, &d.t_step_ptr}, {&p.bwd.out, &d.t_out},
-        {&p.bwd.step_in, &d.t_step_in},   {&p.bwd.step_blk, &d.t_step_blk},
-        {&p.rows_by_nnz, &d.rows_by_nnz},
+    std::vector<Part> parts = {
+        {&p.row_ptr, &d.row_ptr}, {&p.col_idx, &d.col_idx}, {&p.col_ptr, &d.col_ptr},
+        {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.rows_by_nnz, &d.rows_by_nnz},
+        {&p.dw.row, &d.dw_row},   {&p.dw.first, &d.dw_first}, {&p.dw.count, &d.dw_count},
     };
+    for (int k = 0; k < 2; ++k) {
+        for (auto sd : {std::make_pair(&p.fwd[k], &d.fwd[k]), std::make_pair(&p.bwd[k], &d.bwd[k])}) {
+            parts.push_back({&sd.first->order, &sd.second->order});
+            parts.push_back({&sd.first->step_ptr, &sd.second->step_ptr});
+            parts.push_back({&sd.first->out, &sd.second->out});
+            parts.push_back({&sd.first->rec, &sd.second->rec});
+            parts.push_back({&sd.first->hdr, &sd.second->hdr});
+        }
+    }
     size_t total = 0;
     for (const Part &q : parts) total += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);
     if (total == 0) total = 256;
@@ -60,7 +67,7 @@ int32_t upload(bsr_pattern &p) {
         (void)hipFree(base);
         return fail(BSR_ERR_HIP, std::string("hipMemcpy: ") + hipGetErrorString(e));
     }
-    for (size_t k = 0; k < sizeof(parts) / sizeof(parts[0]); ++k)
+    for (size_t k = 0; k < parts.size(); ++k)
         *parts[k].dst = reinterpret_cast<const int32_t *>(static_cast<char *>(base) + offs[k]);
     d.base = base;
     d.bytes = total;
