@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import platform
 import sys
@@ -52,6 +53,124 @@ def op_bytes(w, nnzb: int, op: str, bias: bool) -> int:
     if op == "dw":
         return act_y + act_x + vals + csr
     raise ValueError(op)
+
+
+KERNEL_SOURCES = ("sparse_gemm_amd/csrc/bsr_kernels.hip", "sparse_gemm_amd/csrc/bsr_pattern.cpp",
+                  "sparse_gemm_amd/csrc/bsr_internal.hpp")
+OP_KERNELS = {"fwd": ("k_group_gemm", "k_small_m"), "dx": ("k_group_gemm",), "dw": ("k_dw", "k_dw_reduce")}
+COPY_BYTES = 256 << 20   # plain copy used to calibrate the HBM byte counters
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_name}.txt")
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch of each op from the committed counter summary, or None when the
+    summary is missing or was taken with other kernel sources."""
+    path = traffic_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(("#", " ", "|", "`")):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    out = {}
+    for op in ("fwd", "dx", "dw"):
+        key = f"{op}_hbm_bytes_per_launch"
+        if key in vals:
+            out[op] = float(vals[key])
+    return out
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops) -> str:
+    """Per-op HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB
+    per dispatch) of `bench.py --calibrate-copy`, each scaled by what the same counter reads for a
+    plain copy of COPY_BYTES bytes. Writes the summary under profiles/ and returns its path."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = {}
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return rows
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def avg(rows, pred):
+        v = [x for k, xs in rows.items() if pred(k) for x in xs]
+        return sum(v) / len(v) if v else 0.0
+
+    def is_copy(k):
+        return "copy" in k.lower() or "elementwise" in k.lower()
+
+    # the calibration copy is the largest copy-like dispatch
+    copy_f = max((x for k, xs in fetch.items() if is_copy(k) for x in xs), default=0.0)
+    copy_w = max((x for k, xs in write.items() if is_copy(k) for x in xs), default=0.0)
+    sf = COPY_BYTES / copy_f if copy_f else 1.0
+    sw = COPY_BYTES / copy_w if copy_w else 1.0
+    lines = [f"# HBM traffic per launch, {workload_name}", "",
+             "Two rocprofv3 counter runs of the benchmark (FETCH_SIZE, then WRITE_SIZE), run from the",
+             "repository root on one MI355X:", "",
+             "```",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o run -- python3 bench.py "
+             f"--workload <k> --steps 3 --warmup 1 --no-cpu-baseline --no-extras --calibrate-copy",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o run -- python3 bench.py "
+             f"--workload <k> --steps 3 --warmup 1 --no-cpu-baseline --no-extras --calibrate-copy",
+             "python3 bench.py --workload <k> --pmc-summary <fetch_dir> <write_dir>",
+             "```", "",
+             f"Calibration: a plain copy of {COPY_BYTES} bytes reads FETCH_SIZE = {copy_f:.0f} B and "
+             f"WRITE_SIZE = {copy_w:.0f} B;",
+             f"kernel bytes below are scaled by {sf:.4f} (reads) and {sw:.4f} (writes).", ""]
+    lines.append("| Kernel | dispatches | FETCH B/launch (scaled) | WRITE B/launch (scaled) |")
+    lines.append("|---|---|---|---|")
+    for k in sorted(set(fetch) | set(write)):
+        if "bsr" not in k:
+            continue
+        f_ = fetch.get(k, [])
+        w_ = write.get(k, [])
+        short = re.sub(r"\(.*$", "", k.replace("void ", "").replace("bsr::(anonymous namespace)::", ""))
+        lines.append(f"| `{short}` | {len(f_)} | {sf * sum(f_) / max(1, len(f_)):.0f} | "
+                     f"{sw * sum(w_) / max(1, len(w_)):.0f} |")
+    lines.append("")
+    lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
+    for op in ops:
+        pred = lambda k, op=op: "bsr" in k and any(n in k for n in OP_KERNELS[op])
+        # k_group_gemm serves fwd (TRANS=false) and dx (TRANS=true): split on the template flag
+        if op == "fwd":
+            pred = lambda k: "bsr" in k and (("k_group_gemm" in k and "false>" in k) or "k_small_m" in k)
+        elif op == "dx":
+            pred = lambda k: "bsr" in k and "k_group_gemm" in k and "true>" in k
+        per = sf * avg(fetch, pred) + sw * avg(write, pred)
+        if op == "dw":
+            # the split-M reduce is a second kernel of the same launch
+            per = sf * (avg(fetch, lambda k: "k_dw<" in k or ("k_dw" in k and "reduce" not in k)) +
+                        avg(fetch, lambda k: "k_dw_reduce" in k)) + \
+                  sw * (avg(write, lambda k: "k_dw<" in k or ("k_dw" in k and "reduce" not in k)) +
+                        avg(write, lambda k: "k_dw_reduce" in k))
+        lines.append(f"{op}_hbm_bytes_per_launch: {per:.0f}")
+    path = traffic_path(workload_name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 def cpu_model() -> str:
@@ -228,7 +347,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the density-1.0 and hipBLASLt legs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"also run one plain {COPY_BYTES}-byte device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        from sparse_gemm_amd import synth
+        w = synth.WORKLOADS[args.workload]
+        print(summarize_pmc(args.pmc_summary[0], args.pmc_summary[1], w.name, w.ops))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -285,9 +414,11 @@ def main():
     else:
         roofline = {"bound": "mfma", "achieved": F / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    roofline["traffic"] = None
+    tr = read_traffic(w.name)
+    roofline["traffic"] = tr.get(dom) if tr else None
     roofline["kernel"] = {"fwd": "bsr_linear_fwd", "dx": "bsr_linear_bwd_input", "dw": "bsr_linear_bwd_weight"}[dom]
-    roofline["per_launch"] = {"flops": F, "algorithmic_bytes": dom_bytes, "avg_us": op_ms[dom] * 1e3}
+    roofline["per_launch"] = {"flops": F, "algorithmic_bytes": dom_bytes, "avg_us": op_ms[dom] * 1e3,
+                              "kernels": list(OP_KERNELS[dom])}
 
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": nsteps_graph,
            "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
@@ -343,6 +474,13 @@ def main():
         h_ms, _, _ = time_graph(dense_step, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
         out["hipblaslt_dense_context"] = {"ms_per_step": h_ms, "speedup_of_sparse": h_ms / step_ms}
         del sets_d, dense_w, pd
+
+    if args.calibrate_copy:
+        src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host cores")
