@@ -36,15 +36,15 @@ int32_t upload(bsr_pattern &p) {
     std::vector<Part> parts = {
         {&p.row_ptr, &d.row_ptr}, {&p.col_idx, &d.col_idx}, {&p.col_ptr, &d.col_ptr},
         {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.rows_by_nnz, &d.rows_by_nnz},
-        {&p.dw.row, &d.dw_row},   {&p.dw.first, &d.dw_first}, {&p.dw.count, &d.dw_count},
+        {&p.dw.dense.items, &d.dw_dense}, {&p.dw.runs.items, &d.dw_runs}, {&p.dw.cmap, &d.dw_cmap},
+        {&p.dw.dense_blocks, &d.dw_dense_blocks}, {&p.dw.run_blocks, &d.dw_run_blocks},
     };
     for (int k = 0; k < 2; ++k) {
         for (auto sd : {std::make_pair(&p.fwd[k], &d.fwd[k]), std::make_pair(&p.bwd[k], &d.bwd[k])}) {
             parts.push_back({&sd.first->order, &sd.second->order});
-            parts.push_back({&sd.first->step_ptr, &sd.second->step_ptr});
+            parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
             parts.push_back({&sd.first->out, &sd.second->out});
             parts.push_back({&sd.first->rec, &sd.second->rec});
-            parts.push_back({&sd.first->hdr, &sd.second->hdr});
         }
     }
     size_t total = 0;

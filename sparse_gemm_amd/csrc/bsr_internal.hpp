@@ -10,60 +10,76 @@
 
 namespace bsr {
 
-// Output blocks per work-group of the forward / input-gradient kernels. Each pattern keeps two
-// work lists: a wide one (more output blocks share every activation tile that is loaded) and a
-// narrow one (more work-groups, for shapes that would not fill the chip otherwise).
-inline int wide_group(int b) { return b == 64 ? 4 : 8; }
-inline int narrow_group(int b) { return b == 64 ? 2 : 4; }
-// Kept blocks of one block row handled by one weight-gradient work-group.
-inline int dw_group(int b) { return b == 64 ? 2 : 4; }
+// Group GEMM shapes. A work-group (8 waves x 32 activation rows) computes G output
+// blocks (block rows of W for the forward, block columns for the input gradient). A group's steps
+// are the input blocks its members touch; each step is cut into sub-steps of at most S kept blocks
+// (S == G: "direct" sub-steps, slot t = member t). Candidate (G, S) pairs per block size; the
+// pattern builder keeps, for each of the two G, the S with the fewest estimated load instructions.
+constexpr int kGemmWaves = 8;
+constexpr int gemm_wave_rows(int) { return 32; }
+constexpr int gemm_rows(int b) { return kGemmWaves * gemm_wave_rows(b); }
+inline int wide_group(int b) { return b == 64 ? 2 : 8; }
+inline int narrow_group(int b) { return b == 64 ? 1 : 4; }
+// Slots per sub-step the kernels are instantiated for, per (b, G).
+inline std::vector<int> gemm_slot_options(int b, int G) {
+    if (b == 32) return G == 8 ? std::vector<int>{2, 4, 8} : std::vector<int>{2, 4};
+    return G == 2 ? std::vector<int>{1, 2} : std::vector<int>{1};
+}
 
-// Host-built work list of the forward or input-gradient kernel. Output blocks (block rows of W
-// for the forward, block columns for the input gradient) are grouped G at a time; a group's
-// steps are the union of the input blocks its members touch, padded with empty steps to a
-// multiple of P (the prefetch depth of the kernel, which processes P steps per loop trip).
-// Per step s the kernel reads one record of RS ints, laid out for what it issues at step s:
-//   rec[s*RS + 0]      bit t set = member t has a kept block at step s
-//   rec[s*RS + 1]      input block of step s + P (activations prefetched at step s)
-//   rec[s*RS + 2 + t]  value block of member t at step s + P (prefetched at step s), -1 = none
-// and per group one header of HS ints: the input blocks of its first P steps, then the value
-// blocks of those steps (P runs of G, -1 = none). Past the last real step, input blocks repeat
-// the last real one and value blocks are -1.
+// Host-built work list of the forward or input-gradient kernel. Sub-steps are padded per group to
+// a multiple of P (the kernel's prefetch depth: it handles P sub-steps per loop trip). Record of
+// sub-step s, RS ints: rec[s*RS] = input block; rec[s*RS + 1 + k] = slot k: for S < G,
+// (value block << 5) | member, for S == G the value block of member k; -1 = empty. Padding
+// sub-steps repeat the group's last input block and have empty slots.
 struct GroupSchedule {
-    int G = 0, P = 0, RS = 0, HS = 0;
+    int G = 0, S = 0, P = 0, RS = 0;
     int ngroups = 0;
-    std::vector<int32_t> order;      // processing order of the groups (most steps first)
-    std::vector<int32_t> step_ptr;   // [ngroups + 1], padded steps
-    std::vector<int32_t> out;        // [ngroups * G] output block index per slot, -1 = unused
-    std::vector<int32_t> rec;        // [nsteps * RS]
-    std::vector<int32_t> hdr;        // [ngroups * HS]
+    std::vector<int32_t> order;      // processing order of the groups (most sub-steps first)
+    std::vector<int32_t> sub_ptr;    // [ngroups + 1]
+    std::vector<int32_t> out;        // [ngroups * G] output block index per member, -1 = unused
+    std::vector<int32_t> rec;        // [nsub * RS]
 };
 
-// Prefetch depth (steps per loop trip) of the group GEMM for block size b (compile-time tuning
-// knobs BSR_GEMM_DEPTH32 / BSR_GEMM_DEPTH64).
+// Prefetch depth (sub-steps per loop trip) of the group GEMM for block size b, G members and S
+// slots (compile-time tuning knobs; the shapes with the most registers in use get the shallower).
 #ifndef BSR_GEMM_DEPTH32
 #define BSR_GEMM_DEPTH32 3
 #endif
 #ifndef BSR_GEMM_DEPTH64
 #define BSR_GEMM_DEPTH64 2
 #endif
-constexpr int gemm_depth(int b) { return b == 64 ? BSR_GEMM_DEPTH64 : BSR_GEMM_DEPTH32; }
+constexpr int gemm_depth(int b, int G, int S) {
+    return (b == 64 || (G == 8 && S == 8)) ? BSR_GEMM_DEPTH64 : BSR_GEMM_DEPTH32;
+}
 constexpr int pow2_at_least(int n) { return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
-// Ints per step record and per group header, for G members and depth P (at most 64: one wave
-// lane per int).
-constexpr int rec_stride(int G) { return pow2_at_least(G + 2); }
-constexpr int hdr_stride(int G, int P) { return pow2_at_least(P + P * G); }
+constexpr int rec_stride(int S) { return pow2_at_least(1 + S); }
 
-// Host-built work list of the weight-gradient kernel: runs of up to GB consecutive kept blocks
-// of one block row (they share the block row's slab of dY), most blocks first.
+// Weight-gradient work items. An item is a set of up to TR block rows and up to TC block
+// columns; it computes every kept block where they cross, and stages each row's dY slab and each
+// column's X slab once per chunk of M, so a slab is shared by all the item's blocks in its row or
+// column. "Dense" items (TR x TC = 8 x 8 for b = 32, 4 x 4 for b = 64) take row groups' columns
+// that hold kept blocks in at least half of the group's rows; "runs" (one row, up to 4 (b = 32)
+// or 2 (b = 64) columns) take the remaining blocks. Item layout, TS ints: rows[TR] (-1 unused),
+// cols[TC] (-1 unused), blk[TR*TC] (CSR index of the kept block at (row i, column j), -1 if none).
+struct DwShape {
+    int TR, TC;
+    constexpr int TS() const { return (TR + TC + TR * TC + 15) / 16 * 16; }
+};
+constexpr DwShape dw_dense_shape(int b) { return b == 64 ? DwShape{4, 4} : DwShape{8, 8}; }
+constexpr DwShape dw_runs_shape(int b) { return b == 64 ? DwShape{1, 2} : DwShape{1, 4}; }
+
+struct DwItems {
+    int n = 0;
+    std::vector<int32_t> items;   // [n * TS]
+};
 struct DwSchedule {
-    int GB = 0;
-    int ngroups = 0;
-    std::vector<int32_t> row, first, count;   // [ngroups] each
+    DwItems dense, runs;
+    std::vector<int32_t> cmap;                       // [nnzb] index of the block within its kind
+    std::vector<int32_t> dense_blocks, run_blocks;   // CSR index of each kind's blocks, by that index
 };
 
 struct DevSchedule {
-    const int32_t *order = nullptr, *step_ptr = nullptr, *out = nullptr, *rec = nullptr, *hdr = nullptr;
+    const int32_t *order = nullptr, *sub_ptr = nullptr, *out = nullptr, *rec = nullptr;
 };
 
 // Device copies of the metadata (one allocation, carved into arrays).
@@ -74,7 +90,8 @@ struct DeviceMeta {
     const int32_t *row_ptr = nullptr, *col_idx = nullptr, *col_ptr = nullptr, *row_idx = nullptr,
                   *perm = nullptr;
     DevSchedule fwd[2], bwd[2];   // [0] wide groups, [1] narrow groups
-    const int32_t *dw_row = nullptr, *dw_first = nullptr, *dw_count = nullptr;
+    const int32_t *dw_dense = nullptr, *dw_runs = nullptr, *dw_cmap = nullptr, *dw_dense_blocks = nullptr,
+                  *dw_run_blocks = nullptr;
     const int32_t *rows_by_nnz = nullptr;   // small-M forward: block rows, most blocks first
 };
 

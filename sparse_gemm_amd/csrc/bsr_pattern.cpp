@@ -6,6 +6,7 @@
 // column. The transposed form is what the input-gradient kernel walks, so it needs no atomics.
 #include <algorithm>
 #include <numeric>
+#include <utility>
 
 #include "bsr_internal.hpp"
 
@@ -45,110 +46,204 @@ std::vector<int32_t> by_count_desc(const std::vector<int32_t> &ptr) {
 // Group output blocks (block rows of W for the forward, block columns for the input gradient)
 // G at a time in order of decreasing kept-block count. Each group's steps are the union of the
 // input blocks its members touch, ascending; a member's value block at a step is the block that
-// multiplies that input block into that member, or -1. The steps are then padded and encoded as
-// the per-step records described with GroupSchedule.
+// multiplies that input block into that member. Steps are cut into sub-steps of at most S kept
+// blocks, S chosen among `s_options` to minimise the estimated load instructions (activation tile
+// plus S value blocks per sub-step), then padded and encoded as GroupSchedule records.
 //   ptr / idx / val: for output block o, entries e in [ptr[o], ptr[o+1]) have input block
 //   idx[e] (ascending) and value block val(e).
 template <class ValFn>
-GroupSchedule make_groups(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val,
-                          int G, int P) {
-    GroupSchedule s;
-    s.G = G;
-    s.P = P;
-    s.RS = rec_stride(G);
-    s.HS = hdr_stride(G, P);
-    const int RS = s.RS, HS = s.HS;
+GroupSchedule make_groups(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val, int b,
+                          int G, const std::vector<int> &s_options) {
     const int32_t nout = (int32_t)ptr.size() - 1;
     const std::vector<int32_t> ids = by_count_desc(ptr);
-    s.ngroups = (nout + G - 1) / G;
-    s.step_ptr.assign(s.ngroups + 1, 0);
-    s.out.assign((size_t)s.ngroups * G, -1);
-    s.hdr.assign((size_t)s.ngroups * HS, -1);
-    std::vector<int32_t> cursor(G), in_of, blk_of;   // real steps of the current group
-    for (int32_t g = 0; g < s.ngroups; ++g) {
+    const int ngroups = (nout + G - 1) / G;
+    // real steps of every group: input block and the members' value blocks
+    std::vector<std::vector<int32_t>> in_of(ngroups), blk_of(ngroups);
+    std::vector<int32_t> outs((size_t)ngroups * G, -1);
+    std::vector<int32_t> cursor(G);
+    for (int32_t g = 0; g < ngroups; ++g) {
         int members = 0;
         for (int t = 0; t < G; ++t) {
             const int32_t k = g * G + t;
             if (k < nout) {
-                s.out[(size_t)g * G + t] = ids[k];
+                outs[(size_t)g * G + t] = ids[k];
                 cursor[t] = ptr[ids[k]];
                 members++;
             }
         }
-        in_of.clear();
-        blk_of.clear();
-        // merge the members' ascending input lists
         for (;;) {
             int32_t next_in = INT32_MAX;
             for (int t = 0; t < members; ++t) {
-                const int32_t o = s.out[(size_t)g * G + t];
+                const int32_t o = outs[(size_t)g * G + t];
                 if (cursor[t] < ptr[o + 1]) next_in = std::min(next_in, idx[cursor[t]]);
             }
             if (next_in == INT32_MAX) break;
-            in_of.push_back(next_in);
+            in_of[g].push_back(next_in);
             for (int t = 0; t < G; ++t) {
                 int32_t v = -1;
                 if (t < members) {
-                    const int32_t o = s.out[(size_t)g * G + t];
+                    const int32_t o = outs[(size_t)g * G + t];
                     if (cursor[t] < ptr[o + 1] && idx[cursor[t]] == next_in) {
                         v = val(cursor[t]);
                         cursor[t]++;
                     }
                 }
-                blk_of.push_back(v);
+                blk_of[g].push_back(v);
             }
         }
-        const int32_t n = (int32_t)in_of.size();
-        const int32_t npad = (n + P - 1) / P * P;
-        auto in_at = [&](int32_t k) { return n == 0 ? 0 : in_of[std::min(k, n - 1)]; };
-        auto blk_at = [&](int32_t k, int t) { return k < n ? blk_of[(size_t)k * G + t] : -1; };
-        int32_t *h = &s.hdr[(size_t)g * HS];
-        for (int u = 0; u < P; ++u) {
-            h[u] = in_at(u);
-            for (int t = 0; t < G; ++t) h[P + u * G + t] = blk_at(u, t);
-        }
-        for (int32_t k = 0; k < npad; ++k) {
-            std::vector<int32_t> r(RS, -1);
-            int32_t mask = 0;
-            for (int t = 0; t < G; ++t)
-                if (blk_at(k, t) >= 0) mask |= 1 << t;
-            r[0] = mask;
-            r[1] = in_at(k + P);
-            for (int t = 0; t < G; ++t) r[2 + t] = blk_at(k + P, t);
-            s.rec.insert(s.rec.end(), r.begin(), r.end());
-        }
-        s.step_ptr[g + 1] = s.step_ptr[g] + npad;
     }
-    s.order.resize(s.ngroups);
+    // slots per sub-step: fewest estimated load instructions (1 KB each) per activation row tile
+    const int x_instr = gemm_rows(b) * b * 2 / 1024, w_instr = b * b * 2 / 1024;
+    int best_s = G;
+    double best_cost = 0;
+    for (int S : s_options) {
+        const int P = gemm_depth(b, G, S);
+        double cost = 0;
+        for (int32_t g = 0; g < ngroups; ++g) {
+            const size_t n = in_of[g].size();
+            int64_t subs = 0;
+            for (size_t k = 0; k < n; ++k) {
+                int present = 0;
+                for (int t = 0; t < G; ++t) present += blk_of[g][k * G + t] >= 0;
+                subs += S == G ? 1 : std::max(1, (present + S - 1) / S);
+            }
+            subs = (subs + P - 1) / P * P;
+            cost += (double)subs * (x_instr + S * w_instr);
+        }
+        if (S == s_options.front() || cost < best_cost) {
+            best_cost = cost;
+            best_s = S;
+        }
+    }
+    GroupSchedule s;
+    s.G = G;
+    s.S = best_s;
+    s.P = gemm_depth(b, G, best_s);
+    const int P = s.P;
+    s.RS = rec_stride(best_s);
+    s.ngroups = ngroups;
+    s.out = outs;
+    s.sub_ptr.assign(ngroups + 1, 0);
+    const int S = s.S, RS = s.RS;
+    for (int32_t g = 0; g < ngroups; ++g) {
+        const size_t n = in_of[g].size();
+        const size_t first = s.rec.size() / RS;
+        for (size_t k = 0; k < n; ++k) {
+            std::vector<int32_t> slots;
+            for (int t = 0; t < G; ++t) {
+                const int32_t v = blk_of[g][k * G + t];
+                if (S == G) slots.push_back(v);
+                else if (v >= 0) slots.push_back(v * 32 + t);
+            }
+            size_t used = 0;
+            do {
+                std::vector<int32_t> r(RS, -1);
+                r[0] = in_of[g][k];
+                for (int q = 0; q < S && used < slots.size(); ++q, ++used) r[1 + q] = slots[used];
+                s.rec.insert(s.rec.end(), r.begin(), r.end());
+            } while (used < slots.size());
+        }
+        size_t count = s.rec.size() / RS - first;
+        while (count % P) {   // padding: last input block again, no value blocks
+            std::vector<int32_t> r(RS, -1);
+            r[0] = n ? in_of[g][n - 1] : 0;
+            s.rec.insert(s.rec.end(), r.begin(), r.end());
+            count++;
+        }
+        s.sub_ptr[g + 1] = s.sub_ptr[g] + (int32_t)count;
+    }
+    s.order.resize(ngroups);
     std::iota(s.order.begin(), s.order.end(), 0);
     std::stable_sort(s.order.begin(), s.order.end(), [&](int32_t a, int32_t b) {
-        return s.step_ptr[a + 1] - s.step_ptr[a] > s.step_ptr[b + 1] - s.step_ptr[b];
+        return s.sub_ptr[a + 1] - s.sub_ptr[a] > s.sub_ptr[b + 1] - s.sub_ptr[b];
     });
     return s;
 }
 
-// Weight-gradient runs: every block row is cut into runs of at most GB consecutive kept
-// blocks; runs with more blocks come first.
-DwSchedule make_dw_groups(const bsr_pattern &p, int GB) {
-    DwSchedule s;
-    s.GB = GB;
-    std::vector<int32_t> row, first, count;
-    for (int32_t r = 0; r < p.R; ++r) {
-        for (int32_t i = p.row_ptr[r]; i < p.row_ptr[r + 1]; i += GB) {
-            row.push_back(r);
-            first.push_back(i);
-            count.push_back(std::min<int32_t>(GB, p.row_ptr[r + 1] - i));
+// Weight-gradient items. Block rows are taken in groups of TR, most kept blocks first. Inside a
+// group, a column holding kept blocks in at least half of the group's rows costs one shared X slab
+// in a dense item instead of one slab per block in runs (and the dense kernel multiplies every
+// block of its grid, so it wants items at least half full); those columns go to dense items, TC
+// at a time. Every other kept block goes to a run of its own row (TC_run columns at a time).
+// Items with more blocks come first.
+DwSchedule make_dw_items(const bsr_pattern &p) {
+    const DwShape D = dw_dense_shape(p.b), Rn = dw_runs_shape(p.b);
+    std::vector<std::pair<int32_t, std::vector<int32_t>>> dense, runs;   // (blocks, item)
+    const std::vector<int32_t> rows = by_count_desc(p.row_ptr);
+    std::vector<int32_t> pos(p.C, -1);   // CSR index of (row, column) for the current row
+    std::vector<int32_t> count(p.C, 0);
+    for (size_t g0 = 0; g0 < rows.size(); g0 += D.TR) {
+        const int nr = (int)std::min<size_t>(D.TR, rows.size() - g0);
+        std::fill(count.begin(), count.end(), 0);
+        for (int i = 0; i < nr; ++i) {
+            const int32_t r = rows[g0 + i];
+            for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) count[p.col_idx[e]]++;
+        }
+        const int need = std::max(2, (nr + 1) / 2);
+        std::vector<int32_t> dcols;
+        for (int32_t c = 0; c < p.C; ++c)
+            if (count[c] >= need) dcols.push_back(c);
+        // dense items over the shared columns
+        for (size_t c0 = 0; c0 < dcols.size(); c0 += D.TC) {
+            const int nc = (int)std::min<size_t>(D.TC, dcols.size() - c0);
+            std::vector<int32_t> it(D.TS(), -1);
+            int nblk = 0;
+            for (int i = 0; i < nr; ++i) it[i] = rows[g0 + i];
+            for (int j = 0; j < nc; ++j) it[D.TR + j] = dcols[c0 + j];
+            for (int i = 0; i < nr; ++i) {
+                const int32_t r = rows[g0 + i];
+                for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) pos[p.col_idx[e]] = e;
+                for (int j = 0; j < nc; ++j) {
+                    const int32_t e = pos[dcols[c0 + j]];
+                    it[D.TR + D.TC + i * D.TC + j] = e;
+                    nblk += e >= 0;
+                }
+                for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) pos[p.col_idx[e]] = -1;
+            }
+            dense.emplace_back(nblk, std::move(it));
+        }
+        // runs over the other blocks of each row
+        for (int i = 0; i < nr; ++i) {
+            const int32_t r = rows[g0 + i];
+            std::vector<int32_t> rest;
+            for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e)
+                if (count[p.col_idx[e]] < need) rest.push_back(e);
+            for (size_t k0 = 0; k0 < rest.size(); k0 += Rn.TC) {
+                const int nc = (int)std::min<size_t>(Rn.TC, rest.size() - k0);
+                std::vector<int32_t> it(Rn.TS(), -1);
+                it[0] = r;
+                for (int j = 0; j < nc; ++j) {
+                    it[1 + j] = p.col_idx[rest[k0 + j]];
+                    it[1 + Rn.TC + j] = rest[k0 + j];
+                }
+                runs.emplace_back(nc, std::move(it));
+            }
         }
     }
-    s.ngroups = (int)row.size();
-    std::vector<int32_t> ids(s.ngroups);
-    std::iota(ids.begin(), ids.end(), 0);
-    std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b) { return count[a] > count[b]; });
-    for (int32_t k : ids) {
-        s.row.push_back(row[k]);
-        s.first.push_back(first[k]);
-        s.count.push_back(count[k]);
-    }
+    auto pack = [](std::vector<std::pair<int32_t, std::vector<int32_t>>> &v) {
+        std::stable_sort(v.begin(), v.end(), [](const auto &a, const auto &b) { return a.first > b.first; });
+        DwItems out;
+        out.n = (int)v.size();
+        for (auto &x : v) out.items.insert(out.items.end(), x.second.begin(), x.second.end());
+        return out;
+    };
+    DwSchedule s;
+    s.dense = pack(dense);
+    s.runs = pack(runs);
+    // compact per-kind block numbering (for the split-M partial sums)
+    s.cmap.assign(p.nnzb, -1);
+    auto number = [&](const DwItems &v, int TS, int first_blk, int nblk, std::vector<int32_t> &list) {
+        for (int k = 0; k < v.n; ++k)
+            for (int q = 0; q < nblk; ++q) {
+                const int32_t e = v.items[(size_t)k * TS + first_blk + q];
+                if (e >= 0) {
+                    s.cmap[e] = (int32_t)list.size();
+                    list.push_back(e);
+                }
+            }
+    };
+    number(s.dense, D.TS(), D.TR + D.TC, D.TR * D.TC, s.dense_blocks);
+    number(s.runs, Rn.TS(), Rn.TR + Rn.TC, Rn.TR * Rn.TC, s.run_blocks);
     return s;
 }
 
@@ -158,10 +253,11 @@ void build_pattern(bsr_pattern &p) {
     build_csc(p);
     const int Gs[2] = {wide_group(p.b), narrow_group(p.b)};
     for (int k = 0; k < 2; ++k) {
-        p.fwd[k] = make_groups(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, Gs[k], gemm_depth(p.b));
-        p.bwd[k] = make_groups(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, Gs[k], gemm_depth(p.b));
+        const std::vector<int> opts = gemm_slot_options(p.b, Gs[k]);
+        p.fwd[k] = make_groups(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, Gs[k], opts);
+        p.bwd[k] = make_groups(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, Gs[k], opts);
     }
-    p.dw = make_dw_groups(p, dw_group(p.b));
+    p.dw = make_dw_items(p);
     p.rows_by_nnz = by_count_desc(p.row_ptr);
 }
 
