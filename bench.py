@@ -57,7 +57,7 @@ def op_bytes(w, nnzb: int, op: str, bias: bool) -> int:
 
 KERNEL_SOURCES = ("sparse_gemm_amd/csrc/bsr_kernels.hip", "sparse_gemm_amd/csrc/bsr_pattern.cpp",
                   "sparse_gemm_amd/csrc/bsr_internal.hpp")
-OP_KERNELS = {"fwd": ("k_group_gemm", "k_small_m"), "dx": ("k_group_gemm",), "dw": ("k_dw", "k_dw_reduce")}
+OP_KERNELS = {"fwd": ("k_group_gemm", "k_small_m"), "dx": ("k_group_gemm",), "dw": ("k_dw_tile", "k_dw_runs", "k_dw_reduce")}
 COPY_BYTES = 256 << 20   # plain copy used to calibrate the HBM byte counters
 
 

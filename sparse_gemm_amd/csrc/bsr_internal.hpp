@@ -15,9 +15,12 @@ namespace bsr {
 // are the input blocks its members touch; each step is cut into sub-steps of at most S kept blocks
 // (S == G: "direct" sub-steps, slot t = member t). Candidate (G, S) pairs per block size; the
 // pattern builder keeps, for each of the two G, the S with the fewest estimated load instructions.
+// Work-groups of 8 waves (256 activation rows) by default; the narrow groups also come in a
+// 4-wave (128-row) form, for problems too small to fill the chip with the larger tiles.
 constexpr int kGemmWaves = 8;
 constexpr int gemm_wave_rows(int) { return 32; }
 constexpr int gemm_rows(int b) { return kGemmWaves * gemm_wave_rows(b); }
+constexpr int kGemmWavesSmall = 4;
 inline int wide_group(int b) { return b == 64 ? 2 : 8; }
 inline int narrow_group(int b) { return b == 64 ? 1 : 4; }
 // Slots per sub-step the kernels are instantiated for, per (b, G).

@@ -760,27 +760,26 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 
 // ---- host-side planning ----
 
-// Which of the pattern's two group schedules (wide G or narrow G) a call uses: the one with the
-// fewer estimated load instructions, after scaling by how well its work-groups fill the chip.
-int choose_schedule(const bsr_pattern &p, bool transposed, int64_t M) {
-    const char *f = std::getenv("BSR_GEMM_GROUPS");   // tuning knob: wide | narrow
-    if (f && !std::strcmp(f, "wide")) return 0;
-    if (f && !std::strcmp(f, "narrow")) return 1;
+// Tile of a group GEMM call: which of the pattern's two group schedules (wide G or narrow G)
+// and how many waves (32 activation rows each) per work-group.
+struct GemmTile {
+    int k = 0;    // 0 = wide groups, 1 = narrow groups
+    int nw = kGemmWaves;
+};
+
+// The widest tile that still gives every compute unit at least two work-groups (so that one
+// work-group's prologue and epilogue overlap another's main loop): wide groups of 8 waves, then
+// narrow groups of 8 waves, else narrow groups of 4 waves.
+GemmTile choose_tile(const bsr_pattern &p, bool transposed, int64_t M) {
+    const char *f = std::getenv("BSR_GEMM_TILE");   // tuning knob: wide | narrow | small
+    if (f && !std::strcmp(f, "wide")) return GemmTile{0, kGemmWaves};
+    if (f && !std::strcmp(f, "narrow")) return GemmTile{1, kGemmWaves};
+    if (f && !std::strcmp(f, "small")) return GemmTile{1, kGemmWavesSmall};
     const GroupSchedule *s = transposed ? p.bwd : p.fwd;
     const int64_t nmt = (M + gemm_rows(p.b) - 1) / gemm_rows(p.b);
-    double best = 0;
-    int pick = 0;
-    for (int k = 0; k < 2; ++k) {
-        const int x_instr = gemm_rows(p.b) * p.b * 2 / 1024, w_instr = p.b * p.b * 2 / 1024;
-        const double instr = (double)s[k].rec.size() / s[k].RS * (x_instr + s[k].S * w_instr) * nmt;
-        const double fill = std::min(1.0, (double)s[k].ngroups * nmt / kCUs);
-        const double cost = instr / std::max(fill, 1e-3);
-        if (k == 0 || cost < best) {
-            best = cost;
-            pick = k;
-        }
-    }
-    return pick;
+    if ((int64_t)s[0].ngroups * nmt >= 2 * kCUs) return GemmTile{0, kGemmWaves};
+    if ((int64_t)s[1].ngroups * nmt >= 2 * kCUs) return GemmTile{1, kGemmWaves};
+    return GemmTile{1, kGemmWavesSmall};
 }
 
 // M-split of one kind of weight-gradient item.
@@ -836,29 +835,34 @@ int32_t launched(const char *what) {
     return BSR_OK;
 }
 
-template <int BS, int G, int S, bool TRANS>
-void launch_gg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
-    constexpr int NW = kGemmWaves, WM = gemm_wave_rows(BS), P = gemm_depth(BS, G, S);
-    const int nmtiles = (int)((a.M + gemm_rows(BS) - 1) / gemm_rows(BS));
+template <int BS, int G, int S, int NW, bool TRANS>
+void launch_gg(const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
+    constexpr int WM = gemm_wave_rows(BS), P = gemm_depth(BS, G, S), BM = NW * WM;
+    const int nmtiles = (int)((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
     hipLaunchKernelGGL((k_group_gemm<BS, G, S, WM, NW, P, TRANS>), grid, dim3(NW * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, nmtiles);
 }
 
-// Dispatch on the schedule's (G, S) to the instantiated kernels (see gemm_slot_options).
+// Dispatch on the block size, the schedule's (G, S) and the waves per work-group to the
+// instantiated kernels (see gemm_slot_options; narrow groups also have the 4-wave form).
 template <bool TRANS>
-int32_t launch_gg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a,
-                        hipStream_t st) {
-    const int key = p.b * 10000 + s.G * 100 + s.S;
+int32_t launch_gg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, int nw,
+                        const FwdArgs &a, hipStream_t st) {
+    const int key = (p.b * 10000 + s.G * 100 + s.S) * 10 + (nw == kGemmWaves ? 0 : 1);
+    constexpr int W8 = kGemmWaves, W4 = kGemmWavesSmall;
     switch (key) {
-        case 320802: launch_gg<32, 8, 2, TRANS>(p, s, d, a, st); break;
-        case 320804: launch_gg<32, 8, 4, TRANS>(p, s, d, a, st); break;
-        case 320808: launch_gg<32, 8, 8, TRANS>(p, s, d, a, st); break;
-        case 320402: launch_gg<32, 4, 2, TRANS>(p, s, d, a, st); break;
-        case 320404: launch_gg<32, 4, 4, TRANS>(p, s, d, a, st); break;
-        case 640201: launch_gg<64, 2, 1, TRANS>(p, s, d, a, st); break;
-        case 640202: launch_gg<64, 2, 2, TRANS>(p, s, d, a, st); break;
-        case 640101: launch_gg<64, 1, 1, TRANS>(p, s, d, a, st); break;
+        case 3208020: launch_gg<32, 8, 2, W8, TRANS>(s, d, a, st); break;
+        case 3208040: launch_gg<32, 8, 4, W8, TRANS>(s, d, a, st); break;
+        case 3208080: launch_gg<32, 8, 8, W8, TRANS>(s, d, a, st); break;
+        case 3204020: launch_gg<32, 4, 2, W8, TRANS>(s, d, a, st); break;
+        case 3204040: launch_gg<32, 4, 4, W8, TRANS>(s, d, a, st); break;
+        case 3204021: launch_gg<32, 4, 2, W4, TRANS>(s, d, a, st); break;
+        case 3204041: launch_gg<32, 4, 4, W4, TRANS>(s, d, a, st); break;
+        case 6402010: launch_gg<64, 2, 1, W8, TRANS>(s, d, a, st); break;
+        case 6402020: launch_gg<64, 2, 2, W8, TRANS>(s, d, a, st); break;
+        case 6401010: launch_gg<64, 1, 1, W8, TRANS>(s, d, a, st); break;
+        case 6401011: launch_gg<64, 1, 1, W4, TRANS>(s, d, a, st); break;
         default: return fail(BSR_ERR_UNSUPPORTED, "no kernel for this group shape");
     }
     return BSR_OK;
@@ -868,12 +872,13 @@ int32_t launch_gg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevS
 
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    const int k = choose_schedule(p, transposed, a.M);
-    const GroupSchedule &s = (transposed ? p.bwd : p.fwd)[k];
-    const DevSchedule &d = (transposed ? p.dev.bwd : p.dev.fwd)[k];
-    const int64_t nwg = (int64_t)s.ngroups * ((a.M + gemm_rows(p.b) - 1) / gemm_rows(p.b));
+    const GemmTile t = choose_tile(p, transposed, a.M);
+    const GroupSchedule &s = (transposed ? p.bwd : p.fwd)[t.k];
+    const DevSchedule &d = (transposed ? p.dev.bwd : p.dev.fwd)[t.k];
+    const int rows = t.nw * gemm_wave_rows(p.b);
+    const int64_t nwg = (int64_t)s.ngroups * ((a.M + rows - 1) / rows);
     if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
-    const int32_t rc = transposed ? launch_gg_shape<true>(p, s, d, a, st) : launch_gg_shape<false>(p, s, d, a, st);
+    const int32_t rc = transposed ? launch_gg_shape<true>(p, s, d, t.nw, a, st) : launch_gg_shape<false>(p, s, d, t.nw, a, st);
     if (rc != BSR_OK) return rc;
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }
