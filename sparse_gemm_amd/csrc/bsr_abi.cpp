@@ -39,13 +39,11 @@ int32_t upload(bsr_pattern &p) {
         {&p.dw.dense.items, &d.dw_dense}, {&p.dw.runs.items, &d.dw_runs}, {&p.dw.cmap, &d.dw_cmap},
         {&p.dw.dense_blocks, &d.dw_dense_blocks}, {&p.dw.run_blocks, &d.dw_run_blocks},
     };
-    for (int k = 0; k < 2; ++k) {
-        for (auto sd : {std::make_pair(&p.fwd[k], &d.fwd[k]), std::make_pair(&p.bwd[k], &d.bwd[k])}) {
-            parts.push_back({&sd.first->order, &sd.second->order});
-            parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
-            parts.push_back({&sd.first->out, &sd.second->out});
-            parts.push_back({&sd.first->rec, &sd.second->rec});
-        }
+    for (auto sd : {std::make_pair(&p.fwd, &d.fwd), std::make_pair(&p.bwd, &d.bwd)}) {
+        parts.push_back({&sd.first->order, &sd.second->order});
+        parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
+        parts.push_back({&sd.first->out, &sd.second->out});
+        parts.push_back({&sd.first->rec, &sd.second->rec});
     }
     size_t total = 0;
     for (const Part &q : parts) total += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);

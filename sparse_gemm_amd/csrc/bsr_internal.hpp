@@ -10,52 +10,37 @@
 
 namespace bsr {
 
-// Group GEMM shapes. A work-group (8 waves x 32 activation rows) computes G output
-// blocks (block rows of W for the forward, block columns for the input gradient). A group's steps
-// are the input blocks its members touch; each step is cut into sub-steps of at most S kept blocks
-// (S == G: "direct" sub-steps, slot t = member t). Candidate (G, S) pairs per block size; the
-// pattern builder keeps, for each of the two G, the S with the fewest estimated load instructions.
-// Work-groups of 8 waves (256 activation rows) by default; the narrow groups also come in a
-// 4-wave (128-row) form, for problems too small to fill the chip with the larger tiles.
+// Panel GEMM (forward and input gradient). The activations are consumed in panels of 64
+// columns (128 bytes of bf16 per row, one full cache line), so a panel covers 64 / b input blocks
+// (2 for b = 32, 1 for b = 64). A work-group owns G output blocks (block rows of W for the
+// forward, block columns for the input gradient) and 32 activation rows per wave; its work list
+// is the panels in which its members have kept blocks. A member's kept block inside a panel is a
+// "unit" (unit u = member * (64 / b) + block within the panel). Each sub-step stages one panel of
+// activations and at most S value blocks ("slots"); a panel with more kept blocks than S takes
+// several sub-steps.
+constexpr int kPanelCols = 64;
+// Compute waves (32 activation rows each) per work-group: 8, or 4 for problems that would not
+// fill the chip otherwise; plus kLoaderWaves waves that only issue the loads. Members per group:
+// 4 for b = 32 (128 output columns, 8 units per panel), 1 for b = 64.
 constexpr int kGemmWaves = 8;
-constexpr int gemm_wave_rows(int) { return 32; }
-constexpr int gemm_rows(int b) { return kGemmWaves * gemm_wave_rows(b); }
 constexpr int kGemmWavesSmall = 4;
-inline int wide_group(int b) { return b == 64 ? 2 : 8; }
-inline int narrow_group(int b) { return b == 64 ? 1 : 4; }
-// Slots per sub-step the kernels are instantiated for, per (b, G).
-inline std::vector<int> gemm_slot_options(int b, int G) {
-    if (b == 32) return G == 8 ? std::vector<int>{2, 4, 8} : std::vector<int>{2, 4};
-    return G == 2 ? std::vector<int>{1, 2} : std::vector<int>{1};
-}
+constexpr int kLoaderWaves = 2;
+inline int gemm_group(int b) { return b == 64 ? 1 : 4; }
+// Slots per sub-step: G (half of a panel's units for b = 32, all of them for b = 64).
+inline int gemm_slots(int, int G) { return G; }
 
-// Host-built work list of the forward or input-gradient kernel. Sub-steps are padded per group to
-// a multiple of P (the kernel's prefetch depth: it handles P sub-steps per loop trip). Record of
-// sub-step s, RS ints: rec[s*RS] = input block; rec[s*RS + 1 + k] = slot k: for S < G,
-// (value block << 5) | member, for S == G the value block of member k; -1 = empty. Padding
-// sub-steps repeat the group's last input block and have empty slots.
+// Sub-step record, kRecInts ints: [0] panel index; [1 + k] value block in slot k (-1 = empty),
+// k < S; [1 + S + w] slot of units 8w .. 8w + 7, 4 bits each (unit u at bits 4 * (u % 8); 15 =
+// the unit has no block in this sub-step).
+constexpr int kRecInts = 16;
 struct GroupSchedule {
-    int G = 0, S = 0, P = 0, RS = 0;
+    int G = 0, S = 0;
     int ngroups = 0;
     std::vector<int32_t> order;      // processing order of the groups (most sub-steps first)
     std::vector<int32_t> sub_ptr;    // [ngroups + 1]
     std::vector<int32_t> out;        // [ngroups * G] output block index per member, -1 = unused
-    std::vector<int32_t> rec;        // [nsub * RS]
+    std::vector<int32_t> rec;        // [nsub * kRecInts]
 };
-
-// Prefetch depth (sub-steps per loop trip) of the group GEMM for block size b, G members and S
-// slots (compile-time tuning knobs; the shapes with the most registers in use get the shallower).
-#ifndef BSR_GEMM_DEPTH32
-#define BSR_GEMM_DEPTH32 3
-#endif
-#ifndef BSR_GEMM_DEPTH64
-#define BSR_GEMM_DEPTH64 2
-#endif
-constexpr int gemm_depth(int b, int G, int S) {
-    return (b == 64 || (G == 8 && S == 8)) ? BSR_GEMM_DEPTH64 : BSR_GEMM_DEPTH32;
-}
-constexpr int pow2_at_least(int n) { return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
-constexpr int rec_stride(int S) { return pow2_at_least(1 + S); }
 
 // Weight-gradient work items. An item is a set of up to TR block rows and up to TC block
 // columns; it computes every kept block where they cross, and stages each row's dY slab and each
@@ -92,7 +77,7 @@ struct DeviceMeta {
     int device = -1;
     const int32_t *row_ptr = nullptr, *col_idx = nullptr, *col_ptr = nullptr, *row_idx = nullptr,
                   *perm = nullptr;
-    DevSchedule fwd[2], bwd[2];   // [0] wide groups, [1] narrow groups
+    DevSchedule fwd, bwd;
     const int32_t *dw_dense = nullptr, *dw_runs = nullptr, *dw_cmap = nullptr, *dw_dense_blocks = nullptr,
                   *dw_run_blocks = nullptr;
     const int32_t *rows_by_nnz = nullptr;   // small-M forward: block rows, most blocks first
@@ -103,7 +88,7 @@ struct DeviceMeta {
 struct bsr_pattern {
     int32_t N = 0, K = 0, b = 0, R = 0, C = 0, nnzb = 0;
     std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, rows_by_nnz;
-    bsr::GroupSchedule fwd[2], bwd[2];   // [0] wide groups, [1] narrow groups
+    bsr::GroupSchedule fwd, bwd;
     bsr::DwSchedule dw;
     bsr::DeviceMeta dev;
     bool uploaded = false;

@@ -113,220 +113,282 @@ __device__ __forceinline__ f32x4 add_bias4(f32x4 v, const uint16_t *bias) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Group GEMM: forward (TRANS = false) and input gradient (TRANS = true).
+// Panel GEMM: forward (TRANS = false) and input gradient (TRANS = true).
 //
 // A work-group owns G output blocks (block rows of W for the forward, block columns for the
-// input gradient) and BM = NW * WM activation rows; wave w owns rows [w*WM, (w+1)*WM) for all G
-// blocks, so every wave does the same work whatever blocks are present. A sub-step takes one
-// input block of the activations (block column c of X, or block row r of dY) and up to S of the
-// value blocks kept there (the host splits steps with more into several sub-steps):
-//   out tile^T [n][m] += A[n][k] . B[k][m],   B[k][m] = act[m][in*BS + k]   (32x32x16 MFMA)
+// input gradient) and BM = 32 * NW activation rows; compute wave w owns rows [32 w, 32 w + 32)
+// for all G blocks. The activations are read in panels of 64 columns: one full 128-byte cache
+// line per row, which is what the load path of a CU serves best (it handles a bounded number of
+// distinct cache lines per clock, however few of their bytes are used). A sub-step stages one
+// panel of the work-group's rows and up to S kept value blocks of that panel in LDS, then every
+// compute wave runs the products of each unit (a member's kept block inside the panel) that has
+// a block:
+//   out tile^T [n][m] += A[n][k] . B[k][m],   B[k][m] = act[m][panel*64 + k]   (32x32x16 MFMA)
 //   forward:    A[n][k] = V[i][n][k]   (natural layout, 16-byte LDS reads)
 //   input grad: A[n][k] = V[i][k][n]   (transposed, ds_read_b64_tr_b16 of the natural layout)
-// so each lane ends up with runs of 4 consecutive output columns of one activation row. Only kept blocks
-// are loaded, once per work-group, into LDS slots; a sub-step first reads all its weight
-// fragments, then runs the products of each member (uniform branches, static accumulators).
-// Pipelining: at sub-step s the activation fragments and value blocks of sub-step s + P are
-// loaded into registers (rings of P slots) while sub-step s computes; the value blocks of s + 1,
-// loaded P - 1 sub-steps earlier, then go to the other half of a double-buffered LDS stage.
-// Sub-step records are fetched by wave 0 into a small LDS ring one sub-step ahead of use. Every
-// loop trip issues the same loads, so the compiler's wait counts stay exact.
+// so each lane ends up with runs of 4 consecutive output columns of one activation row.
+// The loads go straight from memory to LDS, three stages deep, and are issued by NL extra loader
+// waves, so that the compute waves never stall behind a full load queue and loads overlap the
+// products. Sub-step s: loaders wait for their loads of s, then a barrier (the stage of s is
+// complete; nobody reads the stage of s - 1 any more), then the loaders issue the loads of s + 2
+// into the stage of s - 1 while the compute waves run the products of s. In each stage the 16-byte
+// chunks of every row are XOR swizzled so that operand reads are free of bank conflicts.
 // ------------------------------------------------------------------------------------------
-template <int BS, int G, int S, int WM, int NW, int P, bool TRANS>
-__global__ __launch_bounds__(NW * 64) void k_group_gemm(
-    const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V,
+
+// Byte offset in the work-group's LDS of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Direct-to-LDS load: lane i's 16 bytes at (voff, soff) of buffer r go to LDS byte address
+// m0 + 16 i. Written as inline assembly so that the compiler, which cannot tell which LDS bytes
+// such a load writes, does not wait for it before every LDS access; the kernels wait for these
+// loads themselves (wait_vm) before the barrier that publishes a stage. The kernels that use it
+// keep nothing else in M0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff),
+                 "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Waits until at most n (wave-uniform, LO <= n <= HI) vector memory loads of this wave are in
+// flight: a binary search over the immediate forms of s_waitcnt vmcnt.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm(int n) {
+    if constexpr (LO == HI) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LO) : "memory");
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n <= MID) wait_vm<LO, MID>(n);
+        else wait_vm<MID + 1, HI>(n);
+    }
+}
+
+// 16-byte chunk swizzles of staged tiles: chunk c of row r is stored at chunk c ^ swz(r). With
+// them, the reads of an MFMA operand (32 consecutive rows, one chunk each, per half-wave) touch
+// distinct LDS banks in every group of 16 lanes, for rows of 8 chunks (128 bytes) and of 4
+// chunks (64 bytes).
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int BS, int G, int S, int NW, int NL, bool TRANS>
+__global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
+    const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
     const int32_t *__restrict__ sub_ptr, const int32_t *__restrict__ gout, const int32_t *__restrict__ rec,
-    int nmtiles) {
-    constexpr bool DIRECT = S == G;         // slot t feeds member t
+    int ngroups, int nmtiles) {
+    constexpr int PB = kPanelCols / BS;     // blocks per panel
+    constexpr int U = G * PB;               // units per panel
     constexpr int NT = BS / 32;             // 32-wide output tiles per block
-    constexpr int KC = BS / 16;             // 16-deep k chunks per block
-    constexpr int MT = WM / 32;             // 32-row activation tiles per wave
-    constexpr int BM = WM * NW;
-    constexpr int LDW = BS + 8;             // padded LDS pitch of a staged block (elements)
-    constexpr int NTH = NW * 64;
-    constexpr int CPB = BS * BS / 8;        // 16-byte chunks per block
-    constexpr int CPT = (S * CPB + NTH - 1) / NTH;   // chunks per thread per sub-step
-    constexpr int RS = rec_stride(S);
-    constexpr int RING = 4;                 // record ring entries in LDS
-    static_assert(CPB % 64 == 0, "a wave's chunks must stay in one block");
-    static_assert(RS <= 64, "one record word per lane");
-    __shared__ __attribute__((aligned(16))) uint16_t wl[2][S][BS][LDW];   // staged blocks, by slot
-    __shared__ __attribute__((aligned(16))) int32_t rring[RING][RS];
+    constexpr int KCB = BS / 16;            // 16-deep k chunks per block
+    constexpr int BM = NW * 32;             // activation rows per work-group
+    constexpr int XB = BM * 128;            // bytes of a staged activation panel
+    constexpr int RB = BS * 2;              // bytes per row of a value block
+    constexpr int WBB = BS * RB;            // bytes per value block
+    constexpr int STAGE = XB + S * WBB + kRecInts * 4;   // activations, value blocks, a record
+    constexpr int NST = 3;                  // stages
+    constexpr int CPS = WBB / 1024;         // 1 KB load chunks per block
+    constexpr int XPL = BM / 8 / NL;        // activation loads (8 rows x 128 bytes) per loader wave
+    constexpr int WPL = S * CPS / NL;       // value-block chunks per loader wave
+    constexpr int MAXL = XPL + WPL + 1;     // loads per loader wave and sub-step, at most
+    static_assert(BM / 8 % NL == 0 && S * CPS % NL == 0, "loads must spread evenly over the loader waves");
+    static_assert(U <= 16 && S <= 8, "unit map: 16 units of 4 bits, slots below 15");
+    static_assert(2 * MAXL <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
-    // Work-groups are dispatched to the 8 XCDs round-robin; give each XCD a contiguous run of
-    // logical tiles, ordered activation-tile-major, so that the groups sharing an activation tile
-    // run together on one XCD and find it in that XCD's L2.
-    const int ngroups = (int)(gridDim.x / nmtiles);
+    // Work-group -> (group, activation tile). Each XCD takes a contiguous run of logical indices
+    // (work-groups are dealt to the XCDs round-robin); logical indices run over chunks of 4
+    // activation tiles, and inside a chunk over the groups (most sub-steps first), then the tiles.
+    // So every XCD gets all groups of its tiles (balanced work), and the work-groups running
+    // together on one XCD share a few activation tiles (their panels) and their groups' value
+    // blocks through that XCD's L2.
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int g = order[L % ngroups];
-    const int mt0 = L / ngroups;
+    const int chunk = L / (4 * ngroups), r4 = L % (4 * ngroups);
+    const int mc = min(4, nmtiles - 4 * chunk);   // tiles in this chunk
+    const int g = order[r4 / mc];
+    const int mt0 = 4 * chunk + r4 % mc;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= NW;
+    const int lw = wave - NW;               // loader index (loader waves only)
     const int l32 = lane & 31, lh = lane >> 5;
-    const int mbase = mt0 * BM + wave * WM;
-    const int rlane = min(lane, RS - 1);
 
     // Activations of this work-group's rows; rows past M read as zeros.
     const int rows = min(BM, M - mt0 * BM);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(act + (int64_t)mt0 * BM * in_ld, (uint32_t)rows * in_ld * 2);
-    uint32_t voff[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) voff[mt] = (uint32_t)(((wave * WM + mt * 32 + l32) * in_ld + lh * 8) * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, v_bytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, (uint32_t)sub_ptr[ngroups] * kRecInts * 4);
+    const uint32_t sbase = lds_addr(smem);
+    // loader lw's activation load i stages tile rows 8 (lw + NL i) .. + 7: lane -> row + lane / 8,
+    // LDS chunk lane % 8, which holds activation chunk (lane % 8) ^ swz8(row); its value-block
+    // load j is the 1 KB part (c % CPS) of slot c / CPS, c = lw + NL j. (Offsets are recomputed at
+    // every issue, so that no registers stay reserved for them next to the accumulators.)
+    auto xoff = [&](int i) __attribute__((always_inline)) {
+        const int r = (lw + NL * i) * 8 + (lane >> 3);
+        return (uint32_t)(r * in_ld * 2 + (((lane & 7) ^ swz8(r)) << 4));
+    };
+    auto woff = [&](int j) __attribute__((always_inline)) {
+        const int q = (lw + NL * j) % CPS;
+        if constexpr (BS == 32) {
+            const int n = 16 * q + (lane >> 2);
+            return (uint32_t)(n * RB + (((lane & 3) ^ swz4(n)) << 4));
+        } else {
+            const int n = 8 * q + (lane >> 3);
+            return (uint32_t)(n * RB + (((lane & 7) ^ swz8(n)) << 4));
+        }
+    };
 
-    f32x16 acc[G][NT][MT];
+    // Sub-step records travel with the stages: the stage of sub-step s also receives the record of
+    // sub-step s + 2 (loader 0, lanes 0..3), so that at sub-step s the record needed to issue the
+    // loads of s + 2 is read from LDS.
+    struct Rec {
+        int panel, map0, map1, blk[WPL];
+    };
+    auto rec_from = [&](const int32_t *e) __attribute__((always_inline)) {
+        Rec x;
+        x.panel = __builtin_amdgcn_readfirstlane(e[0]);
+        x.map0 = __builtin_amdgcn_readfirstlane(e[1 + S]);
+        x.map1 = __builtin_amdgcn_readfirstlane(e[2 + S]);
+        if (loader) {
+#pragma unroll
+            for (int j = 0; j < WPL; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[1 + (lw + NL * j) / CPS]);
+        }
+        return x;
+    };
+    // a loader's loads of one sub-step (record x) into stage st, and, from loader 0, the record
+    // of sub-step rsidx (if valid); returns how many loads it issued
+    auto issue = [&](int st, const Rec &x, int rsidx) __attribute__((always_inline)) {
+        const uint32_t base = sbase + (uint32_t)st * STAGE;
+        const uint32_t soff = (uint32_t)x.panel * 128u;
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) dma16(ra, base + (uint32_t)(lw + NL * i) * 1024u, xoff(i), soff);
+        int n = XPL;
+#pragma unroll
+        for (int j = 0; j < WPL; ++j) {
+            const int c = lw + NL * j;
+            if (x.blk[j] >= 0) {
+                dma16(rv, base + XB + (uint32_t)(c / CPS) * WBB + (uint32_t)(c % CPS) * 1024u, woff(j),
+                      (uint32_t)x.blk[j] * WBB);
+                ++n;
+            }
+        }
+        if (lw == 0 && rsidx >= 0) {
+            if (lane < kRecInts / 4) dma16(rr, base + XB + S * WBB, (uint32_t)lane * 16u, (uint32_t)rsidx * kRecInts * 4u);
+            ++n;
+        }
+        return n;
+    };
+
+    f32x16 acc[G][NT];
 #pragma unroll
     for (int t = 0; t < G; ++t)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int v = 0; v < 16; ++v) acc[t][nt][v] = 0.f;
+
+    // products of one staged sub-step: the wave's activation fragments once, then for every unit
+    // with a block (uniform tests) its value fragments and products
+    auto compute = [&](int st, int map0, int map1) __attribute__((always_inline)) {
+        const unsigned char *xt = smem + st * STAGE;
+        const unsigned char *wt = xt + XB;
+        const int r = wave * 32 + l32;
+        bf16x8 xf[4];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[t][nt][mt][v] = 0.f;
+        for (int kc = 0; kc < 4; ++kc)
+            xf[kc] = *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * kc + lh) ^ swz8(r)) << 4));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int slot = ((u < 8 ? map0 : map1) >> (4 * (u % 8))) & 15;
+            if (slot == 15) continue;
+            const int t = u / PB, h = u % PB;
+            const unsigned char *wb = wt + slot * WBB;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                bf16x8 wf[KCB];
+#pragma unroll
+                for (int kc = 0; kc < KCB; ++kc) {
+                    if constexpr (!TRANS) {
+                        const int n = nt * 32 + l32, kg = 2 * kc + lh;
+                        const int sw = BS == 32 ? swz4(n) : swz8(n);
+                        wf[kc] = *reinterpret_cast<const bf16x8 *>(wb + n * RB + ((kg ^ sw) << 4));
+                    } else {
+                        // lane l: V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], two transposing reads
+                        // of 4 rows each; lane s of a 16-lane group points at row R + s / 4,
+                        // columns C .. C + 3
+                        const int gq = lane >> 4, s16 = lane & 15;
+                        const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
+                        const int C = nt * 32 + (gq & 1) * 16 + 4 * (s16 & 3);
+                        auto at = [&](int row) {
+                            const int sw = BS == 32 ? swz4(row) : swz8(row);
+                            return (lds_i16x4 *)(wb + row * RB + ((((C >> 3) ^ sw) << 4) | ((C & 7) << 1)));
+                        };
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+                        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        wf[kc] = __builtin_bit_cast(bf16x8, v);
+                    }
+                }
+#pragma unroll
+                for (int kc = 0; kc < KCB; ++kc) acc[t][nt] = mfma32(wf[kc], xf[h * KCB + kc], acc[t][nt]);
+            }
+        }
+    };
 
     const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
-    bf16x8 xr[P][MT][KC];   // activation fragments of the next P sub-steps (ring)
-    u32x4 wr[P][CPT];       // value-block chunks of the next P sub-steps (ring)
-    int slot_of[P][S];      // slot words of the next P sub-steps (uniform)
-    int rr[P];              // wave 0: records further ahead (ring; lane k holds word k)
-
-    auto rec_at = [&](int sidx) __attribute__((always_inline)) {
-        return rec[(size_t)min(sidx, s1 - 1) * RS + rlane];
-    };
-    auto load_x = [&](bf16x8(&slot)[MT][KC], int in_blk) __attribute__((always_inline)) {
-        const uint32_t soff = (uint32_t)in_blk * BS * 2;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) slot[mt][kc] = buf_load16(ra, voff[mt] + kc * 32, soff);
-    };
-    // value block of a slot word
-    auto blk_of = [](int word) __attribute__((always_inline)) { return DIRECT ? word : (word < 0 ? -1 : word >> 5); };
-    auto load_w = [&](u32x4(&slot)[CPT], const int(&words)[S]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int k = (j * NTH + wave * 64) / CPB;   // slot: uniform per wave
-            if (k >= S) continue;
-            const int w = (tid + j * NTH) % CPB;
-            const int blk = blk_of(words[k]);
-            const __amdgpu_buffer_rsrc_t rw = make_rsrc(V + (size_t)max(blk, 0) * BS * BS, blk >= 0 ? BS * BS * 2 : 0);
-            slot[j] = buf_load16u(rw, (uint32_t)w * 16, 0);
-        }
-    };
-    // member fed by a slot word
-    auto member_of = [](int k, int word) __attribute__((always_inline)) { return DIRECT ? k : (word & 31); };
-    auto store_w = [&](int buf, const u32x4(&slot)[CPT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int k = (j * NTH + wave * 64) / CPB;
-            if (k >= S) continue;
-            const int w = (tid + j * NTH) % CPB;
-            *reinterpret_cast<u32x4 *>(&wl[buf][k][w / (BS / 8)][(w % (BS / 8)) * 8]) = slot[j];
-        }
-    };
-    // All of the sub-step's weight fragments are read from LDS first (empty slots read stale data
-    // that no product uses), then the products run member by member: for member t, every slot k
-    // that feeds it (uniform tests), so each accumulator stays in its own registers.
-    auto compute = [&](int buf, const bf16x8(&x)[MT][KC], const int(&words)[S]) __attribute__((always_inline)) {
-        bf16x8 a[S][NT][KC];
-#pragma unroll
-        for (int k = 0; k < S; ++k)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    if constexpr (!TRANS)
-                        a[k][nt][kc] = *reinterpret_cast<const bf16x8 *>(&wl[buf][k][nt * 32 + l32][kc * 16 + lh * 8]);
-                    else
-                        a[k][nt][kc] = lds_read_tr8_32(&wl[buf][k][0][0], LDW, kc * 16, nt * 32, lane);
-                }
-#pragma unroll
-        for (int t = 0; t < G; ++t)
-#pragma unroll
-            for (int k = 0; k < S; ++k) {
-                if (DIRECT && k != t) continue;
-                if (words[k] < 0 || member_of(k, words[k]) != t) continue;   // uniform
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int kc = 0; kc < KC; ++kc)
-                            acc[t][nt][mt] = mfma32(a[k][nt][kc], x[mt][kc], acc[t][nt][mt]);
-            }
-    };
-    // record words from the LDS ring, all lanes reading the same entry
-    auto ring_words = [&](int sidx, int &in_blk, int(&words)[S]) __attribute__((always_inline)) {
-        const int32_t *e = rring[sidx % RING];
-        in_blk = __builtin_amdgcn_readfirstlane(e[0]);
-#pragma unroll
-        for (int k = 0; k < S; ++k) words[k] = __builtin_amdgcn_readfirstlane(e[1 + k]);
-    };
-
     if (s0 < s1) {
-        // prologue: the first P sub-steps' records straight from memory, their loads, and the
-        // record ring / wave 0's record registers set up as the loop expects at sub-step s0
-#pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int r = rec_at(s0 + u);
-            int words[S];
-#pragma unroll
-            for (int k = 0; k < S; ++k) words[k] = __builtin_amdgcn_readlane(r, 1 + k);
-#pragma unroll
-            for (int k = 0; k < S; ++k) slot_of[u][k] = words[k];
-            load_x(xr[u], __builtin_amdgcn_readlane(r, 0));
-            load_w(wr[u], words);
+        // prologue: the loaders put sub-steps s0 and s0 + 1 in flight (with the records of s0 + 2
+        // and s0 + 3)
+        const Rec r0 = rec_from(rec + (size_t)s0 * kRecInts);
+        int n1 = 0, mapB0 = -1, mapB1 = -1;
+        if (loader) issue(0, r0, s0 + 2 < s1 ? s0 + 2 : -1);
+        if (s0 + 1 < s1) {
+            const Rec r1 = rec_from(rec + (size_t)(s0 + 1) * kRecInts);
+            if (loader) n1 = issue(1, r1, s0 + 3 < s1 ? s0 + 3 : -1);
+            mapB0 = r1.map0;
+            mapB1 = r1.map1;
         }
-        if (wave == 0) {
-            if (lane < RS) rring[(s0 + P) % RING][lane] = rec_at(s0 + P);
-#pragma unroll
-            for (int v = 0; v < P; ++v) rr[v] = rec_at(s0 + (v == 0 ? 2 * P : P + v));
-        }
-        store_w(0, wr[0]);
-        __builtin_amdgcn_s_waitcnt(0);   // drain: the loop's wait counts then hold on entry too
-        __syncthreads();
-        for (int s = s0; s < s1; s += P) {
-#pragma unroll
-            for (int u = 0; u < P; ++u) {
-                const int cs = s + u;
-                const int buf = (cs - s0) & 1;
-                int in_next, words_next[S];
-                ring_words(cs + P, in_next, words_next);       // record of sub-step cs + P
-                load_w(wr[u], words_next);                      // its value blocks
-                compute(buf, xr[u], slot_of[u]);
-                load_x(xr[u], in_next);                         // its activations
-#pragma unroll
-                for (int k = 0; k < S; ++k) slot_of[u][k] = words_next[k];
-                if (wave == 0) {                                // record of cs + P + 1 into the ring
-                    if (lane < RS) rring[(cs + P + 1) % RING][lane] = rr[(u + 1) % P];
-                    rr[(u + 1) % P] = rec_at(cs + 2 * P + 1);
-                }
-                store_w(buf ^ 1, wr[(u + 1) % P]);              // value blocks of sub-step cs + 1
-                __syncthreads();
+        int mapA0 = r0.map0, mapA1 = r0.map1;
+        int st = 0;   // stage of sub-step s
+        for (int s = s0; s < s1; ++s) {
+            if (loader) wait_vm<0, MAXL>(n1);   // this loader's loads of sub-step s have landed
+            __syncthreads();                     // everyone's have; nobody reads sub-step s - 1 any more
+            const int st2 = st == 0 ? 2 : st - 1;   // stage of s + 2 (= that of s - 1)
+            int m20 = -1, m21 = -1;
+            if (s + 2 < s1) {
+                const Rec x = rec_from(reinterpret_cast<const int32_t *>(smem + st * STAGE + XB + S * WBB));
+                if (loader) n1 = issue(st2, x, s + 4 < s1 ? s + 4 : -1);
+                m20 = x.map0;
+                m21 = x.map1;
+            } else {
+                n1 = 0;
             }
+            if (!loader) compute(st, mapA0, mapA1);
+            mapA0 = mapB0;
+            mapA1 = mapB1;
+            mapB0 = m20;
+            mapB1 = m21;
+            st = st == 2 ? 0 : st + 1;
         }
     }
+    if (loader) return;
 
     // Epilogue: item v of lane l is output column nt*32 + 8*(v/4) + 4*(l/32) + v%4 of the block,
-    // activation row mt*32 + l%32 of the wave.
+    // activation row l%32 of the wave.
+    const int m = mt0 * BM + wave * 32 + l32;
 #pragma unroll
     for (int t = 0; t < G; ++t) {
         const int o = gout[g * G + t];
-        if (o < 0) continue;
+        if (o < 0 || m >= M) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mbase + mt * 32 + l32;
-            if (m >= M) continue;
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = o * BS + nt * 32 + q * 8 + lh * 4;
-                    f32x4 v = quad(acc[t][nt][mt], q);
-                    if (bias) v = add_bias4(v, bias + n);
-                    store4_bf16(out + (int64_t)m * out_ld + n, v[0], v[1], v[2], v[3]);
-                }
-        }
+            for (int q = 0; q < 4; ++q) {
+                const int n = o * BS + nt * 32 + q * 8 + lh * 4;
+                f32x4 v = quad(acc[t][nt], q);
+                if (bias) v = add_bias4(v, bias + n);
+                store4_bf16(out + (int64_t)m * out_ld + n, v[0], v[1], v[2], v[3]);
+            }
     }
 }
 
@@ -760,26 +822,16 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 
 // ---- host-side planning ----
 
-// Tile of a group GEMM call: which of the pattern's two group schedules (wide G or narrow G)
-// and how many waves (32 activation rows each) per work-group.
-struct GemmTile {
-    int k = 0;    // 0 = wide groups, 1 = narrow groups
-    int nw = kGemmWaves;
-};
-
-// The widest tile that still gives every compute unit at least two work-groups (so that one
-// work-group's prologue and epilogue overlap another's main loop): wide groups of 8 waves, then
-// narrow groups of 8 waves, else narrow groups of 4 waves.
-GemmTile choose_tile(const bsr_pattern &p, bool transposed, int64_t M) {
-    const char *f = std::getenv("BSR_GEMM_TILE");   // tuning knob: wide | narrow | small
-    if (f && !std::strcmp(f, "wide")) return GemmTile{0, kGemmWaves};
-    if (f && !std::strcmp(f, "narrow")) return GemmTile{1, kGemmWaves};
-    if (f && !std::strcmp(f, "small")) return GemmTile{1, kGemmWavesSmall};
-    const GroupSchedule *s = transposed ? p.bwd : p.fwd;
-    const int64_t nmt = (M + gemm_rows(p.b) - 1) / gemm_rows(p.b);
-    if ((int64_t)s[0].ngroups * nmt >= 2 * kCUs) return GemmTile{0, kGemmWaves};
-    if ((int64_t)s[1].ngroups * nmt >= 2 * kCUs) return GemmTile{1, kGemmWaves};
-    return GemmTile{1, kGemmWavesSmall};
+// Compute waves per work-group of a panel GEMM call: 8 (256 activation rows) when that gives every
+// compute unit at least two work-groups (so that one work-group's prologue and epilogue overlap
+// another's main loop), else 4.
+int choose_waves(const bsr_pattern &p, bool transposed, int64_t M) {
+    const char *f = std::getenv("BSR_GEMM_WAVES");   // tuning knob: 8 | 4
+    if (f && !std::strcmp(f, "8")) return kGemmWaves;
+    if (f && !std::strcmp(f, "4")) return kGemmWavesSmall;
+    const GroupSchedule &s = transposed ? p.bwd : p.fwd;
+    const int64_t tiles = (M + kGemmWaves * 32 - 1) / (kGemmWaves * 32);
+    return (int64_t)s.ngroups * tiles >= 2 * kCUs ? kGemmWaves : kGemmWavesSmall;
 }
 
 // M-split of one kind of weight-gradient item.
@@ -835,34 +887,30 @@ int32_t launched(const char *what) {
     return BSR_OK;
 }
 
-template <int BS, int G, int S, int NW, bool TRANS>
-void launch_gg(const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
-    constexpr int WM = gemm_wave_rows(BS), P = gemm_depth(BS, G, S), BM = NW * WM;
+template <int BS, int G, int NW, bool TRANS>
+void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
+    constexpr int BM = NW * 32;
     const int nmtiles = (int)((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
-    hipLaunchKernelGGL((k_group_gemm<BS, G, S, WM, NW, P, TRANS>), grid, dim3(NW * 64), 0, st, a.act, a.in_ld,
-                       (int)a.M, a.V, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, nmtiles);
+    const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
+    constexpr int NL = kLoaderWaves;
+    hipLaunchKernelGGL((k_panel_gemm<BS, G, G, NW, NL, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
+                       (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles);
 }
 
-// Dispatch on the block size, the schedule's (G, S) and the waves per work-group to the
-// instantiated kernels (see gemm_slot_options; narrow groups also have the 4-wave form).
+// Dispatch on the block size, the schedule's G and the compute waves per work-group to the
+// instantiated kernels (slots per sub-step S = G, see gemm_slots).
 template <bool TRANS>
-int32_t launch_gg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, int nw,
+int32_t launch_pg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, int nw,
                         const FwdArgs &a, hipStream_t st) {
-    const int key = (p.b * 10000 + s.G * 100 + s.S) * 10 + (nw == kGemmWaves ? 0 : 1);
+    if (s.S != s.G) return fail(BSR_ERR_UNSUPPORTED, "no kernel for this slot count");
+    const int key = (p.b * 100 + s.G) * 10 + nw;
     constexpr int W8 = kGemmWaves, W4 = kGemmWavesSmall;
     switch (key) {
-        case 3208020: launch_gg<32, 8, 2, W8, TRANS>(s, d, a, st); break;
-        case 3208040: launch_gg<32, 8, 4, W8, TRANS>(s, d, a, st); break;
-        case 3208080: launch_gg<32, 8, 8, W8, TRANS>(s, d, a, st); break;
-        case 3204020: launch_gg<32, 4, 2, W8, TRANS>(s, d, a, st); break;
-        case 3204040: launch_gg<32, 4, 4, W8, TRANS>(s, d, a, st); break;
-        case 3204021: launch_gg<32, 4, 2, W4, TRANS>(s, d, a, st); break;
-        case 3204041: launch_gg<32, 4, 4, W4, TRANS>(s, d, a, st); break;
-        case 6402010: launch_gg<64, 2, 1, W8, TRANS>(s, d, a, st); break;
-        case 6402020: launch_gg<64, 2, 2, W8, TRANS>(s, d, a, st); break;
-        case 6401010: launch_gg<64, 1, 1, W8, TRANS>(s, d, a, st); break;
-        case 6401011: launch_gg<64, 1, 1, W4, TRANS>(s, d, a, st); break;
+        case 32040 + W8: launch_pg<32, 4, W8, TRANS>(p, s, d, a, st); break;
+        case 32040 + W4: launch_pg<32, 4, W4, TRANS>(p, s, d, a, st); break;
+        case 64010 + W8: launch_pg<64, 1, W8, TRANS>(p, s, d, a, st); break;
+        case 64010 + W4: launch_pg<64, 1, W4, TRANS>(p, s, d, a, st); break;
         default: return fail(BSR_ERR_UNSUPPORTED, "no kernel for this group shape");
     }
     return BSR_OK;
@@ -872,13 +920,17 @@ int32_t launch_gg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevS
 
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    const GemmTile t = choose_tile(p, transposed, a.M);
-    const GroupSchedule &s = (transposed ? p.bwd : p.fwd)[t.k];
-    const DevSchedule &d = (transposed ? p.dev.bwd : p.dev.fwd)[t.k];
-    const int rows = t.nw * gemm_wave_rows(p.b);
+    const int nw = choose_waves(p, transposed, a.M);
+    const GroupSchedule &s = transposed ? p.bwd : p.fwd;
+    const DevSchedule &d = transposed ? p.dev.bwd : p.dev.fwd;
+    const int rows = nw * 32;
     const int64_t nwg = (int64_t)s.ngroups * ((a.M + rows - 1) / rows);
     if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
-    const int32_t rc = transposed ? launch_gg_shape<true>(p, s, d, t.nw, a, st) : launch_gg_shape<false>(p, s, d, t.nw, a, st);
+    if ((size_t)p.nnzb * p.b * p.b * 2 > (size_t)UINT32_MAX)
+        return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
+    if ((int64_t)rows * a.in_ld * 2 > (int64_t)UINT32_MAX)
+        return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
+    const int32_t rc = transposed ? launch_pg_shape<true>(p, s, d, nw, a, st) : launch_pg_shape<false>(p, s, d, nw, a, st);
     if (rc != BSR_OK) return rc;
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }

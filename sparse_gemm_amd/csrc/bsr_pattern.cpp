@@ -44,115 +44,72 @@ std::vector<int32_t> by_count_desc(const std::vector<int32_t> &ptr) {
 }
 
 // Group output blocks (block rows of W for the forward, block columns for the input gradient)
-// G at a time in order of decreasing kept-block count. Each group's steps are the union of the
-// input blocks its members touch, ascending; a member's value block at a step is the block that
-// multiplies that input block into that member. Steps are cut into sub-steps of at most S kept
-// blocks, S chosen among `s_options` to minimise the estimated load instructions (activation tile
-// plus S value blocks per sub-step), then padded and encoded as GroupSchedule records.
+// G at a time in order of decreasing kept-block count, so that a group's members need similar
+// numbers of panels. A group's work list is the activation panels (kPanelCols columns, i.e.
+// kPanelCols / b input blocks) in which any member has a kept block, ascending; the units of a
+// panel (member t, block h inside the panel: unit t * PB + h) that have kept blocks go S at a time
+// into sub-steps, in unit order.
 //   ptr / idx / val: for output block o, entries e in [ptr[o], ptr[o+1]) have input block
 //   idx[e] (ascending) and value block val(e).
 template <class ValFn>
-GroupSchedule make_groups(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val, int b,
-                          int G, const std::vector<int> &s_options) {
+GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val, int b, int G,
+                          int S) {
+    const int PB = kPanelCols / b;
+    const int U = G * PB;
     const int32_t nout = (int32_t)ptr.size() - 1;
     const std::vector<int32_t> ids = by_count_desc(ptr);
-    const int ngroups = (nout + G - 1) / G;
-    // real steps of every group: input block and the members' value blocks
-    std::vector<std::vector<int32_t>> in_of(ngroups), blk_of(ngroups);
-    std::vector<int32_t> outs((size_t)ngroups * G, -1);
-    std::vector<int32_t> cursor(G);
-    for (int32_t g = 0; g < ngroups; ++g) {
-        int members = 0;
-        for (int t = 0; t < G; ++t) {
-            const int32_t k = g * G + t;
-            if (k < nout) {
-                outs[(size_t)g * G + t] = ids[k];
-                cursor[t] = ptr[ids[k]];
-                members++;
-            }
-        }
-        for (;;) {
-            int32_t next_in = INT32_MAX;
-            for (int t = 0; t < members; ++t) {
-                const int32_t o = outs[(size_t)g * G + t];
-                if (cursor[t] < ptr[o + 1]) next_in = std::min(next_in, idx[cursor[t]]);
-            }
-            if (next_in == INT32_MAX) break;
-            in_of[g].push_back(next_in);
-            for (int t = 0; t < G; ++t) {
-                int32_t v = -1;
-                if (t < members) {
-                    const int32_t o = outs[(size_t)g * G + t];
-                    if (cursor[t] < ptr[o + 1] && idx[cursor[t]] == next_in) {
-                        v = val(cursor[t]);
-                        cursor[t]++;
-                    }
-                }
-                blk_of[g].push_back(v);
-            }
-        }
-    }
-    // slots per sub-step: fewest estimated load instructions (1 KB each) per activation row tile
-    const int x_instr = gemm_rows(b) * b * 2 / 1024, w_instr = b * b * 2 / 1024;
-    int best_s = G;
-    double best_cost = 0;
-    for (int S : s_options) {
-        const int P = gemm_depth(b, G, S);
-        double cost = 0;
-        for (int32_t g = 0; g < ngroups; ++g) {
-            const size_t n = in_of[g].size();
-            int64_t subs = 0;
-            for (size_t k = 0; k < n; ++k) {
-                int present = 0;
-                for (int t = 0; t < G; ++t) present += blk_of[g][k * G + t] >= 0;
-                subs += S == G ? 1 : std::max(1, (present + S - 1) / S);
-            }
-            subs = (subs + P - 1) / P * P;
-            cost += (double)subs * (x_instr + S * w_instr);
-        }
-        if (S == s_options.front() || cost < best_cost) {
-            best_cost = cost;
-            best_s = S;
-        }
-    }
     GroupSchedule s;
     s.G = G;
-    s.S = best_s;
-    s.P = gemm_depth(b, G, best_s);
-    const int P = s.P;
-    s.RS = rec_stride(best_s);
-    s.ngroups = ngroups;
-    s.out = outs;
-    s.sub_ptr.assign(ngroups + 1, 0);
-    const int S = s.S, RS = s.RS;
-    for (int32_t g = 0; g < ngroups; ++g) {
-        const size_t n = in_of[g].size();
-        const size_t first = s.rec.size() / RS;
-        for (size_t k = 0; k < n; ++k) {
-            std::vector<int32_t> slots;
-            for (int t = 0; t < G; ++t) {
-                const int32_t v = blk_of[g][k * G + t];
-                if (S == G) slots.push_back(v);
-                else if (v >= 0) slots.push_back(v * 32 + t);
+    s.S = S;
+    s.ngroups = (nout + G - 1) / G;
+    s.out.assign((size_t)s.ngroups * G, -1);
+    s.sub_ptr.assign(s.ngroups + 1, 0);
+    std::vector<int32_t> cursor(G), unit_blk(U);
+    for (int32_t g = 0; g < s.ngroups; ++g) {
+        int members = 0;
+        for (int t = 0; t < G && g * G + t < nout; ++t, ++members) {
+            s.out[(size_t)g * G + t] = ids[g * G + t];
+            cursor[t] = ptr[ids[g * G + t]];
+        }
+        int32_t nsub = 0;
+        for (;;) {
+            int32_t panel = INT32_MAX;
+            for (int t = 0; t < members; ++t) {
+                const int32_t o = s.out[(size_t)g * G + t];
+                if (cursor[t] < ptr[o + 1]) panel = std::min(panel, idx[cursor[t]] / PB);
             }
-            size_t used = 0;
-            do {
-                std::vector<int32_t> r(RS, -1);
-                r[0] = in_of[g][k];
-                for (int q = 0; q < S && used < slots.size(); ++q, ++used) r[1 + q] = slots[used];
+            if (panel == INT32_MAX) break;
+            std::fill(unit_blk.begin(), unit_blk.end(), -1);
+            for (int t = 0; t < members; ++t) {
+                const int32_t o = s.out[(size_t)g * G + t];
+                while (cursor[t] < ptr[o + 1] && idx[cursor[t]] / PB == panel) {
+                    unit_blk[t * PB + idx[cursor[t]] % PB] = val(cursor[t]);
+                    cursor[t]++;
+                }
+            }
+            int u = 0;
+            while (u < U) {
+                std::vector<int32_t> r(kRecInts, -1);
+                r[0] = panel;
+                uint32_t map[2] = {0xffffffffu, 0xffffffffu};
+                int k = 0;
+                for (; u < U && k < S; ++u) {
+                    if (unit_blk[u] < 0) continue;
+                    r[1 + k] = unit_blk[u];
+                    map[u / 8] &= ~(15u << (4 * (u % 8)));
+                    map[u / 8] |= (uint32_t)k << (4 * (u % 8));
+                    ++k;
+                }
+                if (k == 0) break;   // no kept blocks left in this panel
+                r[1 + S] = (int32_t)map[0];
+                r[2 + S] = (int32_t)map[1];
                 s.rec.insert(s.rec.end(), r.begin(), r.end());
-            } while (used < slots.size());
+                ++nsub;
+            }
         }
-        size_t count = s.rec.size() / RS - first;
-        while (count % P) {   // padding: last input block again, no value blocks
-            std::vector<int32_t> r(RS, -1);
-            r[0] = n ? in_of[g][n - 1] : 0;
-            s.rec.insert(s.rec.end(), r.begin(), r.end());
-            count++;
-        }
-        s.sub_ptr[g + 1] = s.sub_ptr[g] + (int32_t)count;
+        s.sub_ptr[g + 1] = s.sub_ptr[g] + nsub;
     }
-    s.order.resize(ngroups);
+    s.order.resize(s.ngroups);
     std::iota(s.order.begin(), s.order.end(), 0);
     std::stable_sort(s.order.begin(), s.order.end(), [&](int32_t a, int32_t b) {
         return s.sub_ptr[a + 1] - s.sub_ptr[a] > s.sub_ptr[b + 1] - s.sub_ptr[b];
@@ -251,12 +208,9 @@ DwSchedule make_dw_items(const bsr_pattern &p) {
 
 void build_pattern(bsr_pattern &p) {
     build_csc(p);
-    const int Gs[2] = {wide_group(p.b), narrow_group(p.b)};
-    for (int k = 0; k < 2; ++k) {
-        const std::vector<int> opts = gemm_slot_options(p.b, Gs[k]);
-        p.fwd[k] = make_groups(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, Gs[k], opts);
-        p.bwd[k] = make_groups(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, Gs[k], opts);
-    }
+    const int G = gemm_group(p.b), S = gemm_slots(p.b, G);
+    p.fwd = make_panels(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, G, S);
+    p.bwd = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, G, S);
     p.dw = make_dw_items(p);
     p.rows_by_nnz = by_count_desc(p.row_ptr);
 }

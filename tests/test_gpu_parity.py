@@ -41,6 +41,20 @@ def test_shapes(M, N, K, b, d, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
+@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("M,N,K,b,seed", [
+    (300, 512, 480, 32, 11),   # 15 block columns: the last 64-column panel is half a panel
+    (300, 512, 448, 64, 12),
+])
+def test_both_tile_heights(monkeypatch, waves, M, N, K, b, seed):
+    """Both work-group heights of the forward / input-gradient kernel (256 and 128 activation
+    rows), whichever the automatic choice would take for this size, over a ragged row tail."""
+    monkeypatch.setenv("BSR_GEMM_WAVES", waves)
+    say(f"case tile waves={waves} M={M} N={N} K={K} b={b} seed={seed}")
+    host = case_inputs(M, N, K, b, seed, density=0.4, bias=True)
+    full_parity(M, N, K, b, host, dbias=True)
+
+
 @pytest.mark.parametrize("b", [32, 64])
 def test_empty_rows_and_columns(b):
     R, C = 6, 5
