@@ -36,8 +36,7 @@ int32_t upload(bsr_pattern &p) {
     std::vector<Part> parts = {
         {&p.row_ptr, &d.row_ptr}, {&p.col_idx, &d.col_idx}, {&p.col_ptr, &d.col_ptr},
         {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.rows_by_nnz, &d.rows_by_nnz},
-        {&p.dw.dense.items, &d.dw_dense}, {&p.dw.runs.items, &d.dw_runs}, {&p.dw.cmap, &d.dw_cmap},
-        {&p.dw.dense_blocks, &d.dw_dense_blocks}, {&p.dw.run_blocks, &d.dw_run_blocks},
+        {&p.dw.items, &d.dw_items},
     };
     for (auto sd : {std::make_pair(&p.fwd, &d.fwd), std::make_pair(&p.bwd, &d.bwd)}) {
         parts.push_back({&sd.first->order, &sd.second->order});

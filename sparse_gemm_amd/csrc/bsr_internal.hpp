@@ -42,28 +42,20 @@ struct GroupSchedule {
     std::vector<int32_t> rec;        // [nsub * kRecInts]
 };
 
-// Weight-gradient work items. An item is a set of up to TR block rows and up to TC block
-// columns; it computes every kept block where they cross, and stages each row's dY slab and each
-// column's X slab once per chunk of M, so a slab is shared by all the item's blocks in its row or
-// column. "Dense" items (TR x TC = 8 x 8 for b = 32, 4 x 4 for b = 64) take row groups' columns
-// that hold kept blocks in at least half of the group's rows; "runs" (one row, up to 4 (b = 32)
-// or 2 (b = 64) columns) take the remaining blocks. Item layout, TS ints: rows[TR] (-1 unused),
-// cols[TC] (-1 unused), blk[TR*TC] (CSR index of the kept block at (row i, column j), -1 if none).
-struct DwShape {
-    int TR, TC;
-    constexpr int TS() const { return (TR + TC + TR * TC + 15) / 16 * 16; }
-};
-constexpr DwShape dw_dense_shape(int b) { return b == 64 ? DwShape{4, 4} : DwShape{8, 8}; }
-constexpr DwShape dw_runs_shape(int b) { return b == 64 ? DwShape{1, 2} : DwShape{1, 4}; }
-
-struct DwItems {
-    int n = 0;
-    std::vector<int32_t> items;   // [n * TS]
-};
+// Weight-gradient work items. A tile is TR consecutive block rows by TC consecutive block columns
+// (TR * b = 256 and TC * b = 512 columns: per activation row, 512 bytes of dY and 1 KB of X, whole
+// cache lines); an item is up to kDwWaves * dw_slots(b) of a tile's kept blocks, each compute wave
+// owning up to dw_slots(b) of them. Item layout, kDwItemInts ints: [0] first block row, [1] first
+// block column, [2 + w] number of blocks of compute wave w, [16 + 8 w + q] block q of wave w:
+// (CSR index << 8) | (row in the tile << 4) | column in the tile.
+constexpr int kDwWaves = 6;
+constexpr int kDwItemInts = 80;
+inline int dw_tile_rows(int b) { return 256 / b; }
+inline int dw_tile_cols(int b) { return 512 / b; }
+inline int dw_slots(int b) { return b == 64 ? 2 : 8; }
 struct DwSchedule {
-    DwItems dense, runs;
-    std::vector<int32_t> cmap;                       // [nnzb] index of the block within its kind
-    std::vector<int32_t> dense_blocks, run_blocks;   // CSR index of each kind's blocks, by that index
+    int n = 0;
+    std::vector<int32_t> items;   // [n * kDwItemInts], most blocks first
 };
 
 struct DevSchedule {
@@ -78,8 +70,7 @@ struct DeviceMeta {
     const int32_t *row_ptr = nullptr, *col_idx = nullptr, *col_ptr = nullptr, *row_idx = nullptr,
                   *perm = nullptr;
     DevSchedule fwd, bwd;
-    const int32_t *dw_dense = nullptr, *dw_runs = nullptr, *dw_cmap = nullptr, *dw_dense_blocks = nullptr,
-                  *dw_run_blocks = nullptr;
+    const int32_t *dw_items = nullptr;
     const int32_t *rows_by_nnz = nullptr;   // small-M forward: block rows, most blocks first
 };
 

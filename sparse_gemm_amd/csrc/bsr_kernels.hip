@@ -458,339 +458,169 @@ __global__ __launch_bounds__(256) void k_small_m(const uint16_t *__restrict__ X,
 // ------------------------------------------------------------------------------------------
 // Weight gradient on the kept blocks (block-masked SDDMM): for block i of row r, column c,
 //   dV[i][p][q] = sum_m dY[m][r*BS + p] * X[m][c*BS + q].
-// Work-group = (item, chunk of M). An item is up to TR block rows x up to TC block columns (see
-// DwSchedule); per stage of KM = 32*KCH rows, each row's dY slab and each column's X slab is staged
-// once in LDS, in its natural m-major layout, and read back transposed with ds_read_b64_tr_b16.
-// The NW waves tile the item's TR x TC grid in WR x WC sub-grids, so a wave's dY fragments serve its
-// WC columns and its X fragments its WR rows. Product orientation (32x32x16 MFMA): A[q][k] =
-// X[m][c*BS + q], B[k][p] = dY[m][r*BS + p], so D[q][p] = dV[p][q] and each lane holds runs of 4
-// consecutive q of one p.
-// Stages are prefetched D deep into registers (rows past the chunk and absent slabs read as zeros)
-// and written to a double-buffered LDS stage one step ahead. FULL items multiply every block of
-// the sub-grid (absent ones are products of real slabs but are never written): no branches around
-// the products, for items that are mostly full. With one chunk of M the sums are
-// rounded to bf16 directly; otherwise fp32 partials go to the workspace for k_dw_reduce.
+// Work-group = (item, chunk of M); an item is up to kDwWaves * SL kept blocks of one tile of TR
+// consecutive block rows by TC consecutive block columns (see DwSchedule). Per stage of KM = 32
+// activation rows, two loader waves stage the tile's dY row segments (TR * BS columns, 512 bytes)
+// and X row segments (TC * BS columns, 1 KB) into LDS with direct-to-LDS loads, three stages
+// deep; every compute wave then runs the products of its blocks from transposing LDS reads:
+//   D[p][q] += A[p][k] . B[k][q],   A[p][k] = dY[m0 + k][r*BS + p],   B[k][q] = X[m0 + k][c*BS + q]
+// (32x32x16 MFMA; lane l ends up with rows 8 (v / 4) + 4 (l / 32) + v % 4 of column l % 32).
+// The 16-byte chunks of each staged row are XOR swizzled by 4 * (row % 4), which keeps the
+// transposing reads (4 rows x 2 chunks per 16 lanes) free of bank conflicts. With one chunk of M
+// the sums are rounded to bf16 directly; otherwise fp32 partials [chunk][block] go to the
+// workspace for k_dw_reduce.
 // ------------------------------------------------------------------------------------------
-template <int BS, int TR, int TC, int WR, int WC, int KCH, int D, bool FULL, int NW>
-__global__ __launch_bounds__(NW * 64) void k_dw_tile(const uint16_t *__restrict__ dY, int N,
-                                                 const uint16_t *__restrict__ X, int K, int M,
-                                                 const int32_t *__restrict__ items, int mchunk, int nchunks,
-                                                 const int32_t *__restrict__ cmap, int nkind,
-                                                 float *__restrict__ partial, uint16_t *__restrict__ dV) {
-    constexpr int NTH = NW * 64;
-    constexpr int WCOLS = TC / WC;            // waves along the item's columns
-    static_assert((TR / WR) * WCOLS == NW && TR % WR == 0 && TC % WC == 0, "waves must tile the item");
-    constexpr int NS = TR + TC;               // staged slabs: dY rows first, then X columns
-    constexpr int KM = 32 * KCH;              // rows per stage
-    constexpr int LD = BS + 8;                // padded slab pitch (elements)
-    constexpr int CPS = KM * BS / 8;          // 16-byte chunks per slab
-    constexpr int LPT = (NS * CPS + NTH - 1) / NTH;   // loads per thread per stage
-    static_assert(CPS % 64 == 0, "a wave's chunks must stay in one slab");
-    constexpr int QT = BS / 32, PT = BS / 32;   // 32x32 output tiles per block
-    constexpr int TS = DwShape{TR, TC}.TS();
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][NS][KM][LD];
+template <int BS, int NL>
+__global__ __launch_bounds__((kDwWaves + NL) * 64) void k_dw_panel(
+    const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X, int K, int M,
+    const int32_t *__restrict__ items, int nitems, int mchunk, float *__restrict__ partial, int nnzb,
+    uint16_t *__restrict__ dV) {
+    constexpr int NW = kDwWaves;
+    constexpr int SL = BS == 64 ? 2 : 8;        // blocks per compute wave (dw_slots)
+    constexpr int NT = BS / 32;                 // 32 x 32 sub-tiles per block side
+    constexpr int KM = 32;                      // activation rows per stage
+    constexpr int DB = 512, XR = 1024;          // bytes per staged row: dY segment, X segment
+    constexpr int DS = KM * DB, XS = KM * XR;
+    constexpr int STAGE = DS + XS;
+    constexpr int NST = 3;
+    constexpr int DPL = KM / 2 / NL;            // dY loads (2 rows each) per loader wave and stage
+    constexpr int XPL = KM / NL;                // X loads (1 row each) per loader wave and stage
+    constexpr int NLD = DPL + XPL;
+    static_assert(KM / 2 % NL == 0 && KM % NL == 0 && 2 * NLD <= 63, "loader split");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
-    const int item = blockIdx.x / nchunks, ch = blockIdx.x % nchunks;
-    const int32_t *it = items + (size_t)item * TS;
+    const int item = blockIdx.x % nitems, ch = blockIdx.x / nitems;
+    const int32_t *it = items + (size_t)item * kDwItemInts;
+    const int r0 = it[0], c0 = it[1];
+    const int m_begin = ch * mchunk, m_end = min(M, m_begin + mchunk);
+    const int nst = (m_end - m_begin + KM - 1) / KM;   // mchunk is a multiple of KM
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= NW;
+    const int lw = wave - NW;
     const int l32 = lane & 31, lh = lane >> 5;
-    const int wr = wave / WCOLS, wc = wave % WCOLS;
-    const int m_begin = ch * mchunk;
-    const int m_end = min(M, m_begin + mchunk);
-    const int nst = ((m_end - m_begin + KM - 1) / KM + D - 1) / D * D;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dY, (uint32_t)((size_t)M * N * 2));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const uint32_t sbase = lds_addr(smem);
 
-    // This thread's staging chunks: slab (uniform per wave: a dY row first, then X columns) and
-    // its byte offset inside the slab.
-    int sid[LPT];
-    uint32_t svoff[LPT];
+    // loads of one stage (activation rows m0 .. m0 + KM - 1) into stage st: staged chunk c of row
+    // `row` holds source chunk c ^ 4 (row % 4). Offsets stay in the range-checked voffset, so rows
+    // past M and columns past the matrix end read as zeros.
+    auto issue = [&](int st, int m0) __attribute__((always_inline)) {
+        const uint32_t base = sbase + (uint32_t)st * STAGE;
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-        const int slab = (j * NTH + wave * 64) / CPS;
-        const int w = (tid + j * NTH) % CPS, row = w / (BS / 8), c8 = (w % (BS / 8)) * 8;
-        sid[j] = slab < NS ? it[slab] : -1;
-        svoff[j] = (uint32_t)(row * (slab < TR ? N : K) + c8) * 2;
+        for (int d = 0; d < DPL; ++d) {
+            const int ins = lw + NL * d, row = 2 * ins + (lane >> 5);
+            const uint32_t voff = (uint32_t)(m0 + row) * (uint32_t)N * 2u + (uint32_t)r0 * BS * 2u +
+                                  (uint32_t)(((lane & 31) ^ ((row & 3) << 2)) << 4);
+            dma16(rd, base + (uint32_t)ins * 1024u, voff, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < XPL; ++x) {
+            const int row = lw + NL * x;
+            const uint32_t voff = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)c0 * BS * 2u +
+                                  (uint32_t)((lane ^ ((row & 3) << 2)) << 4);
+            dma16(rx, base + DS + (uint32_t)row * 1024u, voff, 0);
+        }
+    };
+
+    // T[k0 + 8 (l / 32) .. + 7][n0 + l % 32] of a staged tile (rows of `pitch` bytes), for lane l:
+    // two transposing reads of 4 rows; lane s of a 16-lane group points at row R + s / 4, columns
+    // C .. C + 3 (8 bytes inside one 16-byte chunk)
+    auto frag = [&](const unsigned char *t, int pitch, int k0, int n0) __attribute__((always_inline)) {
+        const int gq = lane >> 4, s16 = lane & 15;
+        const int R = k0 + (gq >> 1) * 8 + (s16 >> 2);
+        const int C = n0 + (gq & 1) * 16 + 4 * (s16 & 3);
+        auto at = [&](int row) {
+            return (lds_i16x4 *)(t + row * pitch + ((((C >> 3) ^ ((row & 3) << 2)) << 4) | ((C & 7) << 1)));
+        };
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    int nq = 0, word[SL];
+    if (!loader) {
+        nq = it[2 + wave];
+#pragma unroll
+        for (int q = 0; q < SL; ++q) word[q] = it[16 + 8 * wave + q];
     }
-    // kept blocks of this wave's sub-grid: bit i*WC + j
-    uint32_t present = 0;
+    f32x16 acc[SL][NT][NT];
 #pragma unroll
-    for (int i = 0; i < WR; ++i)
+    for (int q = 0; q < SL; ++q)
 #pragma unroll
-        for (int j = 0; j < WC; ++j)
-            if (it[TR + TC + (wr * WR + i) * TC + wc * WC + j] >= 0) present |= 1u << (i * WC + j);
+        for (int pt = 0; pt < NT; ++pt)
+#pragma unroll
+            for (int qt = 0; qt < NT; ++qt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[q][pt][qt][v] = 0.f;
 
-    f32x16 acc[WR][WC][QT][PT];
+    auto compute = [&](int st) __attribute__((always_inline)) {
+        const unsigned char *dt = smem + st * STAGE, *xt = dt + DS;
 #pragma unroll
-    for (int i = 0; i < WR; ++i)
+        for (int q = 0; q < SL; ++q) {
+            if (q >= nq) break;
+            const int i = (word[q] >> 4) & 15, j = word[q] & 15;
 #pragma unroll
-        for (int j = 0; j < WC; ++j)
+            for (int kc = 0; kc < KM / 16; ++kc) {
+                bf16x8 a[NT], bq[NT];
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
+                for (int pt = 0; pt < NT; ++pt) a[pt] = frag(dt, DB, kc * 16, i * BS + pt * 32);
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
+                for (int qt = 0; qt < NT; ++qt) bq[qt] = frag(xt, XR, kc * 16, j * BS + qt * 32);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][qt][pt][v] = 0.f;
-
-    u32x4 ring[D][LPT];
-    auto load_stage = [&](u32x4(&slot)[LPT], int st) __attribute__((always_inline)) {
-        const int ms = m_begin + st * KM;
-        const int rows = max(0, min(KM, m_end - ms));
+                for (int pt = 0; pt < NT; ++pt)
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            const int slab = (j * NTH + wave * 64) / CPS;
-            const int ld = slab < TR ? N : K;
-            const bool ok = sid[j] >= 0 && rows > 0;
-            const uint16_t *base = (slab < TR ? dY : X) + (int64_t)ms * ld + (int64_t)max(sid[j], 0) * BS;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(ok ? base : dY, ok ? (uint32_t)rows * ld * 2 : 0);
-            slot[j] = buf_load16u(r, svoff[j], 0);
+                    for (int qt = 0; qt < NT; ++qt) acc[q][pt][qt] = mfma32(a[pt], bq[qt], acc[q][pt][qt]);
+            }
         }
     };
-    auto store_stage = [&](int buf, const u32x4(&slot)[LPT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            const int slab = (j * NTH + wave * 64) / CPS;
-            if (slab >= NS) continue;   // uniform per wave
-            const int w = (tid + j * NTH) % CPS, row = w / (BS / 8), c8 = (w % (BS / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&lds[buf][slab][row][c8]) = slot[j];
+
+    if (loader) {
+        issue(0, m_begin);
+        if (nst > 1) issue(1, m_begin + KM);
+    }
+    int st = 0;
+    for (int s = 0; s < nst; ++s) {
+        if (loader) {
+            if (s + 1 < nst) wait_vm<NLD, NLD>(NLD);   // this loader's loads of stage s have landed
+            else wait_vm<0, 0>(0);
         }
-    };
-    auto compute = [&](int buf) __attribute__((always_inline)) {
+        __syncthreads();   // everyone's have; nobody reads the stage of s - 1 any more
+        if (loader && s + 2 < nst) issue(st == 0 ? 2 : st - 1, m_begin + (s + 2) * KM);
+        if (!loader) compute(st);
+        st = st == 2 ? 0 : st + 1;
+    }
+    if (loader) return;
+
+    // item v of lane l: row pt*32 + 8 (v / 4) + 4 (l / 32) + v % 4, column qt*32 + l % 32
 #pragma unroll
-        for (int kk = 0; kk < 2 * KCH; ++kk) {   // 16 rows of the stage per product
-            const int k0 = kk * 16;
-            bf16x8 bq[WR][PT];
+    for (int q = 0; q < SL; ++q) {
+        if (q >= nq) break;
+        const int blk = word[q] >> 8;
 #pragma unroll
-            for (int i = 0; i < WR; ++i)
+        for (int pt = 0; pt < NT; ++pt)
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) bq[i][pt] = lds_read_tr8_32(&lds[buf][wr * WR + i][0][0], LD, k0, pt * 32, lane);
+            for (int qt = 0; qt < NT; ++qt)
 #pragma unroll
-            for (int j = 0; j < WC; ++j) {
-                uint32_t colmask = 0;
-#pragma unroll
-                for (int i = 0; i < WR; ++i) colmask |= 1u << (i * WC + j);
-                if (!FULL && !(present & colmask)) continue;   // uniform per wave
-                bf16x8 aq[QT];
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt)
-                    aq[qt] = lds_read_tr8_32(&lds[buf][TR + wc * WC + j][0][0], LD, k0, qt * 32, lane);
-#pragma unroll
-                for (int i = 0; i < WR; ++i) {
-                    if (!FULL && !((present >> (i * WC + j)) & 1)) continue;
-#pragma unroll
-                    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) acc[i][j][qt][pt] = mfma32(aq[qt], bq[i][pt], acc[i][j][qt][pt]);
+                for (int v = 0; v < 16; ++v) {
+                    const int pp = pt * 32 + 8 * (v / 4) + 4 * lh + v % 4, qq = qt * 32 + l32;
+                    const size_t e = (size_t)pp * BS + qq;
+                    if (partial) partial[((size_t)ch * nnzb + blk) * BS * BS + e] = acc[q][pt][qt][v];
+                    else dV[(size_t)blk * BS * BS + e] = to_bf16(acc[q][pt][qt][v]);
                 }
-            }
-        }
-    };
-
-#pragma unroll
-    for (int u = 0; u < D; ++u) load_stage(ring[u], u);
-    store_stage(0, ring[0]);
-    __builtin_amdgcn_s_waitcnt(0);   // drain: the loop's wait counts then hold on entry too
-    __syncthreads();
-    for (int st = 0; st < nst; st += D) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int cs = st + u;
-            const int buf = cs & 1;
-            compute(buf);
-            store_stage(buf ^ 1, ring[(u + 1) % D]);   // stage cs + 1, loaded D - 1 stages ago
-            load_stage(ring[u], cs + D);
-            __syncthreads();
-        }
-    }
-
-    // Write the blocks: item v of lane l is q = qt*32 + 8*(v/4) + 4*(l/32) + v%4, p = pt*32 + l%32.
-#pragma unroll
-    for (int i = 0; i < WR; ++i)
-#pragma unroll
-        for (int j = 0; j < WC; ++j) {
-            const int e = it[TR + TC + (wr * WR + i) * TC + wc * WC + j];
-            if (e < 0) continue;
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                    for (int vq = 0; vq < 4; ++vq) {
-                        const int in = (pt * 32 + l32) * BS + qt * 32 + vq * 8 + lh * 4;
-                        const f32x4 v = quad(acc[i][j][qt][pt], vq);
-                        if (nchunks == 1)
-                            store4_bf16(dV + (size_t)e * BS * BS + in, v[0], v[1], v[2], v[3]);
-                        else
-                            *reinterpret_cast<f32x4 *>(partial + ((size_t)ch * nkind + cmap[e]) * BS * BS + in) = v;
-                    }
-        }
-}
-
-// ------------------------------------------------------------------------------------------
-// Weight gradient, runs: an item of one block row r and up to GB of its kept blocks (columns
-// cols[j], CSR index blk[j]). Per stage of KM = 32*NW rows, the row's dY slab and the blocks' X
-// slabs are staged in LDS (m-major) and read back transposed; wave w takes rows [32w, 32w + 32)
-// of the stage for every block of the run, so its dY fragments serve all the run's blocks. The
-// next stage's loads (rows past the chunk and absent blocks read as zeros) are issued into
-// registers before the current stage computes. At the end the waves' partial sums are added in
-// LDS in wave order. Orientation and output as in k_dw_tile.
-// ------------------------------------------------------------------------------------------
-template <int BS, int GB>
-struct DwRunShape {
-    static constexpr int NW = 4;
-    static constexpr int KM = 32 * NW;           // rows per stage
-    static constexpr int LD = BS + 8;            // padded slab pitch (elements)
-    static constexpr int SLAB = KM * LD;         // elements per staged slab
-    static constexpr int RLD = BS + 4;           // padded pitch of the reduction tile (floats)
-    static constexpr size_t STAGE_BYTES = (size_t)(1 + GB) * SLAB * 2;
-    static constexpr size_t RED_BYTES = (size_t)NW * BS * RLD * 4;
-    static constexpr size_t LDS_BYTES = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
-};
-
-template <int BS, int GB>
-__global__ __launch_bounds__(256) void k_dw_runs(const uint16_t *__restrict__ dY, int N,
-                                                 const uint16_t *__restrict__ X, int K, int M,
-                                                 const int32_t *__restrict__ items, int mchunk, int nchunks,
-                                                 const int32_t *__restrict__ cmap, int nkind,
-                                                 float *__restrict__ partial, uint16_t *__restrict__ dV) {
-    using S = DwRunShape<BS, GB>;
-    constexpr int NW = S::NW, KM = S::KM, LD = S::LD, SLAB = S::SLAB, RLD = S::RLD;
-    constexpr int QT = BS / 32, PT = BS / 32;   // 32x32 output tiles per block
-    constexpr int CPR = BS / 8;                  // 16-byte chunks per slab row
-    constexpr int CPS = KM * CPR / (NW * 64);    // chunks per thread per slab
-    constexpr int TS = DwShape{1, GB}.TS();
-    static_assert((KM * CPR) % (NW * 64) == 0, "slab staging must divide evenly");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
-    uint16_t *sdy = reinterpret_cast<uint16_t *>(smem);   // [KM][LD]
-    uint16_t *sx = sdy + SLAB;                             // [GB][KM][LD]
-
-    const int item = blockIdx.x / nchunks, ch = blockIdx.x % nchunks;
-    const int32_t *it = items + (size_t)item * TS;
-    const int r = it[0];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, lh = lane >> 5;
-    const int m_begin = ch * mchunk;
-    const int m_end = min(M, m_begin + mchunk);
-
-    int col[GB];
-    uint32_t present = 0;
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        col[j] = it[1 + j];
-        if (it[1 + GB + j] >= 0) present |= 1u << j;
-    }
-
-    f32x16 acc[GB][QT][PT];
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[j][qt][pt][v] = 0.f;
-
-    u32x4 ry[CPS], rx[GB][CPS];
-    auto load_stage = [&](int ms) __attribute__((always_inline)) {
-        const uint32_t rows = (uint32_t)max(0, min(KM, m_end - ms));
-        const __amdgpu_buffer_rsrc_t rdy = make_rsrc(dY + (int64_t)ms * N + r * BS, rows * N * 2);
-#pragma unroll
-        for (int k = 0; k < CPS; ++k) {
-            const int e = tid + k * NW * 64, row = e / CPR, c8 = (e % CPR) * 8;
-            ry[k] = buf_load16u(rdy, (uint32_t)(row * N + c8) * 2, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < GB; ++j) {
-            const bool ok = col[j] >= 0;
-            const __amdgpu_buffer_rsrc_t rxj =
-                make_rsrc(X + (int64_t)ms * K + (int64_t)max(col[j], 0) * BS, ok ? rows * K * 2 : 0);
-#pragma unroll
-            for (int k = 0; k < CPS; ++k) {
-                const int e = tid + k * NW * 64, row = e / CPR, c8 = (e % CPR) * 8;
-                rx[j][k] = buf_load16u(rxj, (uint32_t)(row * K + c8) * 2, 0);
-            }
-        }
-    };
-    auto store_stage = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < CPS; ++k) {
-            const int e = tid + k * NW * 64, row = e / CPR, c8 = (e % CPR) * 8;
-            *reinterpret_cast<u32x4 *>(sdy + row * LD + c8) = ry[k];
-#pragma unroll
-            for (int j = 0; j < GB; ++j) *reinterpret_cast<u32x4 *>(sx + j * SLAB + row * LD + c8) = rx[j][k];
-        }
-    };
-
-    load_stage(m_begin);
-    for (int ms = m_begin; ms < m_end; ms += KM) {
-        __syncthreads();   // the previous stage's LDS reads are done
-        store_stage();
-        __syncthreads();
-        load_stage(ms + KM);   // past the chunk: zeros, never used
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {   // this wave's 32 rows, 16 per product
-            const int k0 = wave * 32 + kk * 16;
-            bf16x8 bq[PT];
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) bq[pt] = lds_read_tr8_32(sdy, LD, k0, pt * 32, lane);
-#pragma unroll
-            for (int j = 0; j < GB; ++j) {
-                if (!((present >> j) & 1)) continue;   // uniform
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) {
-                    const bf16x8 aq = lds_read_tr8_32(sx + j * SLAB, LD, k0, qt * 32, lane);
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[j][qt][pt] = mfma32(aq, bq[pt], acc[j][qt][pt]);
-                }
-            }
-        }
-    }
-
-    // Sum the waves' partials block by block: wave w writes red[w][p][q], then every thread adds
-    // four consecutive q over w = 0..NW-1.
-    float *red = reinterpret_cast<float *>(smem);
-    constexpr int EPT = BS * BS / (NW * 64);   // output elements per thread per block
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        const int e_blk = it[1 + GB + j];
-        if (e_blk < 0) continue;   // uniform
-        __syncthreads();
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int vq = 0; vq < 4; ++vq)
-                    *reinterpret_cast<f32x4 *>(red + (wave * BS + pt * 32 + l32) * RLD + qt * 32 + vq * 8 + lh * 4) =
-                        quad(acc[j][qt][pt], vq);
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < EPT / 4; ++k) {
-            const int e = (tid + k * NW * 64) * 4, p = e / BS, q = e % BS;
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(red + p * RLD + q);
-#pragma unroll
-            for (int w = 1; w < NW; ++w) sum += *reinterpret_cast<const f32x4 *>(red + (w * BS + p) * RLD + q);
-            if (nchunks == 1)
-                store4_bf16(dV + (size_t)e_blk * BS * BS + e, sum[0], sum[1], sum[2], sum[3]);
-            else
-                *reinterpret_cast<f32x4 *>(partial + ((size_t)ch * nkind + cmap[e_blk]) * BS * BS + e) = sum;
-        }
     }
 }
 
-// Sums the per-chunk fp32 partials of one kind of work item in chunk order and rounds to bf16
-// (4 elements per thread). partial is [nchunks][nblocks][bb]; block k of the kind is CSR block
-// blocks[k].
-__global__ __launch_bounds__(256) void k_dw_reduce(const float *__restrict__ partial, int nchunks,
-                                                   const int32_t *__restrict__ blocks, int nblocks, int bb,
+// dV[b][e] = bf16(sum over chunks of partial[chunk][b][e]), 4 elements per thread.
+__global__ __launch_bounds__(256) void k_dw_reduce(const float *__restrict__ partial, int nchunks, size_t count,
                                                    uint16_t *__restrict__ dV) {
     const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    const size_t count = (size_t)nblocks * bb;
     if (e >= count) return;
     f32x4 s = *reinterpret_cast<const f32x4 *>(partial + e);
     for (int ch = 1; ch < nchunks; ++ch) s += *reinterpret_cast<const f32x4 *>(partial + (size_t)ch * count + e);
-    const size_t k = e / bb;
-    store4_bf16(dV + (size_t)blocks[k] * bb + (e - k * bb), s[0], s[1], s[2], s[3]);
+    store4_bf16(dV + e, s[0], s[1], s[2], s[3]);
 }
 
 // Bias gradient, pass 1: column sums of dY over one chunk of rows -> fp32 partials.
@@ -834,49 +664,32 @@ int choose_waves(const bsr_pattern &p, bool transposed, int64_t M) {
     return (int64_t)s.ngroups * tiles >= 2 * kCUs ? kGemmWaves : kGemmWavesSmall;
 }
 
-// M-split of one kind of weight-gradient item.
-struct DwSplit {
-    int nchunks = 1, mchunk = 0;
-    size_t off = 0, bytes = 0;   // fp32 partials in the workspace (only when nchunks > 1)
-};
-
+// Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage) so that items x
+// chunks give every CU a work-group, with chunks of at least 256 rows (each chunk beyond the first
+// costs an fp32 partial of every block and its share of the reduction); workspace layout.
 struct DwPlan {
-    DwSplit dense, runs;
-    int bchunks = 1;        // row chunks of the bias column sums
+    int nchunks = 1, mchunk = 0;
+    size_t partial_bytes = 0;   // [nchunks][nnzb][b*b] fp32, only when nchunks > 1
+    int bchunks = 1;            // row chunks of the bias column sums
     int64_t brows = 0;
     size_t bias_off = 0, bias_bytes = 0, total = 0;
 };
 
-// Enough chunks of M for `slots` work-groups from n items, chunks of at least min_rows rows
-// (each split costs an fp32 partial of the kind's blocks).
-DwSplit split_m(int64_t M, int n, int64_t slots, int64_t min_rows) {
-    DwSplit s;
-    if (n <= 0) return s;
-    const int64_t want = (slots + n - 1) / n;
-    const int64_t maxc = std::max<int64_t>(1, M / min_rows);
-    s.nchunks = (int)std::max<int64_t>(1, std::min(want, maxc));
-    s.mchunk = (int)(((M + s.nchunks - 1) / s.nchunks + 127) / 128 * 128);
-    s.nchunks = (int)((M + s.mchunk - 1) / s.mchunk);
-    return s;
-}
-
 DwPlan plan_dw(const bsr_pattern &p, int64_t M) {
     DwPlan d;
     if (M <= 0) return d;
-    // dense items: one 8-wave work-group per CU; runs: three 4-wave work-groups per CU
-    d.dense = split_m(M, p.dw.dense.n, kCUs, 256);
-    d.runs = split_m(M, p.dw.runs.n, 3 * kCUs, 512);
+    const int64_t n = std::max(p.dw.n, 1);
+    const int64_t want = (kCUs + n - 1) / n;
+    d.nchunks = (int)std::max<int64_t>(1, std::min(want, M / 256));
+    d.mchunk = (int)(((M + d.nchunks - 1) / d.nchunks + 31) / 32 * 32);
+    d.nchunks = (int)((M + d.mchunk - 1) / d.mchunk);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    const size_t bb = (size_t)p.b * p.b * sizeof(float);
-    d.dense.bytes = d.dense.nchunks > 1 ? (size_t)d.dense.nchunks * p.dw.dense_blocks.size() * bb : 0;
-    d.runs.bytes = d.runs.nchunks > 1 ? (size_t)d.runs.nchunks * p.dw.run_blocks.size() * bb : 0;
-    d.dense.off = 0;
-    d.runs.off = al(d.dense.bytes);
+    d.partial_bytes = d.nchunks > 1 ? (size_t)d.nchunks * p.nnzb * p.b * p.b * sizeof(float) : 0;
     d.bchunks = (int)std::min<int64_t>(64, std::max<int64_t>(1, M / 256));
     d.brows = (M + d.bchunks - 1) / d.bchunks;
     d.bchunks = (int)((M + d.brows - 1) / d.brows);
     d.bias_bytes = (size_t)d.bchunks * p.N * sizeof(float);
-    d.bias_off = d.runs.off + al(d.runs.bytes);
+    d.bias_off = al(d.partial_bytes);
     d.total = d.bias_off + al(d.bias_bytes);
     return d;
 }
@@ -963,31 +776,23 @@ int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream) {
     }
     const DwPlan pl = plan_dw(p, a.M);
     char *ws = static_cast<char *>(a.ws);
+    if ((size_t)(a.M + 32) * p.N * 2 > (size_t)UINT32_MAX || (size_t)(a.M + 32) * p.K * 2 > (size_t)UINT32_MAX)
+        return fail(BSR_ERR_INVALID_ARG, "activations above 4 GiB for 32-bit buffer offsets");
     if (p.nnzb > 0) {
-        const DwArgs &x = a;
-        auto launch = [&](auto kernel, int nthreads, int n, const int32_t *items, const DwSplit &sp, int nkind) {
-            if (n == 0) return;
-            float *partial = sp.nchunks > 1 ? reinterpret_cast<float *>(ws + sp.off) : nullptr;
-            hipLaunchKernelGGL(kernel, dim3((unsigned)((int64_t)n * sp.nchunks)), dim3(nthreads), 0, st, x.dY, p.N, x.X,
-                               p.K, (int)x.M, items, sp.mchunk, sp.nchunks, d.dw_cmap, nkind, partial, x.dV);
-        };
-        const int nd = (int)p.dw.dense_blocks.size(), nr = (int)p.dw.run_blocks.size();
-        if (p.b == 32) {
-            launch(k_dw_tile<32, 8, 8, 4, 2, 1, 2, true, 8>, 512, p.dw.dense.n, d.dw_dense, pl.dense, nd);
-            launch(k_dw_runs<32, 4>, 256, p.dw.runs.n, d.dw_runs, pl.runs, nr);
-        } else {
-            launch(k_dw_tile<64, 4, 4, 2, 1, 1, 2, true, 8>, 512, p.dw.dense.n, d.dw_dense, pl.dense, nd);
-            launch(k_dw_runs<64, 2>, 256, p.dw.runs.n, d.dw_runs, pl.runs, nr);
+        float *partial = pl.nchunks > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+        const dim3 grid((unsigned)((int64_t)p.dw.n * pl.nchunks));
+        constexpr int NL = kLoaderWaves, NT = (kDwWaves + NL) * 64;
+        if (p.b == 32)
+            hipLaunchKernelGGL((k_dw_panel<32, NL>), grid, dim3(NT), 0, st, a.dY, p.N, a.X, p.K, (int)a.M, d.dw_items,
+                               p.dw.n, pl.mchunk, partial, p.nnzb, a.dV);
+        else
+            hipLaunchKernelGGL((k_dw_panel<64, NL>), grid, dim3(NT), 0, st, a.dY, p.N, a.X, p.K, (int)a.M, d.dw_items,
+                               p.dw.n, pl.mchunk, partial, p.nnzb, a.dV);
+        if (partial) {
+            const size_t count = (size_t)p.nnzb * p.b * p.b;
+            hipLaunchKernelGGL(k_dw_reduce, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, st, partial,
+                               pl.nchunks, count, a.dV);
         }
-        const int bb = p.b * p.b;
-        auto reduce = [&](const DwSplit &sp, const int32_t *blocks, int nblk) {
-            if (sp.nchunks <= 1 || nblk == 0) return;
-            const size_t count = (size_t)nblk * bb;
-            hipLaunchKernelGGL(k_dw_reduce, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, st,
-                               reinterpret_cast<const float *>(ws + sp.off), sp.nchunks, blocks, nblk, bb, a.dV);
-        };
-        reduce(pl.dense, d.dw_dense_blocks, nd);
-        reduce(pl.runs, d.dw_run_blocks, nr);
     }
     if (a.dbias) {
         float *bp = reinterpret_cast<float *>(ws + pl.bias_off);

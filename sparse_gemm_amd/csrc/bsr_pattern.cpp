@@ -117,90 +117,39 @@ GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int
     return s;
 }
 
-// Weight-gradient items. Block rows are taken in groups of TR, most kept blocks first. Inside a
-// group, a column holding kept blocks in at least half of the group's rows costs one shared X slab
-// in a dense item instead of one slab per block in runs (and the dense kernel multiplies every
-// block of its grid, so it wants items at least half full); those columns go to dense items, TC
-// at a time. Every other kept block goes to a run of its own row (TC_run columns at a time).
-// Items with more blocks come first.
+// Weight-gradient items: the kept blocks of every tile (dw_tile_rows x dw_tile_cols block
+// positions) in row-major order, at most kDwWaves * dw_slots blocks per item (a fuller tile makes
+// several items), spread over the compute waves in contiguous runs as even as possible (blocks of
+// one run mostly share a row). Items with more blocks come first.
 DwSchedule make_dw_items(const bsr_pattern &p) {
-    const DwShape D = dw_dense_shape(p.b), Rn = dw_runs_shape(p.b);
-    std::vector<std::pair<int32_t, std::vector<int32_t>>> dense, runs;   // (blocks, item)
-    const std::vector<int32_t> rows = by_count_desc(p.row_ptr);
-    std::vector<int32_t> pos(p.C, -1);   // CSR index of (row, column) for the current row
-    std::vector<int32_t> count(p.C, 0);
-    for (size_t g0 = 0; g0 < rows.size(); g0 += D.TR) {
-        const int nr = (int)std::min<size_t>(D.TR, rows.size() - g0);
-        std::fill(count.begin(), count.end(), 0);
-        for (int i = 0; i < nr; ++i) {
-            const int32_t r = rows[g0 + i];
-            for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) count[p.col_idx[e]]++;
-        }
-        const int need = std::max(2, (nr + 1) / 2);
-        std::vector<int32_t> dcols;
-        for (int32_t c = 0; c < p.C; ++c)
-            if (count[c] >= need) dcols.push_back(c);
-        // dense items over the shared columns
-        for (size_t c0 = 0; c0 < dcols.size(); c0 += D.TC) {
-            const int nc = (int)std::min<size_t>(D.TC, dcols.size() - c0);
-            std::vector<int32_t> it(D.TS(), -1);
-            int nblk = 0;
-            for (int i = 0; i < nr; ++i) it[i] = rows[g0 + i];
-            for (int j = 0; j < nc; ++j) it[D.TR + j] = dcols[c0 + j];
-            for (int i = 0; i < nr; ++i) {
-                const int32_t r = rows[g0 + i];
-                for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) pos[p.col_idx[e]] = e;
-                for (int j = 0; j < nc; ++j) {
-                    const int32_t e = pos[dcols[c0 + j]];
-                    it[D.TR + D.TC + i * D.TC + j] = e;
-                    nblk += e >= 0;
+    const int TR = dw_tile_rows(p.b), TC = dw_tile_cols(p.b), SL = dw_slots(p.b), cap = kDwWaves * SL;
+    std::vector<std::pair<int32_t, std::vector<int32_t>>> items;
+    std::vector<int32_t> blk;   // (CSR index << 8) | (i << 4) | j, row-major inside the tile
+    for (int32_t r0 = 0; r0 < p.R; r0 += TR) {
+        for (int32_t c0 = 0; c0 < p.C; c0 += TC) {
+            blk.clear();
+            for (int32_t r = r0; r < std::min(p.R, r0 + TR); ++r)
+                for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e)
+                    if (p.col_idx[e] >= c0 && p.col_idx[e] < c0 + TC)
+                        blk.push_back((e << 8) | ((r - r0) << 4) | (p.col_idx[e] - c0));
+            for (size_t f = 0; f < blk.size(); f += cap) {
+                const int n = (int)std::min<size_t>(cap, blk.size() - f);
+                std::vector<int32_t> it(kDwItemInts, 0);
+                it[0] = r0;
+                it[1] = c0;
+                for (int w = 0; w < kDwWaves; ++w) {
+                    const int q0 = n * w / kDwWaves, q1 = n * (w + 1) / kDwWaves;
+                    it[2 + w] = q1 - q0;
+                    for (int q = q0; q < q1; ++q) it[16 + 8 * w + (q - q0)] = blk[f + q];
                 }
-                for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) pos[p.col_idx[e]] = -1;
-            }
-            dense.emplace_back(nblk, std::move(it));
-        }
-        // runs over the other blocks of each row
-        for (int i = 0; i < nr; ++i) {
-            const int32_t r = rows[g0 + i];
-            std::vector<int32_t> rest;
-            for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e)
-                if (count[p.col_idx[e]] < need) rest.push_back(e);
-            for (size_t k0 = 0; k0 < rest.size(); k0 += Rn.TC) {
-                const int nc = (int)std::min<size_t>(Rn.TC, rest.size() - k0);
-                std::vector<int32_t> it(Rn.TS(), -1);
-                it[0] = r;
-                for (int j = 0; j < nc; ++j) {
-                    it[1 + j] = p.col_idx[rest[k0 + j]];
-                    it[1 + Rn.TC + j] = rest[k0 + j];
-                }
-                runs.emplace_back(nc, std::move(it));
+                items.emplace_back(n, std::move(it));
             }
         }
     }
-    auto pack = [](std::vector<std::pair<int32_t, std::vector<int32_t>>> &v) {
-        std::stable_sort(v.begin(), v.end(), [](const auto &a, const auto &b) { return a.first > b.first; });
-        DwItems out;
-        out.n = (int)v.size();
-        for (auto &x : v) out.items.insert(out.items.end(), x.second.begin(), x.second.end());
-        return out;
-    };
+    std::stable_sort(items.begin(), items.end(), [](const auto &a, const auto &b) { return a.first > b.first; });
     DwSchedule s;
-    s.dense = pack(dense);
-    s.runs = pack(runs);
-    // compact per-kind block numbering (for the split-M partial sums)
-    s.cmap.assign(p.nnzb, -1);
-    auto number = [&](const DwItems &v, int TS, int first_blk, int nblk, std::vector<int32_t> &list) {
-        for (int k = 0; k < v.n; ++k)
-            for (int q = 0; q < nblk; ++q) {
-                const int32_t e = v.items[(size_t)k * TS + first_blk + q];
-                if (e >= 0) {
-                    s.cmap[e] = (int32_t)list.size();
-                    list.push_back(e);
-                }
-            }
-    };
-    number(s.dense, D.TS(), D.TR + D.TC, D.TR * D.TC, s.dense_blocks);
-    number(s.runs, Rn.TS(), Rn.TR + Rn.TC, Rn.TR * Rn.TC, s.run_blocks);
+    s.n = (int)items.size();
+    for (auto &x : items) s.items.insert(s.items.end(), x.second.begin(), x.second.end());
     return s;
 }
 
