@@ -371,24 +371,40 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
             st = st == 2 ? 0 : st + 1;
         }
     }
+    // Epilogue, through LDS: each compute wave writes its 32 rows x G*BS columns (bias added, bf16)
+    // into a region of its own, then stores them as 16-byte pieces, 64 lanes covering whole
+    // 64-byte block rows (instead of 8-byte pieces spread over 32 rows).
+    __syncthreads();   // every wave is done with the stages
     if (loader) return;
-
-    // Epilogue: item v of lane l is output column nt*32 + 8*(v/4) + 4*(l/32) + v%4 of the block,
-    // activation row l%32 of the wave.
-    const int m = mt0 * BM + wave * 32 + l32;
+    constexpr int OC = G * BS;              // output columns of the work-group
+    constexpr int OP = OC * 2 + 16;         // LDS pitch of a staged output row (bytes)
+    static_assert(NW * 32 * OP <= NST * STAGE, "output staging fits in the stages");
+    unsigned char *ot = smem + wave * 32 * OP;
+    const int m0 = mt0 * BM + wave * 32;
+    // item v of lane l is output column nt*32 + 8*(v/4) + 4*(l/32) + v%4 of member t, row l%32
 #pragma unroll
     for (int t = 0; t < G; ++t) {
         const int o = gout[g * G + t];
-        if (o < 0 || m >= M) continue;
+        if (o < 0) continue;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = o * BS + nt * 32 + q * 8 + lh * 4;
+                const int c = t * BS + nt * 32 + q * 8 + lh * 4;
                 f32x4 v = quad(acc[t][nt], q);
-                if (bias) v = add_bias4(v, bias + n);
-                store4_bf16(out + (int64_t)m * out_ld + n, v[0], v[1], v[2], v[3]);
+                if (bias) v = add_bias4(v, bias + o * BS + nt * 32 + q * 8 + lh * 4);
+                store4_bf16(reinterpret_cast<uint16_t *>(ot + l32 * OP + c * 2), v[0], v[1], v[2], v[3]);
             }
+    }
+    constexpr int SPR = OC / 8;             // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < 32 * SPR / 64; ++i) {
+        const int seg = i * 64 + lane, row = seg / SPR, cs = seg % SPR;
+        const int t = cs * 8 / BS, within = cs * 8 % BS;
+        const int o = gout[g * G + t];
+        if (o < 0 || m0 + row >= M) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(ot + row * OP + cs * 16);
+        *reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + row) * out_ld + o * BS + within) = val;
     }
 }
 
