@@ -57,7 +57,21 @@ def op_bytes(w, nnzb: int, op: str, bias: bool) -> int:
 
 KERNEL_SOURCES = ("sparse_gemm_amd/csrc/bsr_kernels.hip", "sparse_gemm_amd/csrc/bsr_pattern.cpp",
                   "sparse_gemm_amd/csrc/bsr_internal.hpp")
-OP_KERNELS = {"fwd": ("k_group_gemm", "k_small_m"), "dx": ("k_group_gemm",), "dw": ("k_dw_tile", "k_dw_runs", "k_dw_reduce")}
+OP_KERNELS = {"fwd": ("k_panel_gemm", "k_small_m"), "dx": ("k_panel_gemm",), "dw": ("k_dw_panel", "k_dw_reduce")}
+
+
+def op_of_kernel(name: str):
+    """The op (fwd, dx, dw) a library kernel belongs to, from its (demangled) name: the panel GEMM
+    serves the forward (template flag false) and the input gradient (flag true)."""
+    if "bsr" not in name:
+        return None
+    if "k_panel_gemm" in name:
+        return "dx" if "true>" in name else "fwd"
+    if "k_small_m" in name:
+        return "fwd"
+    if "k_dw_panel" in name or "k_dw_reduce" in name or "k_colsum" in name:
+        return "dw"
+    return None
 COPY_BYTES = 256 << 20   # plain copy used to calibrate the HBM byte counters
 
 
@@ -152,19 +166,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops) -> st
     lines.append("")
     lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
     for op in ops:
-        pred = lambda k, op=op: "bsr" in k and any(n in k for n in OP_KERNELS[op])
-        # k_group_gemm serves fwd (TRANS=false) and dx (TRANS=true): split on the template flag
-        if op == "fwd":
-            pred = lambda k: "bsr" in k and (("k_group_gemm" in k and "false>" in k) or "k_small_m" in k)
-        elif op == "dx":
-            pred = lambda k: "bsr" in k and "k_group_gemm" in k and "true>" in k
-        per = sf * avg(fetch, pred) + sw * avg(write, pred)
-        if op == "dw":
-            # the split-M reduce is a second kernel of the same launch
-            per = sf * (avg(fetch, lambda k: "k_dw<" in k or ("k_dw" in k and "reduce" not in k)) +
-                        avg(fetch, lambda k: "k_dw_reduce" in k)) + \
-                  sw * (avg(write, lambda k: "k_dw<" in k or ("k_dw" in k and "reduce" not in k)) +
-                        avg(write, lambda k: "k_dw_reduce" in k))
+        # every kernel of the op counts once per launch of the op (e.g. the split-M reduce)
+        names = sorted({k for k in set(fetch) | set(write) if op_of_kernel(k) == op})
+        per = sum(sf * avg(fetch, lambda k, n=n: k == n) + sw * avg(write, lambda k, n=n: k == n) for n in names)
         lines.append(f"{op}_hbm_bytes_per_launch: {per:.0f}")
     path = traffic_path(workload_name)
     os.makedirs(os.path.dirname(path), exist_ok=True)

@@ -55,7 +55,7 @@ inline int dw_tile_cols(int b) { return 512 / b; }
 inline int dw_slots(int b) { return b == 64 ? 2 : 8; }
 struct DwSchedule {
     int n = 0;
-    std::vector<int32_t> items;   // [n * kDwItemInts], most blocks first
+    std::vector<int32_t> items;   // [n * kDwItemInts], by super-tiles of 8 x 4 tiles
 };
 
 struct DevSchedule {

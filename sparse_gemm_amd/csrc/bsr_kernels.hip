@@ -505,7 +505,9 @@ __global__ __launch_bounds__((kDwWaves + NL) * 64) void k_dw_panel(
     static_assert(KM / 2 % NL == 0 && KM % NL == 0 && 2 * NLD <= 63, "loader split");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
-    const int item = blockIdx.x % nitems, ch = blockIdx.x / nitems;
+    // each XCD takes a contiguous run of (chunk, item) pairs, items fastest
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int item = L % nitems, ch = L / nitems;
     const int32_t *it = items + (size_t)item * kDwItemInts;
     const int r0 = it[0], c0 = it[1];
     const int m_begin = ch * mchunk, m_end = min(M, m_begin + mchunk);

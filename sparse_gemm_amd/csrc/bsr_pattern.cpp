@@ -6,6 +6,7 @@
 // column. The transposed form is what the input-gradient kernel walks, so it needs no atomics.
 #include <algorithm>
 #include <numeric>
+#include <tuple>
 #include <utility>
 
 #include "bsr_internal.hpp"
@@ -120,7 +121,7 @@ GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int
 // Weight-gradient items: the kept blocks of every tile (dw_tile_rows x dw_tile_cols block
 // positions) in row-major order, at most kDwWaves * dw_slots blocks per item (a fuller tile makes
 // several items), spread over the compute waves in contiguous runs as even as possible (blocks of
-// one run mostly share a row). Items with more blocks come first.
+// one run mostly share a row). Items are ordered by super-tiles of 8 x 4 tiles.
 DwSchedule make_dw_items(const bsr_pattern &p) {
     const int TR = dw_tile_rows(p.b), TC = dw_tile_cols(p.b), SL = dw_slots(p.b), cap = kDwWaves * SL;
     std::vector<std::pair<int32_t, std::vector<int32_t>>> items;
@@ -146,7 +147,12 @@ DwSchedule make_dw_items(const bsr_pattern &p) {
             }
         }
     }
-    std::stable_sort(items.begin(), items.end(), [](const auto &a, const auto &b) { return a.first > b.first; });
+    // super-tiles of 8 x 4 tiles (row-major), items of a tile in order: the kernel hands each XCD a
+    // contiguous run of items, so the ones running together share dY and X row segments in L2
+    auto key = [&](const std::vector<int32_t> &it) {
+        return std::make_tuple(it[0] / (8 * TR), it[1] / (4 * TC), it[0], it[1]);
+    };
+    std::stable_sort(items.begin(), items.end(), [&](const auto &a, const auto &b) { return key(a.second) < key(b.second); });
     DwSchedule s;
     s.n = (int)items.size();
     for (auto &x : items) s.items.insert(s.items.end(), x.second.begin(), x.second.end());
