@@ -434,6 +434,7 @@ __global__ __launch_bounds__(256) void k_small_m(const uint16_t *__restrict__ X,
     const int l16 = lane & 15, lq = lane >> 4;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * K * 2);   // rows past M read as zero
     const uint32_t xoff = (uint32_t)(l16 * K + lq * 8) * 2;
+    const uint32_t xend = (uint32_t)M * K * 2;   // past the activations: reads zeros
     const uint32_t voff = (uint32_t)((slice * 16 + l16) * BS + lq * 8) * 2;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -446,10 +447,13 @@ __global__ __launch_bounds__(256) void k_small_m(const uint16_t *__restrict__ X,
             const int ic = min(iu, i1 - 1);
             const uint32_t coff = (uint32_t)col_idx[ic] * BS * 2;
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t)ic * BS * BS, iu < i1 ? BS * BS * 2 : 0);
+            // blocks past the row's end read zeros for both operands (a zero block times a
+            // non-finite activation would not be zero)
+            const uint32_t xo = iu < i1 ? xoff : xend;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 a[u][kc] = buf_load16(rv, voff + kc * 64, 0);
-                b[u][kc] = buf_load16(rx, xoff + kc * 64, coff);
+                b[u][kc] = buf_load16(rx, xo + kc * 64, coff);
             }
         }
 #pragma unroll
