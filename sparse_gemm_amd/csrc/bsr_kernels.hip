@@ -171,7 +171,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BS, int G, int S, int NW, int NL, bool TRANS>
+template <int BS, int G, int S, int NW, int NL, int NST, bool TRANS>
 __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
@@ -186,7 +186,8 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     constexpr int RB = BS * 2;              // bytes per row of a value block
     constexpr int WBB = BS * RB;            // bytes per value block
     constexpr int STAGE = XB + S * WBB + kRecInts * 4;   // activations, value blocks, a record
-    constexpr int NST = 3;                  // stages
+    constexpr int D = NST - 1;              // sub-steps in flight ahead of the one computed
+    static_assert(NST == 2 || NST == 3, "two or three stages");
     constexpr int CPS = WBB / 1024;         // 1 KB load chunks per block
     constexpr int XPL = BM / 8 / NL;        // activation loads (8 rows x 128 bytes) per loader wave
     constexpr int WPL = S * CPS / NL;       // value-block chunks per loader wave
@@ -337,38 +338,47 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 
     const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
     if (s0 < s1) {
-        // prologue: the loaders put sub-steps s0 and s0 + 1 in flight (with the records of s0 + 2
-        // and s0 + 3)
-        const Rec r0 = rec_from(rec + (size_t)s0 * kRecInts);
-        int n1 = 0, mapB0 = -1, mapB1 = -1;
-        if (loader) issue(0, r0, s0 + 2 < s1 ? s0 + 2 : -1);
-        if (s0 + 1 < s1) {
-            const Rec r1 = rec_from(rec + (size_t)(s0 + 1) * kRecInts);
-            if (loader) n1 = issue(1, r1, s0 + 3 < s1 ? s0 + 3 : -1);
-            mapB0 = r1.map0;
-            mapB1 = r1.map1;
+        // Stage q holds sub-step q's panel and value blocks and the record of sub-step q + D. The
+        // prologue puts sub-steps s0 .. s0 + D - 1 in flight.
+        int mp0[D], mp1[D];   // unit maps of sub-steps s .. s + D - 1
+        int nlast = 0;        // loads this loader issued for the latest sub-step in flight
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            mp0[q] = mp1[q] = -1;
+            if (s0 + q < s1) {
+                const Rec x = rec_from(rec + (size_t)(s0 + q) * kRecInts);
+                if (loader) nlast = issue(q, x, s0 + q + D < s1 ? s0 + q + D : -1);
+                mp0[q] = x.map0;
+                mp1[q] = x.map1;
+            }
         }
-        int mapA0 = r0.map0, mapA1 = r0.map1;
         int st = 0;   // stage of sub-step s
         for (int s = s0; s < s1; ++s) {
-            if (loader) wait_vm<0, MAXL>(n1);   // this loader's loads of sub-step s have landed
-            __syncthreads();                     // everyone's have; nobody reads sub-step s - 1 any more
-            const int st2 = st == 0 ? 2 : st - 1;   // stage of s + 2 (= that of s - 1)
-            int m20 = -1, m21 = -1;
-            if (s + 2 < s1) {
-                const Rec x = rec_from(reinterpret_cast<const int32_t *>(smem + st * STAGE + XB + S * WBB));
-                if (loader) n1 = issue(st2, x, s + 4 < s1 ? s + 4 : -1);
-                m20 = x.map0;
-                m21 = x.map1;
-            } else {
-                n1 = 0;
+            // this loader's loads of sub-step s have landed (those of s + 1 .. s + D - 1 may not)
+            if (loader) {
+                if (D == 2 && s + 1 < s1) wait_vm<0, MAXL>(nlast);
+                else wait_vm<0, 0>(0);
             }
-            if (!loader) compute(st, mapA0, mapA1);
-            mapA0 = mapB0;
-            mapA1 = mapB1;
-            mapB0 = m20;
-            mapB1 = m21;
-            st = st == 2 ? 0 : st + 1;
+            __syncthreads();   // everyone's have; nobody reads sub-step s - 1 any more
+            int m0 = -1, m1 = -1;
+            if (s + D < s1) {
+                const Rec x = rec_from(reinterpret_cast<const int32_t *>(smem + st * STAGE + XB + S * WBB));
+                // into the stage of s - 1
+                if (loader) nlast = issue(st == 0 ? NST - 1 : st - 1, x, s + 2 * D < s1 ? s + 2 * D : -1);
+                m0 = x.map0;
+                m1 = x.map1;
+            } else {
+                nlast = 0;
+            }
+            if (!loader) compute(st, mp0[0], mp1[0]);
+#pragma unroll
+            for (int q = 0; q + 1 < D; ++q) {
+                mp0[q] = mp0[q + 1];
+                mp1[q] = mp1[q + 1];
+            }
+            mp0[D - 1] = m0;
+            mp1[D - 1] = m1;
+            st = st == NST - 1 ? 0 : st + 1;
         }
     }
     // Epilogue, through LDS: each compute wave writes its 32 rows x G*BS columns (bias added, bf16)
@@ -729,7 +739,9 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
     const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
     constexpr int NL = kLoaderWaves;
-    hipLaunchKernelGGL((k_panel_gemm<BS, G, G, NW, NL, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
+    // three stages; two for the 4-wave tile, whose smaller LDS footprint then fits 3 work-groups per CU
+    constexpr int NST = NW == kGemmWavesSmall ? 2 : 3;
+    hipLaunchKernelGGL((k_panel_gemm<BS, G, G, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles);
 }
 
