@@ -38,11 +38,13 @@ int32_t upload(bsr_pattern &p) {
         {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.rows_by_nnz, &d.rows_by_nnz},
         {&p.dw.items, &d.dw_items},
     };
-    for (auto sd : {std::make_pair(&p.fwd, &d.fwd), std::make_pair(&p.bwd, &d.bwd)}) {
-        parts.push_back({&sd.first->order, &sd.second->order});
-        parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
-        parts.push_back({&sd.first->out, &sd.second->out});
-        parts.push_back({&sd.first->rec, &sd.second->rec});
+    for (int k = 0; k < kGemmVariants; ++k) {
+        for (auto sd : {std::make_pair(&p.fwd[k], &d.fwd[k]), std::make_pair(&p.bwd[k], &d.bwd[k])}) {
+            parts.push_back({&sd.first->order, &sd.second->order});
+            parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
+            parts.push_back({&sd.first->out, &sd.second->out});
+            parts.push_back({&sd.first->rec, &sd.second->rec});
+        }
     }
     size_t total = 0;
     for (const Part &q : parts) total += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);

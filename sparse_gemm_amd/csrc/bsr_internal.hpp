@@ -19,15 +19,22 @@ namespace bsr {
 // activations and at most S value blocks ("slots"); a panel with more kept blocks than S takes
 // several sub-steps.
 constexpr int kPanelCols = 64;
-// Compute waves (32 activation rows each) per work-group: 8, or 4 for problems that would not
-// fill the chip otherwise; plus kLoaderWaves waves that only issue the loads. Members per group:
-// 4 for b = 32 (128 output columns, 8 units per panel), 1 for b = 64.
-constexpr int kGemmWaves = 8;
-constexpr int kGemmWavesSmall = 4;
+// Kernel variants (members per group G, slots per sub-step S, compute waves per work-group; each
+// variant has its own work lists, since S decides how panels split into sub-steps):
+//   0: G = 4, S = 8 (all 8 units of a panel), 8 waves (256 activation rows) -- large problems;
+//   1: G = 4, S = 4, 4 waves (128 rows, two LDS stages: 3 work-groups per CU);
+//   2: G = 2, S = 4 (all 4 units), 4 waves -- problems too small to fill the chip with variant 1.
+// For b = 64 every variant has G = S = 1 (one 64 x 64 block per panel). Every work-group also has
+// kLoaderWaves waves that only issue the loads.
+constexpr int kGemmVariants = 3;
 constexpr int kLoaderWaves = 2;
-inline int gemm_group(int b) { return b == 64 ? 1 : 4; }
-// Slots per sub-step: G (half of a panel's units for b = 32, all of them for b = 64).
-inline int gemm_slots(int, int G) { return G; }
+struct GemmVariant {
+    int G, S, waves;
+};
+inline GemmVariant gemm_variant(int b, int k) {
+    if (b == 64) return GemmVariant{1, 1, k == 0 ? 8 : 4};
+    return k == 0 ? GemmVariant{4, 8, 8} : k == 1 ? GemmVariant{4, 4, 4} : GemmVariant{2, 4, 4};
+}
 
 // Sub-step record, kRecInts ints: [0] panel index; [1 + k] value block in slot k (-1 = empty),
 // k < S; [1 + S + w] slot of units 8w .. 8w + 7, 4 bits each (unit u at bits 4 * (u % 8); 15 =
@@ -36,6 +43,8 @@ constexpr int kRecInts = 16;
 struct GroupSchedule {
     int G = 0, S = 0;
     int ngroups = 0;
+    int64_t npanels = 0;             // (group, panel) pairs with kept blocks; sub-steps / npanels > 1
+                                     // when panels hold more units than S
     std::vector<int32_t> order;      // processing order of the groups (most sub-steps first)
     std::vector<int32_t> sub_ptr;    // [ngroups + 1]
     std::vector<int32_t> out;        // [ngroups * G] output block index per member, -1 = unused
@@ -69,7 +78,7 @@ struct DeviceMeta {
     int device = -1;
     const int32_t *row_ptr = nullptr, *col_idx = nullptr, *col_ptr = nullptr, *row_idx = nullptr,
                   *perm = nullptr;
-    DevSchedule fwd, bwd;
+    DevSchedule fwd[kGemmVariants], bwd[kGemmVariants];
     const int32_t *dw_items = nullptr;
     const int32_t *rows_by_nnz = nullptr;   // small-M forward: block rows, most blocks first
 };
@@ -79,7 +88,7 @@ struct DeviceMeta {
 struct bsr_pattern {
     int32_t N = 0, K = 0, b = 0, R = 0, C = 0, nnzb = 0;
     std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, rows_by_nnz;
-    bsr::GroupSchedule fwd, bwd;
+    bsr::GroupSchedule fwd[bsr::kGemmVariants], bwd[bsr::kGemmVariants];
     bsr::DwSchedule dw;
     bsr::DeviceMeta dev;
     bool uploaded = false;

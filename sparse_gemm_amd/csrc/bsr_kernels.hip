@@ -684,16 +684,24 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 
 // ---- host-side planning ----
 
-// Compute waves per work-group of a panel GEMM call: 8 (256 activation rows) when that gives every
+// Variant of a panel GEMM call (see gemm_variant). If variant 1's 128-row work-groups give every
 // compute unit at least two work-groups (so that one work-group's prologue and epilogue overlap
-// another's main loop), else 4.
-int choose_waves(const bsr_pattern &p, bool transposed, int64_t M) {
-    const char *f = std::getenv("BSR_GEMM_WAVES");   // tuning knob: 8 | 4
-    if (f && !std::strcmp(f, "8")) return kGemmWaves;
-    if (f && !std::strcmp(f, "4")) return kGemmWavesSmall;
-    const GroupSchedule &s = transposed ? p.bwd : p.fwd;
-    const int64_t tiles = (M + kGemmWaves * 32 - 1) / (kGemmWaves * 32);
-    return (int64_t)s.ngroups * tiles >= 2 * kCUs ? kGemmWaves : kGemmWavesSmall;
+// another's main loop): variant 1, or variant 0 when variant 1's panels often hold more than its 4
+// slots (each extra sub-step reloads the panel) and variant 0 also fills the chip; else variant 2.
+int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
+    if (const char *f = std::getenv("BSR_GEMM_VARIANT")) {   // tuning knob: 0 | 1 | 2
+        const int k = std::atoi(f);
+        if (k >= 0 && k < kGemmVariants) return k;
+    }
+    const GroupSchedule *s = transposed ? p.bwd : p.fwd;
+    auto fills = [&](int k) {
+        const int rows = gemm_variant(p.b, k).waves * 32;
+        return (int64_t)s[k].ngroups * ((M + rows - 1) / rows) >= 2 * kCUs;
+    };
+    if (!fills(1)) return 2;
+    const int64_t nsub1 = s[1].sub_ptr.empty() ? 0 : s[1].sub_ptr.back();
+    const bool splits = (double)nsub1 > 1.15 * (double)std::max<int64_t>(1, s[1].npanels);
+    return splits && fills(0) ? 0 : 1;
 }
 
 // Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage) so that items x
@@ -732,33 +740,31 @@ int32_t launched(const char *what) {
     return BSR_OK;
 }
 
-template <int BS, int G, int NW, bool TRANS>
+template <int BS, int G, int S, int NW, bool TRANS>
 void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
     constexpr int BM = NW * 32;
     const int nmtiles = (int)((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
     const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
     constexpr int NL = kLoaderWaves;
-    // three stages; two for the 4-wave tile, whose smaller LDS footprint then fits 3 work-groups per CU
-    constexpr int NST = NW == kGemmWavesSmall ? 2 : 3;
-    hipLaunchKernelGGL((k_panel_gemm<BS, G, G, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
+    // three stages; two for the 4-wave tiles, whose smaller LDS footprint then fits 3 work-groups per CU
+    constexpr int NST = NW == 4 ? 2 : 3;
+    hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles);
 }
 
-// Dispatch on the block size, the schedule's G and the compute waves per work-group to the
-// instantiated kernels (slots per sub-step S = G, see gemm_slots).
+// Dispatch on the block size and the variant to the instantiated kernels.
 template <bool TRANS>
-int32_t launch_pg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, int nw,
-                        const FwdArgs &a, hipStream_t st) {
-    if (s.S != s.G) return fail(BSR_ERR_UNSUPPORTED, "no kernel for this slot count");
-    const int key = (p.b * 100 + s.G) * 10 + nw;
-    constexpr int W8 = kGemmWaves, W4 = kGemmWavesSmall;
-    switch (key) {
-        case 32040 + W8: launch_pg<32, 4, W8, TRANS>(p, s, d, a, st); break;
-        case 32040 + W4: launch_pg<32, 4, W4, TRANS>(p, s, d, a, st); break;
-        case 64010 + W8: launch_pg<64, 1, W8, TRANS>(p, s, d, a, st); break;
-        case 64010 + W4: launch_pg<64, 1, W4, TRANS>(p, s, d, a, st); break;
-        default: return fail(BSR_ERR_UNSUPPORTED, "no kernel for this group shape");
+int32_t launch_pg_variant(const bsr_pattern &p, int k, const FwdArgs &a, hipStream_t st) {
+    const GroupSchedule &s = (TRANS ? p.bwd : p.fwd)[k];
+    const DevSchedule &d = (TRANS ? p.dev.bwd : p.dev.fwd)[k];
+    if (p.b == 32) {
+        if (k == 0) launch_pg<32, 4, 8, 8, TRANS>(p, s, d, a, st);
+        else if (k == 1) launch_pg<32, 4, 4, 4, TRANS>(p, s, d, a, st);
+        else launch_pg<32, 2, 4, 4, TRANS>(p, s, d, a, st);
+    } else {
+        if (k == 0) launch_pg<64, 1, 1, 8, TRANS>(p, s, d, a, st);
+        else launch_pg<64, 1, 1, 4, TRANS>(p, s, d, a, st);
     }
     return BSR_OK;
 }
@@ -767,17 +773,17 @@ int32_t launch_pg_shape(const bsr_pattern &p, const GroupSchedule &s, const DevS
 
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    const int nw = choose_waves(p, transposed, a.M);
-    const GroupSchedule &s = transposed ? p.bwd : p.fwd;
-    const DevSchedule &d = transposed ? p.dev.bwd : p.dev.fwd;
-    const int rows = nw * 32;
+    const int k = choose_variant(p, transposed, a.M);
+    const GemmVariant v = gemm_variant(p.b, k);
+    const GroupSchedule &s = (transposed ? p.bwd : p.fwd)[k];
+    const int rows = v.waves * 32;
     const int64_t nwg = (int64_t)s.ngroups * ((a.M + rows - 1) / rows);
     if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
     if ((size_t)p.nnzb * p.b * p.b * 2 > (size_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
     if ((int64_t)rows * a.in_ld * 2 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
-    const int32_t rc = transposed ? launch_pg_shape<true>(p, s, d, nw, a, st) : launch_pg_shape<false>(p, s, d, nw, a, st);
+    const int32_t rc = transposed ? launch_pg_variant<true>(p, k, a, st) : launch_pg_variant<false>(p, k, a, st);
     if (rc != BSR_OK) return rc;
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }

@@ -80,6 +80,7 @@ GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int
                 if (cursor[t] < ptr[o + 1]) panel = std::min(panel, idx[cursor[t]] / PB);
             }
             if (panel == INT32_MAX) break;
+            ++s.npanels;
             std::fill(unit_blk.begin(), unit_blk.end(), -1);
             for (int t = 0; t < members; ++t) {
                 const int32_t o = s.out[(size_t)g * G + t];
@@ -163,9 +164,11 @@ DwSchedule make_dw_items(const bsr_pattern &p) {
 
 void build_pattern(bsr_pattern &p) {
     build_csc(p);
-    const int G = gemm_group(p.b), S = gemm_slots(p.b, G);
-    p.fwd = make_panels(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, G, S);
-    p.bwd = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, G, S);
+    for (int k = 0; k < kGemmVariants; ++k) {
+        const GemmVariant v = gemm_variant(p.b, k);
+        p.fwd[k] = make_panels(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, v.G, v.S);
+        p.bwd[k] = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, v.G, v.S);
+    }
     p.dw = make_dw_items(p);
     p.rows_by_nnz = by_count_desc(p.row_ptr);
 }

@@ -41,17 +41,19 @@ def test_shapes(M, N, K, b, d, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
-@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("variant", ["0", "1", "2"])
 @pytest.mark.parametrize("M,N,K,b,seed", [
     (300, 512, 480, 32, 11),   # 15 block columns: the last 64-column panel is half a panel
     (300, 512, 448, 64, 12),
+    (260, 768, 256, 32, 13),   # dense enough that panels fill every slot
 ])
-def test_both_tile_heights(monkeypatch, waves, M, N, K, b, seed):
-    """Both work-group heights of the forward / input-gradient kernel (256 and 128 activation
-    rows), whichever the automatic choice would take for this size, over a ragged row tail."""
-    monkeypatch.setenv("BSR_GEMM_WAVES", waves)
-    say(f"case tile waves={waves} M={M} N={N} K={K} b={b} seed={seed}")
-    host = case_inputs(M, N, K, b, seed, density=0.4, bias=True)
+def test_every_gemm_variant(monkeypatch, variant, M, N, K, b, seed):
+    """Every forward / input-gradient kernel variant (256-row work-groups with 8 slots, 128-row
+    with 4, 128-row with half-width groups), whichever the automatic choice would take for this
+    size, over a ragged row tail."""
+    monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
+    say(f"case variant={variant} M={M} N={N} K={K} b={b} seed={seed}")
+    host = case_inputs(M, N, K, b, seed, density=0.4 if seed != 13 else 0.8, bias=True)
     full_parity(M, N, K, b, host, dbias=True)
 
 
