@@ -288,50 +288,56 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[t][nt][v] = 0.f;
 
-    // products of one staged sub-step: the wave's activation fragments once, then for every unit
-    // with a block (uniform tests) its value fragments and products
+    // products of one staged sub-step, panel half by panel half: the wave's activation fragments of
+    // the half, then for every member with a block there (uniform tests) its value fragments and
+    // products
     auto compute = [&](int st, int map0, int map1) __attribute__((always_inline)) {
         const unsigned char *xt = smem + st * STAGE;
         const unsigned char *wt = xt + XB;
         const int r = wave * 32 + l32;
-        bf16x8 xf[4];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-            xf[kc] = *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * kc + lh) ^ swz8(r)) << 4));
+        for (int h = 0; h < PB; ++h) {
+            bf16x8 xf[KCB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int slot = ((u < 8 ? map0 : map1) >> (4 * (u % 8))) & 15;
-            if (slot == 15) continue;
-            const int t = u / PB, h = u % PB;
-            const unsigned char *wb = wt + slot * WBB;
+            for (int kc = 0; kc < KCB; ++kc) {
+                const int c = h * KCB + kc;   // 16-column chunk of the panel
+                xf[kc] = *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
+            }
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                bf16x8 wf[KCB];
+            for (int t = 0; t < G; ++t) {
+                const int u = t * PB + h;
+                const int slot = ((u < 8 ? map0 : map1) >> (4 * (u % 8))) & 15;
+                if (slot == 15) continue;
+                const unsigned char *wb = wt + slot * WBB;
 #pragma unroll
-                for (int kc = 0; kc < KCB; ++kc) {
-                    if constexpr (!TRANS) {
-                        const int n = nt * 32 + l32, kg = 2 * kc + lh;
-                        const int sw = BS == 32 ? swz4(n) : swz8(n);
-                        wf[kc] = *reinterpret_cast<const bf16x8 *>(wb + n * RB + ((kg ^ sw) << 4));
-                    } else {
-                        // lane l: V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], two transposing reads
-                        // of 4 rows each; lane s of a 16-lane group points at row R + s / 4,
-                        // columns C .. C + 3
-                        const int gq = lane >> 4, s16 = lane & 15;
-                        const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
-                        const int C = nt * 32 + (gq & 1) * 16 + 4 * (s16 & 3);
-                        auto at = [&](int row) {
-                            const int sw = BS == 32 ? swz4(row) : swz8(row);
-                            return (lds_i16x4 *)(wb + row * RB + ((((C >> 3) ^ sw) << 4) | ((C & 7) << 1)));
-                        };
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
-                        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        wf[kc] = __builtin_bit_cast(bf16x8, v);
+                for (int nt = 0; nt < NT; ++nt) {
+                    bf16x8 wf[KCB];
+#pragma unroll
+                    for (int kc = 0; kc < KCB; ++kc) {
+                        if constexpr (!TRANS) {
+                            const int n = nt * 32 + l32, kg = 2 * kc + lh;
+                            const int sw = BS == 32 ? swz4(n) : swz8(n);
+                            wf[kc] = *reinterpret_cast<const bf16x8 *>(wb + n * RB + ((kg ^ sw) << 4));
+                        } else {
+                            // lane l: V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], two transposing
+                            // reads of 4 rows each; lane s of a 16-lane group points at row R + s / 4,
+                            // columns C .. C + 3
+                            const int gq = lane >> 4, s16 = lane & 15;
+                            const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
+                            const int C = nt * 32 + (gq & 1) * 16 + 4 * (s16 & 3);
+                            auto at = [&](int row) {
+                                const int sw = BS == 32 ? swz4(row) : swz8(row);
+                                return (lds_i16x4 *)(wb + row * RB + ((((C >> 3) ^ sw) << 4) | ((C & 7) << 1)));
+                            };
+                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+                            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            wf[kc] = __builtin_bit_cast(bf16x8, v);
+                        }
                     }
-                }
 #pragma unroll
-                for (int kc = 0; kc < KCB; ++kc) acc[t][nt] = mfma32(wf[kc], xf[h * KCB + kc], acc[t][nt]);
+                    for (int kc = 0; kc < KCB; ++kc) acc[t][nt] = mfma32(wf[kc], xf[kc], acc[t][nt]);
+                }
             }
         }
     };
