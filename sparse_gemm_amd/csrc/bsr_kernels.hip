@@ -176,7 +176,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
     const int32_t *__restrict__ sub_ptr, const int32_t *__restrict__ gout, const int32_t *__restrict__ rec,
-    int ngroups, int nmtiles) {
+    int ngroups, int nmtiles, int tpc) {
     constexpr int PB = kPanelCols / BS;     // blocks per panel
     constexpr int U = G * PB;               // units per panel
     constexpr int NT = BS / 32;             // 32-wide output tiles per block
@@ -198,16 +198,16 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
     // Work-group -> (group, activation tile). Each XCD takes a contiguous run of logical indices
-    // (work-groups are dealt to the XCDs round-robin); logical indices run over chunks of 4
+    // (work-groups are dealt to the XCDs round-robin); logical indices run over chunks of tpc
     // activation tiles, and inside a chunk over the groups (most sub-steps first), then the tiles.
     // So every XCD gets all groups of its tiles (balanced work), and the work-groups running
     // together on one XCD share a few activation tiles (their panels) and their groups' value
     // blocks through that XCD's L2.
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int chunk = L / (4 * ngroups), r4 = L % (4 * ngroups);
-    const int mc = min(4, nmtiles - 4 * chunk);   // tiles in this chunk
+    const int chunk = L / (tpc * ngroups), r4 = L % (tpc * ngroups);
+    const int mc = min(tpc, nmtiles - tpc * chunk);   // tiles in this chunk
     const int g = order[r4 / mc];
-    const int mt0 = 4 * chunk + r4 % mc;
+    const int mt0 = tpc * chunk + r4 % mc;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool loader = wave >= NW;
@@ -288,53 +288,60 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[t][nt][v] = 0.f;
 
-    // products of one staged sub-step, panel half by panel half: the wave's activation fragments of
+    // fragment of value block wb for output tile nt and 16-deep chunk kc: natural layout for the
+    // forward; for the input gradient lane l holds V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], from
+    // two transposing reads of 4 rows each (lane s of a 16-lane group points at row R + s / 4,
+    // columns C .. C + 3)
+    auto wfrag = [&](const unsigned char *wb, int nt, int kc) __attribute__((always_inline)) {
+        if constexpr (!TRANS) {
+            const int n = nt * 32 + l32, kg = 2 * kc + lh;
+            const int sw = BS == 32 ? swz4(n) : swz8(n);
+            return *reinterpret_cast<const bf16x8 *>(wb + n * RB + ((kg ^ sw) << 4));
+        } else {
+            const int gq = lane >> 4, s16 = lane & 15;
+            const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
+            const int C = nt * 32 + (gq & 1) * 16 + 4 * (s16 & 3);
+            auto at = [&](int row) {
+                const int sw = BS == 32 ? swz4(row) : swz8(row);
+                return (lds_i16x4 *)(wb + row * RB + ((((C >> 3) ^ sw) << 4) | ((C & 7) << 1)));
+            };
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        }
+    };
+    // activation fragment of 16-column chunk c of the panel (the wave's 32 rows)
+    auto xfrag = [&](const unsigned char *xt, int c) __attribute__((always_inline)) {
+        const int r = wave * 32 + l32;
+        return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
+    };
+    auto slot_of = [&](int u, int map0, int map1) __attribute__((always_inline)) {
+        return ((u < 8 ? map0 : map1) >> (4 * (u % 8))) & 15;
+    };
+
+    // Products of one staged sub-step, panel half by panel half: the wave's activation fragments of
     // the half, then for every member with a block there (uniform tests) its value fragments and
-    // products
+    // products. (Reading every unit's fragments first, absent ones included, and skipping only the
+    // products measured slower: the extra LDS reads slow the loads landing in LDS.)
     auto compute = [&](int st, int map0, int map1) __attribute__((always_inline)) {
         const unsigned char *xt = smem + st * STAGE;
         const unsigned char *wt = xt + XB;
-        const int r = wave * 32 + l32;
 #pragma unroll
         for (int h = 0; h < PB; ++h) {
             bf16x8 xf[KCB];
 #pragma unroll
-            for (int kc = 0; kc < KCB; ++kc) {
-                const int c = h * KCB + kc;   // 16-column chunk of the panel
-                xf[kc] = *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
-            }
+            for (int kc = 0; kc < KCB; ++kc) xf[kc] = xfrag(xt, h * KCB + kc);
 #pragma unroll
             for (int t = 0; t < G; ++t) {
-                const int u = t * PB + h;
-                const int slot = ((u < 8 ? map0 : map1) >> (4 * (u % 8))) & 15;
+                const int slot = slot_of(t * PB + h, map0, map1);
                 if (slot == 15) continue;
                 const unsigned char *wb = wt + slot * WBB;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     bf16x8 wf[KCB];
 #pragma unroll
-                    for (int kc = 0; kc < KCB; ++kc) {
-                        if constexpr (!TRANS) {
-                            const int n = nt * 32 + l32, kg = 2 * kc + lh;
-                            const int sw = BS == 32 ? swz4(n) : swz8(n);
-                            wf[kc] = *reinterpret_cast<const bf16x8 *>(wb + n * RB + ((kg ^ sw) << 4));
-                        } else {
-                            // lane l: V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], two transposing
-                            // reads of 4 rows each; lane s of a 16-lane group points at row R + s / 4,
-                            // columns C .. C + 3
-                            const int gq = lane >> 4, s16 = lane & 15;
-                            const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
-                            const int C = nt * 32 + (gq & 1) * 16 + 4 * (s16 & 3);
-                            auto at = [&](int row) {
-                                const int sw = BS == 32 ? swz4(row) : swz8(row);
-                                return (lds_i16x4 *)(wb + row * RB + ((((C >> 3) ^ sw) << 4) | ((C & 7) << 1)));
-                            };
-                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
-                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
-                            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                            wf[kc] = __builtin_bit_cast(bf16x8, v);
-                        }
-                    }
+                    for (int kc = 0; kc < KCB; ++kc) wf[kc] = wfrag(wb, nt, kc);
 #pragma unroll
                     for (int kc = 0; kc < KCB; ++kc) acc[t][nt] = mfma32(wf[kc], xf[kc], acc[t][nt]);
                 }
@@ -690,10 +697,8 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 
 // ---- host-side planning ----
 
-// Variant of a panel GEMM call (see gemm_variant). If variant 1's 128-row work-groups give every
-// compute unit at least two work-groups (so that one work-group's prologue and epilogue overlap
-// another's main loop): variant 1, or variant 0 when variant 1's panels often hold more than its 4
-// slots (each extra sub-step reloads the panel) and variant 0 also fills the chip; else variant 2.
+// Variant of a panel GEMM call (see gemm_variant); "fills" = at least two work-groups per compute
+// unit, so that one work-group's prologue and epilogue overlap another's main loop.
 int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
     if (const char *f = std::getenv("BSR_GEMM_VARIANT")) {   // tuning knob: 0 | 1 | 2
         const int k = std::atoi(f);
@@ -704,10 +709,14 @@ int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
         const int rows = gemm_variant(p.b, k).waves * 32;
         return (int64_t)s[k].ngroups * ((M + rows - 1) / rows) >= 2 * kCUs;
     };
-    if (!fills(1)) return 2;
+    // Panels that often hold more than 4 kept blocks (dense groups) favour the 4-member groups:
+    // every staged panel feeds more products. The 256-row tile when it still gives every CU two
+    // work-groups, else the 128-row one. Sparser patterns take the 2-member groups, whose smaller
+    // register footprint fits three work-groups per CU.
     const int64_t nsub1 = s[1].sub_ptr.empty() ? 0 : s[1].sub_ptr.back();
     const bool splits = (double)nsub1 > 1.15 * (double)std::max<int64_t>(1, s[1].npanels);
-    return splits && fills(0) ? 0 : 1;
+    if (!splits) return 2;
+    return fills(0) ? 0 : fills(1) ? 1 : 2;
 }
 
 // Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage) so that items x
@@ -746,17 +755,25 @@ int32_t launched(const char *what) {
     return BSR_OK;
 }
 
+// Activation tiles per chunk of the work-group order (see k_panel_gemm).
+int tiles_per_chunk(int nmtiles) {
+    int t = 4;
+    if (const char *f = std::getenv("BSR_GEMM_TPC")) t = std::atoi(f);   // tuning knob
+    return std::max(1, std::min(t, nmtiles));
+}
+
 template <int BS, int G, int S, int NW, bool TRANS>
 void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
     constexpr int BM = NW * 32;
     const int nmtiles = (int)((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
     const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
-    constexpr int NL = kLoaderWaves;
-    // three stages; two for the 4-wave tiles, whose smaller LDS footprint then fits 3 work-groups per CU
+    constexpr int NL = panel_loader_waves(NW);
+    // three stages; two for the 4-wave tiles, whose smaller LDS footprint then fits 2 work-groups per CU
     constexpr int NST = NW == 4 ? 2 : 3;
     hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
-                       (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles);
+                       (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles,
+                       tiles_per_chunk(nmtiles));
 }
 
 // Dispatch on the block size and the variant to the instantiated kernels.

@@ -57,6 +57,48 @@ def test_every_gemm_variant(monkeypatch, variant, M, N, K, b, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
+@pytest.mark.parametrize("variant", ["0", "1", "2"])
+@pytest.mark.parametrize("M", [9, 300])
+def test_nonfinite_activation_stays_in_its_blocks(monkeypatch, variant, M):
+    """The layer sums over kept blocks only: an infinite activation in input block 1 reaches the
+    outputs of block rows that keep a block in column 1 and no others, also where another member
+    of the same 64-column panel group skips block 1 (a skipped block must not be multiplied as a
+    zero block: zero times infinity is NaN). Same for an infinite output gradient and the input
+    gradient. M = 9 takes the small-M forward."""
+    monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
+    b, R, C = 32, 8, 4
+    mask = np.ones((R, C), dtype=np.uint8)
+    mask[0::2, 1] = 0             # even block rows skip input block 1 ...
+    mask[:, 3] = 0
+    mask[5, :] = 0
+    mask[5, 1] = 1                # ... and block row 5 keeps only block 1
+    host = case_inputs(M, R * b, C * b, b, 21, mask=mask, bias=True)
+    say(f"case non-finite activation variant={variant} M={M}")
+    m_bad = M // 2
+    X, dY = host["X"].clone(), host["dY"].clone()
+    X[m_bad, b + 3] = float("inf")
+    dY[m_bad, 2 * b + 5] = float("-inf")   # block row 2 (keeps input blocks 0 and 2)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, R * b, C * b, b)
+    Y = binding.linear_fwd(p, X.to(dev()), host["V"].to(dev()), host["bias"].to(dev())).cpu()
+    dX = binding.linear_bwd_input(p, dY.to(dev()), host["V"].to(dev())).cpu()
+    torch.cuda.synchronize()
+    # outputs that do not touch the infinite entry match the oracle on the finite inputs
+    ref, S = oracle.fwd(host["X"], md["row_ptr"], md["col_idx"], host["V"], R * b, b, bias=host["bias"])
+    uses = np.repeat(mask[:, 1].astype(bool), b)            # output columns whose block row keeps block 1
+    clean = np.ones((M, R * b), dtype=bool)
+    clean[m_bad, uses] = False
+    assert torch.isfinite(Y[~torch.from_numpy(clean)].float()).sum() == 0
+    check("fwd (untouched)", Y[torch.from_numpy(clean)], ref[clean], S[clean])
+    ref, S = oracle.dx(host["dY"], md["row_ptr"], md["col_idx"], host["V"], C * b, b)
+    uses = np.repeat(mask[2, :].astype(bool), b)            # input columns fed by block row 2
+    clean = np.ones((M, C * b), dtype=bool)
+    clean[m_bad, uses] = False
+    assert torch.isfinite(dX[~torch.from_numpy(clean)].float()).sum() == 0
+    check("dx (untouched)", dX[torch.from_numpy(clean)], ref[clean], S[clean])
+    p.close()
+
+
 @pytest.mark.parametrize("b", [32, 64])
 def test_empty_rows_and_columns(b):
     R, C = 6, 5
