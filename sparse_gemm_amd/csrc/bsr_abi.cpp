@@ -35,7 +35,7 @@ int32_t upload(bsr_pattern &p) {
     DeviceMeta &d = p.dev;
     std::vector<Part> parts = {
         {&p.row_ptr, &d.row_ptr}, {&p.col_idx, &d.col_idx}, {&p.col_ptr, &d.col_ptr},
-        {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.rows_by_nnz, &d.rows_by_nnz},
+        {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.small_m_rows, &d.small_m_rows},
         {&p.dw.items, &d.dw_items},
     };
     for (int k = 0; k < kGemmVariants; ++k) {

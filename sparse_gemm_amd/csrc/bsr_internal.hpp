@@ -84,14 +84,15 @@ struct DeviceMeta {
                   *perm = nullptr;
     DevSchedule fwd[kGemmVariants], bwd[kGemmVariants];
     const int32_t *dw_items = nullptr;
-    const int32_t *rows_by_nnz = nullptr;   // small-M forward: block rows, most blocks first
+    const int32_t *small_m_rows = nullptr;  // small-M forward: [R][4] {block row, first block, end
+                                            // block, 0}, most blocks first
 };
 
 }  // namespace bsr
 
 struct bsr_pattern {
     int32_t N = 0, K = 0, b = 0, R = 0, C = 0, nnzb = 0;
-    std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, rows_by_nnz;
+    std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, small_m_rows;
     bsr::GroupSchedule fwd[bsr::kGemmVariants], bwd[bsr::kGemmVariants];
     bsr::DwSchedule dw;
     bsr::DeviceMeta dev;

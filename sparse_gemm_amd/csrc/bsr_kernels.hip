@@ -434,64 +434,82 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 // ------------------------------------------------------------------------------------------
 // Small-M forward (M <= 16): a streaming pass over the block values, the memory-bound regime
 // where the kept blocks are loaded once and expanded into dense matrix-core products (GPU MODE
-// lecture 11 summary, 48:12, "load and sparse expand"). Work-group = (block row, 16-row slice of
-// the block); its 4 waves take the row's kept blocks round-robin, each keeping U blocks of loads
-// in flight, and their partial products are summed in LDS in wave order (deterministic).
-//   A[p][k] = V[i][slice*16 + p][k]   B[k][m] = X[m][c*BS + k]   (m < 16; rows past M are 0)
+// lecture 11 summary, 48:12, "load and sparse expand"). Work-group = PSW consecutive 16-row slices
+// of one block row (rows are dealt heaviest first); its NW waves take the row's kept blocks U at a
+// time (wave w: blocks w*U .. w*U + U - 1 of each pass of NW*U), each reading its slices of whole
+// blocks (PSW*16 rows: contiguous bytes) and the activation columns of each block once for all
+// its slices. Every load of a pass is requested before the first product. The waves' partial
+// products are summed in LDS in wave order (deterministic).
+//   slice s:  A[p][k] = V[i][s*16 + p][k]   B[k][m] = X[m][c*BS + k]   (m < 16; rows past M are 0)
 // ------------------------------------------------------------------------------------------
-template <int BS>
-__global__ __launch_bounds__(256) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
-                                                 const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
-                                                 uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ row_ptr,
-                                                 const int32_t *__restrict__ col_idx,
-                                                 const int32_t *__restrict__ rows_by_nnz) {
-    constexpr int PS = BS / 16;   // 16-row slices per block
+template <int BS, int NW, int U, int PSW>
+__global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
+                                                     const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
+                                                     uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
+                                                     const int32_t *__restrict__ rows) {
+    constexpr int PS = PSW;       // 16-row slices of each block handled by this work-group
     constexpr int KC = BS / 32;   // 32-deep k chunks per block
-    constexpr int U = 8 / KC;     // blocks in flight per wave
-    constexpr int NW = 4;
-    __shared__ f32x4 red[NW][64];
+    constexpr int PARTS = BS / 16 / PSW;
+    __shared__ f32x4 red[NW][PS][64];
 
-    const int r = rows_by_nnz[blockIdx.x / PS];
-    const int slice = blockIdx.x % PS;
+    // work-group entry {block row, first block, end block}: one read ahead of the first value loads
+    const int4 e = reinterpret_cast<const int4 *>(rows)[blockIdx.x / PARTS];
+    const int r = e.x, i1 = e.z, s0 = (int)(blockIdx.x % PARTS) * PSW;   // first slice
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lq = lane >> 4;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * K * 2);   // rows past M read as zero
     const uint32_t xoff = (uint32_t)(l16 * K + lq * 8) * 2;
     const uint32_t xend = (uint32_t)M * K * 2;   // past the activations: reads zeros
-    const uint32_t voff = (uint32_t)((slice * 16 + l16) * BS + lq * 8) * 2;
+    const uint32_t voff = (uint32_t)((s0 * 16 + l16) * BS + lq * 8) * 2;   // + s * 16 rows + kc * 32 columns
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int i1 = row_ptr[r + 1];
-    for (int i = row_ptr[r] + wave; i < i1; i += NW * U) {
-        bf16x8 a[U][KC], b[U][KC];
+    f32x4 acc[PS];
+#pragma unroll
+    for (int s = 0; s < PS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = e.y; i0 < i1; i0 += NW * U) {
+        const int ib = i0 + wave * U;
+        // the value loads need only the block index: requested before the column indices, whose
+        // read would otherwise delay them
+        bf16x8 a[U][PS][KC], b[U][KC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int iu = i + u * NW;
-            const int ic = min(iu, i1 - 1);
-            const uint32_t coff = (uint32_t)col_idx[ic] * BS * 2;
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t)ic * BS * BS, iu < i1 ? BS * BS * 2 : 0);
+            const int iu = ib + u;
+            const __amdgpu_buffer_rsrc_t rv =
+                make_rsrc(V + (size_t)min(iu, i1 - 1) * BS * BS, iu < i1 ? BS * BS * 2 : 0);
+#pragma unroll
+            for (int s = 0; s < PS; ++s)
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) a[u][s][kc] = buf_load16(rv, voff + (s * 16 * BS + kc * 32) * 2, 0);
+        }
+        int col[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) col[u] = col_idx[min(ib + u, i1 - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             // blocks past the row's end read zeros for both operands (a zero block times a
             // non-finite activation would not be zero)
-            const uint32_t xo = iu < i1 ? xoff : xend;
+            const uint32_t xo = ib + u < i1 ? xoff : xend;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                a[u][kc] = buf_load16(rv, voff + kc * 64, 0);
-                b[u][kc] = buf_load16(rx, xo + kc * 64, coff);
-            }
+            for (int kc = 0; kc < KC; ++kc) b[u][kc] = buf_load16(rx, xo + kc * 64, (uint32_t)col[u] * BS * 2);
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the products after every load
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) acc = mfma(a[u][kc], b[u][kc], acc);
-    }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        f32x4 v = red[0][lane];
+            for (int s = 0; s < PS; ++s)
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][lane];
+                for (int kc = 0; kc < KC; ++kc) acc[s] = mfma(a[u][s][kc], b[u][kc], acc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < PS; ++s) red[wave][s][lane] = acc[s];
+    __syncthreads();
+    // wave w < PS sums slice w over the waves; lane l holds output rows n = 4 (l / 16) .. + 3 of the
+    // slice for activation row l % 16
+    if (wave < PS) {
+        f32x4 v = red[0][wave][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][wave][lane];
         if (l16 < M) {
-            const int n = r * BS + slice * 16 + lq * 4;
+            const int n = r * BS + (s0 + wave) * 16 + lq * 4;
             if (bias) v = add_bias4(v, bias + n);
             store4_bf16(Y + (int64_t)l16 * N + n, v[0], v[1], v[2], v[3]);
         }
@@ -831,13 +849,20 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
     const DeviceMeta &d = p.dev;
-    const dim3 grid((unsigned)(p.R * (p.b / 16)));
-    if (p.b == 32)
-        hipLaunchKernelGGL((k_small_m<32>), grid, dim3(256), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out, p.N,
-                           d.row_ptr, d.col_idx, d.rows_by_nnz);
-    else
-        hipLaunchKernelGGL((k_small_m<64>), grid, dim3(256), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out, p.N,
-                           d.row_ptr, d.col_idx, d.rows_by_nnz);
+    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group; b = 64: 8 waves x
+    // 2 blocks, two of the four slices per work-group (two work-groups per block row spread the
+    // heavier rows over more compute units; measured best among 4-16 waves, 2-4 blocks, 1-4 slices)
+    if (p.b == 32) {
+        constexpr int NW = 8, U = 8, PSW = 2;
+        const dim3 grid((unsigned)(p.R * (2 / PSW)));
+        hipLaunchKernelGGL((k_small_m<32, NW, U, PSW>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out,
+                           p.N, d.col_idx, d.small_m_rows);
+    } else {
+        constexpr int NW = 8, U = 2, PSW = 2;
+        const dim3 grid((unsigned)(p.R * (4 / PSW)));
+        hipLaunchKernelGGL((k_small_m<64, NW, U, PSW>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out,
+                           p.N, d.col_idx, d.small_m_rows);
+    }
     return launched("fwd small-M launch");
 }
 

@@ -170,7 +170,10 @@ void build_pattern(bsr_pattern &p) {
         p.bwd[k] = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, v.G, v.S);
     }
     p.dw = make_dw_items(p);
-    p.rows_by_nnz = by_count_desc(p.row_ptr);
+    // small-M forward work list: one entry per block row, {row, first block, end block, 0}, most
+    // blocks first (the heaviest rows start first)
+    p.small_m_rows.clear();
+    for (int32_t r : by_count_desc(p.row_ptr)) p.small_m_rows.insert(p.small_m_rows.end(), {r, p.row_ptr[r], p.row_ptr[r + 1], 0});
 }
 
 }  // namespace bsr
