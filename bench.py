@@ -429,7 +429,9 @@ def main():
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02) blocks)",
            "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.b, "density": w.density,
                       "nnzb": nnzb, "pattern": w.pattern, "ops": "+".join(w.ops),
-                      "buffers": "warm (1 set)" if nsets == 1 else f"cold ({nsets} rotated sets)",
+                      "buffers": (f"cold ({nsets} rotated sets)" if nsets > 1 else
+                                  "cold (one set, each step touches more than the rotation size)"
+                                  if not args.warm else "warm (1 set)"),
                       "pattern_sha256": synth.mask_digest(host["mask"]), "rows": synth.row_histogram(host["mask"])},
            "pct_bf16_mfma_peak": 100 * value / PEAK_BF16_TFLOPS,
            "ops": per_op, "roofline": roofline,
