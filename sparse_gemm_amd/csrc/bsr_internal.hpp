@@ -22,8 +22,8 @@ constexpr int kPanelCols = 64;
 // Kernel variants (members per group G, slots per sub-step S, compute waves per work-group; each
 // variant has its own work lists, since S decides how panels split into sub-steps):
 //   0: G = 4, S = 8 (all 8 units of a panel), 8 waves (256 activation rows) -- large problems;
-//   1: G = 4, S = 4, 4 waves (128 rows, two LDS stages: 2 work-groups per CU);
-//   2: G = 2, S = 4 (all 4 units), 4 waves -- problems too small to fill the chip with variant 1.
+//   1: G = 4, S = 4, 4 waves (128 rows, three LDS stages: 2 work-groups per CU);
+//   2: G = 2, S = 4 (all 4 units), 4 waves (two LDS stages: 3 work-groups per CU).
 // For b = 64 every variant has G = S = 1 (one 64 x 64 block per panel). Every work-group also has
 // waves that only issue the loads: panel_loader_waves(compute waves) of them. Each load into LDS
 // takes a wave tens of cycles to issue while the memory system is busy, so more issuing waves

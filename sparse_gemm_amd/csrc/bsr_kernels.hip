@@ -729,12 +729,16 @@ int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
     };
     // Panels that often hold more than 4 kept blocks (dense groups) favour the 4-member groups:
     // every staged panel feeds more products. The 256-row tile when it still gives every CU two
-    // work-groups, else the 128-row one. Sparser patterns take the 2-member groups, whose smaller
-    // register footprint fits three work-groups per CU.
+    // work-groups, else the 128-row one. For sparser patterns, long chains of sub-steps per
+    // work-group (>= 16) favour the 128-row 4-member tile with three LDS stages; short ones the
+    // 2-member tile, three work-groups per CU, whose prologues and epilogues overlap more (measured:
+    // square 8192 x 4096 -> 4096 at density 0.1, ~36 sub-steps: 88 vs 96 us; BERT-base FFN-up,
+    // ~11 sub-steps: 19 vs 21 us forward).
     const int64_t nsub1 = s[1].sub_ptr.empty() ? 0 : s[1].sub_ptr.back();
     const bool splits = (double)nsub1 > 1.15 * (double)std::max<int64_t>(1, s[1].npanels);
-    if (!splits) return 2;
-    return fills(0) ? 0 : fills(1) ? 1 : 2;
+    if (splits) return fills(0) ? 0 : fills(1) ? 1 : 2;
+    const bool long_chains = nsub1 >= 16 * (int64_t)std::max(1, s[1].ngroups);
+    return long_chains && fills(1) ? 1 : 2;
 }
 
 // Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage, at least 256 rows)
@@ -804,8 +808,9 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
     const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
     constexpr int NL = panel_loader_waves(NW);
-    // three stages; two for the 4-wave tiles, whose smaller LDS footprint then fits 2 work-groups per CU
-    constexpr int NST = NW == 4 ? 2 : 3;
+    // three LDS stages (two sub-steps of loads in flight); two for the 2-member groups, which then
+    // fit three work-groups per CU
+    constexpr int NST = NW == 4 && G == 2 ? 2 : 3;
     hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles,
                        tiles_per_chunk(nmtiles));
