@@ -224,9 +224,11 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     // LDS chunk lane % 8, which holds activation chunk (lane % 8) ^ swz8(row); its value-block
     // load j is the 1 KB part (c % CPS) of slot c / CPS, c = lw + NL j. (Offsets are recomputed at
     // every issue, so that no registers stay reserved for them next to the accumulators.)
-    auto xoff = [&](int i) __attribute__((always_inline)) {
+    // (the panel's column offset rides in the range-checked voffset too: a last half panel then
+    // reads zeros past the end of the buffer instead of bytes beyond it)
+    auto xoff = [&](int i, uint32_t col_bytes) __attribute__((always_inline)) {
         const int r = (lw + NL * i) * 8 + (lane >> 3);
-        return (uint32_t)(r * in_ld * 2 + (((lane & 7) ^ swz8(r)) << 4));
+        return (uint32_t)r * (uint32_t)in_ld * 2u + col_bytes + (uint32_t)(((lane & 7) ^ swz8(r)) << 4);
     };
     auto woff = [&](int j) __attribute__((always_inline)) {
         const int q = (lw + NL * j) % CPS;
@@ -260,9 +262,9 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     // of sub-step rsidx (if valid); returns how many loads it issued
     auto issue = [&](int st, const Rec &x, int rsidx) __attribute__((always_inline)) {
         const uint32_t base = sbase + (uint32_t)st * STAGE;
-        const uint32_t soff = (uint32_t)x.panel * 128u;
+        const uint32_t pcol = (uint32_t)x.panel * 128u;
 #pragma unroll
-        for (int i = 0; i < XPL; ++i) dma16(ra, base + (uint32_t)(lw + NL * i) * 1024u, xoff(i), soff);
+        for (int i = 0; i < XPL; ++i) dma16(ra, base + (uint32_t)(lw + NL * i) * 1024u, xoff(i, pcol), 0);
         int n = XPL;
 #pragma unroll
         for (int j = 0; j < WPL; ++j) {
@@ -844,7 +846,7 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
     if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
     if ((size_t)p.nnzb * p.b * p.b * 2 > (size_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
-    if ((int64_t)rows * a.in_ld * 2 > (int64_t)UINT32_MAX)
+    if ((int64_t)rows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
     const int32_t rc = transposed ? launch_pg_variant<true>(p, k, a, st) : launch_pg_variant<false>(p, k, a, st);
     if (rc != BSR_OK) return rc;
