@@ -127,12 +127,13 @@ __device__ __forceinline__ f32x4 add_bias4(f32x4 v, const uint16_t *bias) {
 //   forward:    A[n][k] = V[i][n][k]   (natural layout, 16-byte LDS reads)
 //   input grad: A[n][k] = V[i][k][n]   (transposed, ds_read_b64_tr_b16 of the natural layout)
 // so each lane ends up with runs of 4 consecutive output columns of one activation row.
-// The loads go straight from memory to LDS, three stages deep, and are issued by NL extra loader
-// waves, so that the compute waves never stall behind a full load queue and loads overlap the
-// products. Sub-step s: loaders wait for their loads of s, then a barrier (the stage of s is
-// complete; nobody reads the stage of s - 1 any more), then the loaders issue the loads of s + 2
-// into the stage of s - 1 while the compute waves run the products of s. In each stage the 16-byte
-// chunks of every row are XOR swizzled so that operand reads are free of bank conflicts.
+// The loads go straight from memory to LDS, NST stages deep (D = NST - 1 sub-steps ahead), and are
+// issued by NL extra loader waves, so that the compute waves never stall behind a full load queue
+// and loads overlap the products. Sub-step s: loaders wait for their loads of s, then a barrier
+// (the stage of s is complete; nobody reads the stage of s - 1 any more), then the loaders issue
+// the loads of s + D into the stage of s - 1 while the compute waves run the products of s. In
+// each stage the 16-byte chunks of every row are XOR swizzled so that operand reads are free of
+// bank conflicts.
 // ------------------------------------------------------------------------------------------
 
 // Byte offset in the work-group's LDS of a __shared__ object.
@@ -242,8 +243,8 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     };
 
     // Sub-step records travel with the stages: the stage of sub-step s also receives the record of
-    // sub-step s + 2 (loader 0, lanes 0..3), so that at sub-step s the record needed to issue the
-    // loads of s + 2 is read from LDS.
+    // sub-step s + D (loader 0, lanes 0..3), so that at sub-step s the record needed to issue the
+    // loads of s + D is read from LDS.
     struct Rec {
         int panel, map0, map1, blk[WPL];
     };
