@@ -43,6 +43,9 @@
  *     several streams at once. The pattern's device metadata lives on the device that
  *     was current at creation; compute calls must run with that device current.
  *   - No C++ exception crosses this interface.
+ *   - Size limits (32-bit buffer offsets in the kernels; BSR_ERR_INVALID_ARG beyond them):
+ *     V below 4 GiB; 256 rows of X (forward) or dY (input gradient) below 4 GiB; for the
+ *     weight gradient (M + 32) rows of dY and of X each below 4 GiB.
  */
 #ifndef BSR_LINEAR_H
 #define BSR_LINEAR_H
