@@ -172,7 +172,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BS, int G, int S, int NW, int NL, int NST, bool TRANS>
+template <int BS, int G, int S, int NW, int NL, int NST, int MS, bool TRANS>
 __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
@@ -183,6 +183,11 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     constexpr int NT = BS / 32;             // 32-wide output tiles per block
     constexpr int KCB = BS / 16;            // 16-deep k chunks per block
     constexpr int BM = NW * 32;             // activation rows per work-group
+    // Compute wave w takes RW = MS tiles of 32 rows and GW = G / MS members: rows
+    // [wr * 32 * MS, + 32 * MS) and members [wm * GW, + GW) with wr = w % (NW / MS), wm = w / (NW / MS).
+    // With MS = 2 every value fragment read from LDS feeds two products (one per row tile).
+    constexpr int RW = MS, GW = G / MS;
+    static_assert(G % MS == 0 && NW % MS == 0, "member split");
     constexpr int XB = BM * 128;            // bytes of a staged activation panel
     constexpr int RB = BS * 2;              // bytes per row of a value block
     constexpr int WBB = BS * RB;            // bytes per value block
@@ -213,6 +218,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool loader = wave >= NW;
     const int lw = wave - NW;               // loader index (loader waves only)
+    const int wr = wave % (NW / MS), wm = wave / (NW / MS);   // compute waves: row group, member group
     const int l32 = lane & 31, lh = lane >> 5;
 
     // Activations of this work-group's rows; rows past M read as zeros.
@@ -283,13 +289,15 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
         return n;
     };
 
-    f32x16 acc[G][NT];
+    f32x16 acc[RW][GW][NT];   // [row tile][member of the wave][output tile]
 #pragma unroll
-    for (int t = 0; t < G; ++t)
+    for (int rt = 0; rt < RW; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int t = 0; t < GW; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[t][nt][v] = 0.f;
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[rt][t][nt][v] = 0.f;
 
     // fragment of value block wb for output tile nt and 16-deep chunk kc: natural layout for the
     // forward; for the input gradient lane l holds V[kc*16 + 8 (l / 32) .. + 7][nt*32 + l % 32], from
@@ -314,9 +322,9 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
             return __builtin_bit_cast(bf16x8, v);
         }
     };
-    // activation fragment of 16-column chunk c of the panel (the wave's 32 rows)
-    auto xfrag = [&](const unsigned char *xt, int c) __attribute__((always_inline)) {
-        const int r = wave * 32 + l32;
+    // activation fragment of 16-column chunk c of the panel (row tile rt of the wave: 32 rows)
+    auto xfrag = [&](const unsigned char *xt, int rt, int c) __attribute__((always_inline)) {
+        const int r = (wr * RW + rt) * 32 + l32;
         return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
     };
     auto slot_of = [&](int u, int map0, int map1) __attribute__((always_inline)) {
@@ -324,20 +332,22 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     };
 
     // Products of one staged sub-step, panel half by panel half: the wave's activation fragments of
-    // the half, then for every member with a block there (uniform tests) its value fragments and
-    // products. (Reading every unit's fragments first, absent ones included, and skipping only the
-    // products measured slower: the extra LDS reads slow the loads landing in LDS.)
+    // the half, then for every member of the wave with a block there (uniform tests) its value
+    // fragments and products. (Reading every unit's fragments first, absent ones included, and
+    // skipping only the products measured slower: the extra LDS reads slow the loads landing in LDS.)
     auto compute = [&](int st, int map0, int map1) __attribute__((always_inline)) {
         const unsigned char *xt = smem + st * STAGE;
         const unsigned char *wt = xt + XB;
 #pragma unroll
         for (int h = 0; h < PB; ++h) {
-            bf16x8 xf[KCB];
+            bf16x8 xf[RW][KCB];
 #pragma unroll
-            for (int kc = 0; kc < KCB; ++kc) xf[kc] = xfrag(xt, h * KCB + kc);
+            for (int rt = 0; rt < RW; ++rt)
 #pragma unroll
-            for (int t = 0; t < G; ++t) {
-                const int slot = slot_of(t * PB + h, map0, map1);
+                for (int kc = 0; kc < KCB; ++kc) xf[rt][kc] = xfrag(xt, rt, h * KCB + kc);
+#pragma unroll
+            for (int t = 0; t < GW; ++t) {
+                const int slot = slot_of((wm * GW + t) * PB + h, map0, map1);
                 if (slot == 15) continue;
                 const unsigned char *wb = wt + slot * WBB;
 #pragma unroll
@@ -346,7 +356,10 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 #pragma unroll
                     for (int kc = 0; kc < KCB; ++kc) wf[kc] = wfrag(wb, nt, kc);
 #pragma unroll
-                    for (int kc = 0; kc < KCB; ++kc) acc[t][nt] = mfma32(wf[kc], xf[kc], acc[t][nt]);
+                    for (int kc = 0; kc < KCB; ++kc)
+#pragma unroll
+                        for (int rt = 0; rt < RW; ++rt)
+                            acc[rt][t][nt] = mfma32(wf[kc], xf[rt][kc], acc[rt][t][nt]);
                 }
             }
         }
@@ -397,31 +410,39 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
             st = st == NST - 1 ? 0 : st + 1;
         }
     }
-    // Epilogue, through LDS: each compute wave writes its 32 rows x G*BS columns (bias added, bf16)
-    // into a region of its own, then stores them as 16-byte pieces, 64 lanes covering whole
-    // 64-byte block rows (instead of 8-byte pieces spread over 32 rows).
+    // Epilogue, through LDS: the compute waves write their rows x members (bias added, bf16) into the
+    // staged tile of BM rows x G*BS columns, then each stores 32 rows as 16-byte pieces, 64 lanes
+    // covering whole 64-byte block rows (instead of 8-byte pieces spread over 32 rows). With MS > 1
+    // a stored row holds columns of several waves: a barrier separates the two phases.
     __syncthreads();   // every wave is done with the stages
-    if (loader) return;
     constexpr int OC = G * BS;              // output columns of the work-group
     constexpr int OP = OC * 2 + 16;         // LDS pitch of a staged output row (bytes)
     static_assert(NW * 32 * OP <= NST * STAGE, "output staging fits in the stages");
-    unsigned char *ot = smem + wave * 32 * OP;
-    const int m0 = mt0 * BM + wave * 32;
-    // item v of lane l is output column nt*32 + 8*(v/4) + 4*(l/32) + v%4 of member t, row l%32
+    if (!loader) {
+        // item v of lane l is output column nt*32 + 8*(v/4) + 4*(l/32) + v%4 of member t, row l%32
 #pragma unroll
-    for (int t = 0; t < G; ++t) {
-        const int o = gout[g * G + t];
-        if (o < 0) continue;
+        for (int t = 0; t < GW; ++t) {
+            const int tg = wm * GW + t;
+            const int o = gout[g * G + tg];
+            if (o < 0) continue;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+            for (int rt = 0; rt < RW; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = t * BS + nt * 32 + q * 8 + lh * 4;
-                f32x4 v = quad(acc[t][nt], q);
-                if (bias) v = add_bias4(v, bias + o * BS + nt * 32 + q * 8 + lh * 4);
-                store4_bf16(reinterpret_cast<uint16_t *>(ot + l32 * OP + c * 2), v[0], v[1], v[2], v[3]);
-            }
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = tg * BS + nt * 32 + q * 8 + lh * 4;
+                        const int row = (wr * RW + rt) * 32 + l32;
+                        f32x4 v = quad(acc[rt][t][nt], q);
+                        if (bias) v = add_bias4(v, bias + o * BS + nt * 32 + q * 8 + lh * 4);
+                        store4_bf16(reinterpret_cast<uint16_t *>(smem + row * OP + c * 2), v[0], v[1], v[2], v[3]);
+                    }
+        }
     }
+    if constexpr (MS > 1) __syncthreads();   // the staged tile is complete
+    if (loader) return;
+    const unsigned char *ot = smem + wave * 32 * OP;
+    const int m0 = mt0 * BM + wave * 32;
     constexpr int SPR = OC / 8;             // 16-byte pieces per row
 #pragma unroll
     for (int i = 0; i < 32 * SPR / 64; ++i) {
@@ -799,7 +820,11 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     // three LDS stages (two sub-steps of loads in flight); two for the 2-member groups, which then
     // fit three work-groups per CU
     constexpr int NST = NW == 4 && G == 2 ? 2 : 3;
-    hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
+    // the 256-row 4-member tile: waves of 64 rows x 2 members, each value fragment feeding two
+    // products (Zipf 16384 x 4096 -> 11008: input gradient 631 -> 613 us, forward 579 -> 573 us; no
+    // gain for the 128-row tiles)
+    constexpr int MS = G == 4 && NW == 8 ? 2 : 1;
+    hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, MS, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles,
                        tiles_per_chunk(nmtiles));
 }
