@@ -451,7 +451,10 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
         const int o = gout[g * G + t];
         if (o < 0 || m0 + row >= M) continue;
         const u32x4 val = *reinterpret_cast<const u32x4 *>(ot + row * OP + cs * 16);
-        *reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + row) * out_ld + o * BS + within) = val;
+        // streaming (nontemporal) store: the output is written once and not read back here, so it
+        // should not push the activation panels and value blocks out of L2 and the last-level cache
+        // (BERT-base FFN-up forward 28.8 -> 22.7 us)
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + row) * out_ld + o * BS + within));
     }
 }
 
