@@ -9,7 +9,10 @@ Parts:
             weight grad on the pattern, bias grad), each output paired with
             S = sum of |products| for the tolerance rule;
   meta.py   CSR / CSC / perm metadata by direct scan of the block mask;
-  brute.py  exact Fraction brute force over the dense zero-filled weight.
+  brute.py  exact Fraction brute force over the dense zero-filled weight;
+  convert.py dense <-> BSR conversion and block-magnitude pattern selection
+            (block norms from oracle.c, top-k by a plain sort, gather and
+            scatter of blocks by plain loops).
 
 The acceptance rule for a bf16 result g against the fp64 value o is
 |g - o| <= 4e-3 * S(o), and g == o exactly where S(o) == 0.
@@ -54,7 +57,8 @@ def lib():
         L.oracle_dx.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_dw.argtypes = [i64, i32, i32, i32, P, P, P, P, P, i32, P, P]
         L.oracle_db.argtypes = [i64, i32, P, P, P]
-        for f in (L.oracle_fwd, L.oracle_dx, L.oracle_dw, L.oracle_db):
+        L.oracle_block_norms.argtypes = [i32, i32, i32, i32, P, P]
+        for f in (L.oracle_fwd, L.oracle_dx, L.oracle_dw, L.oracle_db, L.oracle_block_norms):
             f.restype = None
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -122,6 +126,18 @@ def db(dY, want_s: bool = True):
     S = np.empty((N,), dtype=np.float64) if want_s else None
     lib().oracle_db(M, N, _p(dY), _p(out), _p(S))
     return out, S
+
+
+def block_norms(W, b: int, kind: int = 1) -> np.ndarray:
+    """Per-block magnitude of a dense weight W [N, K]: kind 1 = L1, kind 2 = squared L2.
+    Returns an fp64 [N/b, K/b] array (summation order stated in oracle.c)."""
+    if kind not in (1, 2):
+        raise ValueError("kind must be 1 (L1) or 2 (squared L2)")
+    W = _f64(W)
+    N, K = W.shape
+    out = np.empty((N // b, K // b), dtype=np.float64)
+    lib().oracle_block_norms(N, K, b, kind, _p(W), _p(out))
+    return out
 
 
 def max_threads() -> int:

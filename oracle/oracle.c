@@ -167,6 +167,33 @@ void oracle_db(int64_t M, int32_t N, const double *dY, double *db, double *S)
     }
 }
 
+/* Block magnitudes of a dense weight W [N][K] (pytorch/ao sparsity README,
+ * Table 4.2: the magnitude criterion removes the parameters with the lowest
+ * norm, L1 being the usual one; the criteria list's "weights" option scores
+ * with the weight tensor alone). For block (r, c):
+ *   norm = sum over p ascending of ( sum over q ascending of t(W[r*b+p][c*b+q]) )
+ * with t(w) = |w| (kind 1, L1) or w*w (kind 2, squared L2), every sum taken
+ * left to right in fp64 starting from 0. norms is [N/b][K/b] row-major. */
+void oracle_block_norms(int32_t N, int32_t K, int32_t b, int32_t kind,
+                        const double *W, double *norms)
+{
+    const int32_t R = N / b, C = K / b;
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < R; ++r) {
+        for (int32_t c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int32_t p = 0; p < b; ++p) {
+                const double *w = W + ((int64_t)r * b + p) * K + (int64_t)c * b;
+                double row = 0.0;
+                for (int32_t q = 0; q < b; ++q)
+                    row += kind == 1 ? fabs(w[q]) : w[q] * w[q];
+                acc += row;
+            }
+            norms[(int64_t)r * C + c] = acc;
+        }
+    }
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_max_threads(void)
 {

@@ -11,7 +11,7 @@ initialisation, "Future Development Roadmap").
 
 Random streams: one integer seed per workload; stream k of the seed is
 ``numpy.random.default_rng([seed, k])`` with k = 0 pattern, 1 X, 2 V, 3 bias,
-4 dY. Values are drawn for nonzero blocks only, in CSR order (row-major over
+4 dY, 5 a dense weight (dense-to-BSR conversion), 6 its per-block scales. Values are drawn for nonzero blocks only, in CSR order (row-major over
 the block grid). Normal draws are fp32 and are rounded to bf16 with
 round-to-nearest-even (``torch.Tensor.to(torch.bfloat16)``).
 """
@@ -26,6 +26,7 @@ import numpy as np
 import torch
 
 STREAM_PATTERN, STREAM_X, STREAM_V, STREAM_BIAS, STREAM_DY = 0, 1, 2, 3, 4
+STREAM_W, STREAM_W_SCALE = 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -162,6 +163,17 @@ def bias_vector(N: int, seed: int) -> torch.Tensor:
 
 def grad_output(M: int, N: int, seed: int) -> torch.Tensor:
     return normal_bf16((M, N), 1.0, seed, STREAM_DY)
+
+
+def dense_weight(N: int, K: int, seed: int, b: Optional[int] = None) -> torch.Tensor:
+    """A dense [N, K] bf16 weight ~ N(0, 0.02^2). With a block size b, every b x b block is
+    also multiplied by its own factor exp(g), g ~ N(0, 1), before the rounding to bf16, so
+    block magnitudes differ the way a trained layer's do (seeded; no trained weights)."""
+    a = rng(seed, STREAM_W).standard_normal(size=(N, K), dtype=np.float32) * np.float32(0.02)
+    if b is not None:
+        f = np.exp(rng(seed, STREAM_W_SCALE).standard_normal(size=(N // b, K // b))).astype(np.float32)
+        a *= np.repeat(np.repeat(f, b, axis=0), b, axis=1)
+    return to_bf16(a)
 
 
 def make_inputs(w: Workload, seed: int = 0, mask: Optional[np.ndarray] = None, with_dy: Optional[bool] = None):
