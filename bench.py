@@ -340,6 +340,63 @@ def _run_oracle(w, md, host, X64, dY64, rows):
             oracle.dw(dY64[:rows], X64[:rows], md["row_ptr"], md["col_idx"], w.b, want_s=False)
 
 
+def time_launches(fn, nsets: int, reps: int) -> float:
+    """Average ms per launch of fn(k) over reps launches cycling nsets buffer sets, HIP events
+    on the launch stream with the queue pre-filled behind a spin kernel."""
+    import torch
+    for k in range(min(3, reps)):
+        fn(k)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(20.0 * _CYC_PER_MS))
+    a.record()
+    for k in range(reps):
+        fn(k)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+CONVERT_WORKLOAD = 5   # the largest weight of the reference workloads: 11008 x 4096, Zipf rows
+
+
+def convert_leg(dev, reps: int) -> dict:
+    """Dense <-> BSR conversion and block magnitudes (bsr_block_norms, bsr_dense_to_values,
+    bsr_values_to_dense) on the weight of the Zipf workload, cold (rotated sets), with their
+    algorithmic bytes and the fraction of HBM peak."""
+    import torch
+    from sparse_gemm_amd import binding, synth
+    w = synth.WORKLOADS[CONVERT_WORKLOAD]
+    mask = synth.block_mask(w, 0)
+    p = binding.Pattern.from_mask(mask, w.N, w.K, w.b)
+    nnzb, R, C, b = p.nnzb, w.R, w.C, w.b
+    dense_bytes = 2 * w.N * w.K
+    nsets = max(1, -(-ROTATE_BYTES // dense_bytes))
+    W0 = synth.dense_weight(w.N, w.K, 0, b=b).to(dev)
+    Ws = [W0] + [W0.clone() for _ in range(nsets - 1)]
+    Vs = [torch.empty((nnzb, b, b), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    Ns = [torch.empty((R, C), dtype=torch.float64, device=dev) for _ in range(nsets)]
+    Ds = [torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    csr = 4 * (R + 1) + 4 * nnzb
+    legs = {
+        "block_norms_l1": (lambda k: binding.block_norms(Ws[k % nsets], b, 1, out=Ns[k % nsets]),
+                           dense_bytes + 8 * R * C),
+        "dense_to_values": (lambda k: binding.dense_to_values(p, Ws[k % nsets], out=Vs[k % nsets]),
+                            2 * 2 * b * b * nnzb + csr),
+        "values_to_dense": (lambda k: binding.values_to_dense(p, Vs[k % nsets], out=Ds[k % nsets]),
+                            2 * b * b * nnzb + dense_bytes + csr),
+    }
+    out = {"weight": f"{w.N}x{w.K}, b {b}, nnzb {nnzb} ({w.pattern} rows, density {w.density})",
+           "buffers": f"cold ({nsets} rotated sets)"}
+    for name, (fn, by) in legs.items():
+        ms = time_launches(fn, nsets, reps)
+        out[name] = {"us": ms * 1e3, "bytes": by, "gbs": by / (ms * 1e-3) / 1e9,
+                     "pct_hbm_peak": 100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del Ws, Vs, Ns, Ds
+    p.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +537,9 @@ def main():
         h_ms, _, _ = time_graph(dense_step, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
         out["hipblaslt_dense_context"] = {"ms_per_step": h_ms, "speedup_of_sparse": h_ms / step_ms}
         del sets_d, dense_w, pd
+
+        log("[bench] dense <-> BSR conversion kernels")
+        out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
 
     if args.calibrate_copy:
         src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev)

@@ -81,6 +81,18 @@ class Pattern:
         return cls(h, upload, dev)
 
     @classmethod
+    def from_dense(cls, W: torch.Tensor, b: int, keep: int, kind: int = 1) -> "Pattern":
+        """Pattern of the `keep` blocks of largest norm of the dense device weight W [N, K]
+        (kind 1 = L1, 2 = squared L2), via bsr_pattern_create_from_dense."""
+        N, K = W.shape
+        dev = cls._device(True)
+        _check_tensor(W, "W", (N, K), dev)
+        h = ctypes.c_void_p()
+        _lib.check(lib().bsr_pattern_create_from_dense(N, K, b, _ptr(W), int(kind), int(keep), _stream(dev),
+                                                       ctypes.byref(h)), "bsr_pattern_create_from_dense")
+        return cls(h, True, dev)
+
+    @classmethod
     def from_csr(cls, N: int, K: int, b: int, row_ptr, col_idx, upload: bool = True) -> "Pattern":
         rp, ci = _i32(row_ptr), _i32(col_idx)
         dev = cls._device(upload)
@@ -190,3 +202,52 @@ def linear_bwd_weight(p: Pattern, dY: torch.Tensor, X: torch.Tensor, want_dbias:
     _lib.check(lib().bsr_linear_bwd_weight(p.handle, _ptr(dY), _ptr(X), M, _ptr(out), _ptr(dbias), _ptr(workspace),
                                            ws_bytes, _stream(p.device)), "bsr_linear_bwd_weight")
     return out, dbias
+
+
+# ---- dense <-> BSR conversion and block magnitudes (include/bsr_convert.h) ----
+
+NORM_L1, NORM_L2_SQUARED = 1, 2
+
+
+def block_norms(W: torch.Tensor, b: int, kind: int = NORM_L1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp64 [N/b, K/b] block magnitudes of the dense device weight W [N, K] via bsr_block_norms."""
+    N, K = W.shape
+    dev = W.device.index
+    _check_tensor(W, "W", (N, K), dev)
+    if out is None:
+        out = torch.empty((N // b, K // b), dtype=torch.float64, device=W.device)
+    if out.dtype != torch.float64 or tuple(out.shape) != (N // b, K // b) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp64 [N/b, K/b] tensor")
+    _lib.check(lib().bsr_block_norms(N, K, b, _ptr(W), int(kind), _ptr(out), _stream(dev)), "bsr_block_norms")
+    return out
+
+
+def mask_topk(norms, keep: int) -> np.ndarray:
+    """Host [R, C] uint8 mask of the `keep` largest block norms (ties to the lower index)
+    via bsr_mask_topk."""
+    n = np.ascontiguousarray(np.asarray(norms, dtype=np.float64))
+    R, C = n.shape
+    mask = np.empty((R, C), dtype=np.uint8)
+    _lib.check(lib().bsr_mask_topk(R, C, n.ctypes.data_as(ctypes.c_void_p), int(keep),
+                                   mask.ctypes.data_as(ctypes.c_void_p)), "bsr_mask_topk")
+    return mask
+
+
+def dense_to_values(p: Pattern, W: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """V [nnzb, b, b]: the kept blocks of the dense device weight W [N, K], via bsr_dense_to_values."""
+    _check_tensor(W, "W", (p.N, p.K), p.device)
+    if out is None:
+        out = torch.empty((p.nnzb, p.b, p.b), dtype=torch.bfloat16, device=W.device)
+    _check_tensor(out, "out", (p.nnzb, p.b, p.b), p.device)
+    _lib.check(lib().bsr_dense_to_values(p.handle, _ptr(W), _ptr(out), _stream(p.device)), "bsr_dense_to_values")
+    return out
+
+
+def values_to_dense(p: Pattern, V: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dense [N, K] weight with zeros outside the kept blocks, via bsr_values_to_dense."""
+    _check_tensor(V, "V", (p.nnzb, p.b, p.b), p.device)
+    if out is None:
+        out = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=V.device)
+    _check_tensor(out, "out", (p.N, p.K), p.device)
+    _lib.check(lib().bsr_values_to_dense(p.handle, _ptr(V), _ptr(out), _stream(p.device)), "bsr_values_to_dense")
+    return out

@@ -8,7 +8,7 @@
 #include <utility>
 #include <vector>
 
-#include "bsr_internal.hpp"
+#include "bsr_convert_internal.hpp"
 
 namespace bsr {
 
@@ -281,6 +281,75 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
     }
     DwArgs a{dY, X, M, dV, dbias, workspace, ws_bytes};
     return launch_dw(*p, a, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_block_norms(int32_t N, int32_t K, int32_t b, const bsr_bf16 *W, int32_t kind, double *norms,
+                        void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_shape(N, K, b));
+    if (kind != BSR_NORM_L1 && kind != BSR_NORM_L2_SQUARED) return fail(BSR_ERR_INVALID_ARG, "unknown norm kind");
+    if ((int64_t)(N / b) * (K / b) > (int64_t)INT32_MAX / 8) return fail(BSR_ERR_INVALID_ARG, "too many blocks");
+    BSR_CHECK(check_ptr(W, "W"));
+    BSR_CHECK(check_ptr(norms, "norms"));
+    return launch_block_norms(N, K, b, W, kind, norms, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_mask_topk(int32_t R, int32_t C, const double *norms, int64_t keep, uint8_t *mask) {
+    BSR_TRY_BEGIN
+    if (R <= 0 || C <= 0) return fail(BSR_ERR_INVALID_ARG, "R and C must be positive");
+    if (keep < 0 || keep > (int64_t)R * C) return fail(BSR_ERR_INVALID_ARG, "keep must lie in [0, R*C]");
+    if (!norms || !mask) return fail(BSR_ERR_INVALID_ARG, "norms and mask must not be NULL");
+    return mask_topk(R, C, norms, keep, mask);
+    BSR_TRY_END
+}
+
+int32_t bsr_pattern_create_from_dense(int32_t N, int32_t K, int32_t b, const bsr_bf16 *W, int32_t kind,
+                                      int64_t keep, void *stream, bsr_pattern **out) {
+    BSR_TRY_BEGIN
+    if (!out) return fail(BSR_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    BSR_CHECK(check_shape(N, K, b));
+    const int32_t R = N / b, C = K / b;
+    if (keep < 0 || keep > (int64_t)R * C) return fail(BSR_ERR_INVALID_ARG, "keep must lie in [0, R*C]");
+    const size_t bytes = sizeof(double) * (size_t)R * (size_t)C;
+    double *dnorms = nullptr;
+    hipError_t e = hipMalloc(&dnorms, bytes);
+    if (e == hipErrorOutOfMemory) return fail(BSR_ERR_OUT_OF_MEMORY, "hipMalloc of the block norms failed");
+    if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("hipMalloc: ") + hipGetErrorString(e));
+    std::vector<double> norms((size_t)R * C);
+    int32_t st = bsr_block_norms(N, K, b, W, kind, dnorms, stream);
+    if (st == BSR_OK) {
+        hipStream_t hs = static_cast<hipStream_t>(stream);
+        e = hipMemcpyAsync(norms.data(), dnorms, bytes, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) st = fail(BSR_ERR_HIP, std::string("copying the block norms: ") + hipGetErrorString(e));
+    }
+    (void)hipFree(dnorms);
+    if (st != BSR_OK) return st;
+    std::vector<uint8_t> mask((size_t)R * C);
+    BSR_CHECK(mask_topk(R, C, norms.data(), keep, mask.data()));
+    return bsr_pattern_create_from_mask(N, K, b, mask.data(), 1, out);
+    BSR_TRY_END
+}
+
+int32_t bsr_dense_to_values(const bsr_pattern *p, const bsr_bf16 *W, bsr_bf16 *V, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(W, "W"));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    return launch_dense_to_values(*p, W, V, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_values_to_dense(const bsr_pattern *p, const bsr_bf16 *V, bsr_bf16 *W, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    BSR_CHECK(check_ptr(W, "W"));
+    if (p->R >= 65536) return fail(BSR_ERR_INVALID_ARG, "N/b must be below 65536");
+    return launch_values_to_dense(*p, V, W, stream);
     BSR_TRY_END
 }
 

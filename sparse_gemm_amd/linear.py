@@ -100,34 +100,54 @@ class BlockSparseLinear(nn.Module):
         return bsr_linear(x, self.pattern, self.values, self.bias)
 
     def block_mask(self) -> np.ndarray:
-        meta = self.pattern.export()
-        mask = np.zeros((self.pattern.R, self.pattern.C), dtype=np.uint8)
-        for r in range(self.pattern.R):
-            mask[r, meta["col_idx"][meta["row_ptr"][r]:meta["row_ptr"][r + 1]]] = 1
-        return mask
+        return self._mask_of(self.pattern)
 
     @torch.no_grad()
     def to_dense(self) -> torch.Tensor:
         """Dense weight [out, in] with zeros outside the kept blocks (the hand-off format of
-        the pytorch/ao sparsity README, workflow section). Computed by the forward kernel on
-        the identity, Y = I . W~^T: each output has one product, so it is exact."""
-        eye = torch.eye(self.in_features, dtype=torch.bfloat16, device=self.values.device)
-        return binding.linear_fwd(self.pattern, eye, self.values.detach().contiguous()).t().contiguous()
+        the pytorch/ao sparsity README, workflow section), written by bsr_values_to_dense."""
+        return binding.values_to_dense(self.pattern, self.values.detach().contiguous())
 
     @classmethod
     @torch.no_grad()
     def from_dense(cls, linear: nn.Linear, block_mask: np.ndarray, block_size: int = 32) -> "BlockSparseLinear":
-        """Keep the blocks of a dense nn.Linear that block_mask selects."""
-        W = linear.weight.detach()
+        """Keep the blocks of a dense nn.Linear that block_mask selects (bsr_dense_to_values)."""
+        W = linear.weight.detach().to(torch.bfloat16).contiguous()
         out_f, in_f = W.shape
         m = cls(in_f, out_f, bias=linear.bias is not None, block_size=block_size, mask=block_mask, device=W.device)
-        R, C, b = out_f // block_size, in_f // block_size, block_size
-        blocks = W.to(torch.bfloat16).reshape(R, b, C, b).permute(0, 2, 1, 3)
-        keep = torch.from_numpy(np.asarray(block_mask) != 0).to(W.device)
-        m.values.copy_(blocks[keep].contiguous())   # row-major over the block grid = CSR order
+        binding.dense_to_values(m.pattern, W, out=m.values.data)
         if linear.bias is not None:
             m.bias.copy_(linear.bias.detach().to(torch.bfloat16))
         return m
+
+    @classmethod
+    @torch.no_grad()
+    def from_dense_by_magnitude(cls, linear: nn.Linear, density: float, block_size: int = 32,
+                                norm: int = binding.NORM_L1) -> "BlockSparseLinear":
+        """Magnitude pruning at block granularity (pytorch/ao sparsity README, Table 4.2: drop
+        the lowest norms, L1 by default; layer-local scope): keep the floor(density*R*C + 0.5)
+        blocks of largest norm of the dense weight, then read them into BSR."""
+        W = linear.weight.detach().to(torch.bfloat16).contiguous()
+        out_f, in_f = W.shape
+        R, C = out_f // block_size, in_f // block_size
+        keep = max(0, min(R * C, int(math.floor(density * R * C + 0.5))))
+        with torch.cuda.device(W.device):
+            p = Pattern.from_dense(W, block_size, keep, norm)
+        m = cls(in_f, out_f, bias=linear.bias is not None, block_size=block_size, mask=cls._mask_of(p),
+                device=W.device)
+        p.close()
+        binding.dense_to_values(m.pattern, W, out=m.values.data)
+        if linear.bias is not None:
+            m.bias.copy_(linear.bias.detach().to(torch.bfloat16))
+        return m
+
+    @staticmethod
+    def _mask_of(p: Pattern) -> np.ndarray:
+        meta = p.export()
+        mask = np.zeros((p.R, p.C), dtype=np.uint8)
+        for r in range(p.R):
+            mask[r, meta["col_idx"][meta["row_ptr"][r]:meta["row_ptr"][r + 1]]] = 1
+        return mask
 
     def _load_from_state_dict(self, state_dict, prefix, local_metadata, strict, missing_keys, unexpected_keys,
                               error_msgs):

@@ -13,14 +13,17 @@ from sparse_gemm_amd import _lib, synth
 from sparse_gemm_amd.binding import Pattern
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bsr_linear.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(bsr_[a-z_]+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(bsr_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declarations_are_exported():
@@ -129,3 +132,44 @@ def test_workspace_query_is_host_only():
     assert L.bsr_linear_bwd_weight_workspace(p.handle, 0) == 0
     assert L.bsr_linear_bwd_weight_workspace(p.handle, w.M) > 0
     assert L.bsr_linear_bwd_weight_workspace(None, w.M) == 0
+
+
+# ---- host half of the block-magnitude selection: bsr_mask_topk against the oracle ----
+
+def test_mask_topk_matches_oracle_golden():
+    import json
+    from oracle import convert
+    from sparse_gemm_amd import binding
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "block_norms_b2.json")))
+    for case in g["masks"]:
+        norms = np.array(g["l1"] if case["kind"] == 1 else g["l2sq"], dtype=np.float64)
+        assert np.array_equal(binding.mask_topk(norms, case["keep"]), np.array(case["mask"])), case
+        assert np.array_equal(binding.mask_topk(norms, case["keep"]), convert.topk_mask(norms, case["keep"]))
+
+
+@pytest.mark.parametrize("R,C,seed", [(1, 1, 0), (7, 5, 1), (96, 24, 2), (344, 128, 3)])
+def test_mask_topk_matches_oracle_random(R, C, seed):
+    """Bit-exact masks, with many ties (quantised norms) and with distinct norms."""
+    from oracle import convert
+    from sparse_gemm_amd import binding
+    g = np.random.default_rng(seed)
+    for quant in (True, False):
+        norms = g.random((R, C))
+        if quant:
+            norms = np.round(norms * 8) / 8
+        for keep in sorted({0, 1, (R * C) // 3, (R * C) // 2, R * C - 1, R * C}):
+            if keep < 0:
+                continue
+            assert np.array_equal(binding.mask_topk(norms, keep), convert.topk_mask(norms, keep)), (quant, keep)
+
+
+def test_mask_topk_rejects_bad_input():
+    from sparse_gemm_amd import binding
+    with pytest.raises(_lib.BsrError):
+        binding.mask_topk(np.array([[1.0, np.nan]]), 1)
+    with pytest.raises(_lib.BsrError):
+        binding.mask_topk(np.ones((2, 2)), 5)
+    with pytest.raises(_lib.BsrError):
+        binding.mask_topk(np.ones((2, 2)), -1)
+    m = binding.mask_topk(np.array([[np.inf, 1.0, np.inf]]), 1)
+    assert m.tolist() == [[1, 0, 0]]
