@@ -10,6 +10,8 @@ Parts:
             S = sum of |products| for the tolerance rule;
   meta.py   CSR / CSC / perm metadata by direct scan of the block mask;
   brute.py  exact Fraction brute force over the dense zero-filled weight;
+  oracle.c  also: fp8 (OCP E4M3) block values with a power-of-two scale per
+            block (quantise, dequantise);
   convert.py dense <-> BSR conversion and block-magnitude pattern selection
             (block norms from oracle.c, top-k by a plain sort, gather and
             scatter of blocks by plain loops).
@@ -58,7 +60,12 @@ def lib():
         L.oracle_dw.argtypes = [i64, i32, i32, i32, P, P, P, P, P, i32, P, P]
         L.oracle_db.argtypes = [i64, i32, P, P, P]
         L.oracle_block_norms.argtypes = [i32, i32, i32, i32, P, P]
-        for f in (L.oracle_fwd, L.oracle_dx, L.oracle_dw, L.oracle_db, L.oracle_block_norms):
+        L.oracle_quantize_fp8.argtypes = [i32, i32, P, P, P]
+        L.oracle_dequantize_fp8.argtypes = [i32, i32, P, P, P]
+        L.oracle_e4m3_value.argtypes, L.oracle_e4m3_value.restype = [ctypes.c_uint8], ctypes.c_double
+        L.oracle_e4m3_encode.argtypes, L.oracle_e4m3_encode.restype = [ctypes.c_double], ctypes.c_uint8
+        for f in (L.oracle_fwd, L.oracle_dx, L.oracle_dw, L.oracle_db, L.oracle_block_norms, L.oracle_quantize_fp8,
+                  L.oracle_dequantize_fp8):
             f.restype = None
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -137,6 +144,34 @@ def block_norms(W, b: int, kind: int = 1) -> np.ndarray:
     N, K = W.shape
     out = np.empty((N // b, K // b), dtype=np.float64)
     lib().oracle_block_norms(N, K, b, kind, _p(W), _p(out))
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return float(lib().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def quantize_fp8(V):
+    """(codes uint8 [nnzb, b, b], scale exponents int32 [nnzb]) of block values V [nnzb, b, b]."""
+    V = _f64(V)
+    nnzb, b, _ = V.shape
+    codes = np.empty((nnzb, b, b), dtype=np.uint8)
+    se = np.empty((nnzb,), dtype=np.int32)
+    lib().oracle_quantize_fp8(nnzb, b, _p(V), _p(codes), _p(se))
+    return codes, se
+
+
+def dequantize_fp8(codes, se) -> np.ndarray:
+    """fp64 [nnzb, b, b]: code value * 2^se per block."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    se = _i32(se)
+    nnzb, b, _ = codes.shape
+    out = np.empty((nnzb, b, b), dtype=np.float64)
+    lib().oracle_dequantize_fp8(nnzb, b, _p(codes), _p(se), _p(out))
     return out
 
 

@@ -194,6 +194,77 @@ void oracle_block_norms(int32_t N, int32_t K, int32_t b, int32_t kind,
     }
 }
 
+/* ---- fp8 (OCP E4M3) block values with one power-of-two scale per block ----
+ * (pytorch_block_sparse summary page and Lecture 11 at 30:31 and 48:12: sparsity combined with
+ * quantization; for memory-bound layers the weights are loaded in a compact form and expanded
+ * on the GPU before a dense product.)
+ *
+ * E4M3 as defined by the OCP 8-bit floating point specification: 1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; 0x7F and 0xFF
+ * are NaN; the largest finite magnitude is 448 = 1.75 * 2^8. */
+
+/* Value of an E4M3 code (NaN codes give NaN). */
+double oracle_e4m3_value(uint8_t c)
+{
+    const int s = c >> 7, E = (c >> 3) & 15, m = c & 7;
+    if (E == 15 && m == 7) return NAN;
+    const double v = E ? ldexp(1.0 + m / 8.0, E - 7) : ldexp((double)m, -9);
+    return s ? -v : v;
+}
+
+/* Nearest E4M3 code of x, ties to the even code, |x| <= 448 (the caller guarantees it); the
+ * sign of x (also of a zero result) is kept. */
+uint8_t oracle_e4m3_encode(double x)
+{
+    const uint8_t s = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs(x);
+    if (a < ldexp(1.0, -6)) {                      /* subnormal grid, step 2^-9 */
+        const double k = nearbyint(ldexp(a, 9));   /* 0 .. 8; RNE in the default mode */
+        if (k >= 8.0) return s | 0x08;             /* rounds up to the smallest normal */
+        return s | (uint8_t)k;
+    }
+    int E;
+    const double f = frexp(a, &E);                 /* a = f * 2^E, f in [0.5, 1) */
+    double m = nearbyint((2.0 * f - 1.0) * 8.0);   /* mantissa of a = (1 + m/8) 2^(E-1) */
+    int e = E - 1;
+    if (m >= 8.0) {
+        m = 0.0;
+        e += 1;
+    }
+    return s | (uint8_t)((e + 7) << 3) | (uint8_t)m;
+}
+
+/* Per block i: amax = max |V[i]|; scale exponent se[i] = the smallest integer e >= -126 with
+ * amax <= 448 * 2^e (0 for an all-zero block); codes = E4M3 code of V / 2^se[i] for every
+ * element. V is [nnzb][b][b] (fp64 values of bf16 inputs). */
+void oracle_quantize_fp8(int32_t nnzb, int32_t b, const double *V, uint8_t *codes, int32_t *se)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t i = 0; i < nnzb; ++i) {
+        const double *v = V + (int64_t)i * b * b;
+        double amax = 0.0;
+        for (int32_t k = 0; k < b * b; ++k)
+            if (fabs(v[k]) > amax) amax = fabs(v[k]);
+        int32_t e = 0;
+        if (amax > 0.0) {
+            e = -126;
+            while (amax > ldexp(448.0, e)) ++e;
+        }
+        se[i] = e;
+        for (int32_t k = 0; k < b * b; ++k)
+            codes[(int64_t)i * b * b + k] = oracle_e4m3_encode(ldexp(v[k], -e));
+    }
+}
+
+/* Dequantised values: code value * 2^se[i], as fp64. */
+void oracle_dequantize_fp8(int32_t nnzb, int32_t b, const uint8_t *codes, const int32_t *se, double *V)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t i = 0; i < nnzb; ++i)
+        for (int32_t k = 0; k < b * b; ++k)
+            V[(int64_t)i * b * b + k] = ldexp(oracle_e4m3_value(codes[(int64_t)i * b * b + k]), se[i]);
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_max_threads(void)
 {
