@@ -397,6 +397,47 @@ def convert_leg(dev, reps: int) -> dict:
     return out
 
 
+FP8_WORKLOAD = 4   # the memory-bound decode shape: X[8,4096], W[14336,4096], 64 x 64 blocks
+
+
+def fp8_leg(dev, reps: int) -> dict:
+    """The decode forward with fp8 (E4M3) block values and a power-of-two scale per block
+    (bsr_linear_fwd_fp8) beside the bf16 forward (bsr_linear_fwd) on the same pattern, cold
+    (rotated value sets), with algorithmic bytes and the fraction of HBM peak."""
+    import torch
+    from sparse_gemm_amd import binding, synth
+    w = synth.WORKLOADS[FP8_WORKLOAD]
+    host = synth.make_inputs(w, 0)
+    p = binding.Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    nnzb, R = p.nnzb, w.R
+    X = host["X"].to(dev)
+    Y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    V0 = host["V"].to(dev)
+    code_bytes = nnzb * w.b * w.b
+    nsets = max(1, -(-ROTATE_BYTES // code_bytes))
+    q = [binding.values_quantize_fp8(p, V0)]
+    q += [(a.clone(), s_.clone()) for a, s_ in [q[0]] * (nsets - 1)]
+    nsets16 = max(1, -(-ROTATE_BYTES // (2 * code_bytes)))
+    V16 = [V0] + [V0.clone() for _ in range(nsets16 - 1)]
+    meta = 4 * (R + 1) + 4 * nnzb
+    act = 2 * w.M * w.K + 2 * w.M * w.N
+    by8 = code_bytes + 4 * nnzb + act + meta
+    by16 = 2 * code_bytes + act + meta
+    ms8 = time_launches(lambda k: binding.linear_fwd_fp8(p, X, q[k % nsets][0], q[k % nsets][1], out=Y), nsets, reps)
+    ms16 = time_launches(lambda k: binding.linear_fwd(p, X, V16[k % nsets16], out=Y), nsets16, reps)
+    F = 2.0 * w.M * w.b * w.b * nnzb
+    out = {"workload": w.name, "buffers": f"cold ({nsets} rotated fp8 value sets, {nsets16} bf16)",
+           "fwd_fp8": {"us": ms8 * 1e3, "bytes": by8, "gbs": by8 / (ms8 * 1e-3) / 1e9,
+                       "pct_hbm_peak": 100 * by8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "tflops": F / (ms8 * 1e-3) / 1e12},
+           "fwd_bf16": {"us": ms16 * 1e3, "bytes": by16, "gbs": by16 / (ms16 * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100 * by16 / (ms16 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+           "speedup_fp8_vs_bf16": ms16 / ms8}
+    del q, V16
+    p.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,6 +581,8 @@ def main():
 
         log("[bench] dense <-> BSR conversion kernels")
         out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
+        log("[bench] fp8 block values, decode forward")
+        out["next_rows"]["fp8_decode"] = fp8_leg(dev, max(50, args.steps))
 
     if args.calibrate_copy:
         src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev)

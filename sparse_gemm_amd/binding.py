@@ -251,3 +251,59 @@ def values_to_dense(p: Pattern, V: torch.Tensor, out: Optional[torch.Tensor] = N
     _check_tensor(out, "out", (p.N, p.K), p.device)
     _lib.check(lib().bsr_values_to_dense(p.handle, _ptr(V), _ptr(out), _stream(p.device)), "bsr_values_to_dense")
     return out
+
+
+# ---- fp8 (OCP E4M3) block values with a power-of-two scale per block (include/bsr_fp8.h) ----
+
+def values_quantize_fp8(p: Pattern, V: torch.Tensor, out=None):
+    """(codes uint8 [nnzb, b, b], scale exponents int32 [nnzb]) via bsr_values_quantize_fp8."""
+    _check_tensor(V, "V", (p.nnzb, p.b, p.b), p.device)
+    if out is None:
+        out = (torch.empty((p.nnzb, p.b, p.b), dtype=torch.uint8, device=V.device),
+               torch.empty((p.nnzb,), dtype=torch.int32, device=V.device))
+    V8, se = out
+    _check_raw(V8, "V8", (p.nnzb, p.b, p.b), torch.uint8, p.device)
+    _check_raw(se, "se", (p.nnzb,), torch.int32, p.device)
+    _lib.check(lib().bsr_values_quantize_fp8(p.handle, _ptr(V), _ptr(V8), _ptr(se), _stream(p.device)),
+               "bsr_values_quantize_fp8")
+    return V8, se
+
+
+def values_dequantize_fp8(p: Pattern, V8: torch.Tensor, se: torch.Tensor, out=None) -> torch.Tensor:
+    """bf16 [nnzb, b, b] = code * 2^se via bsr_values_dequantize_fp8."""
+    _check_raw(V8, "V8", (p.nnzb, p.b, p.b), torch.uint8, p.device)
+    _check_raw(se, "se", (p.nnzb,), torch.int32, p.device)
+    if out is None:
+        out = torch.empty((p.nnzb, p.b, p.b), dtype=torch.bfloat16, device=V8.device)
+    _check_tensor(out, "out", (p.nnzb, p.b, p.b), p.device)
+    _lib.check(lib().bsr_values_dequantize_fp8(p.handle, _ptr(V8), _ptr(se), _ptr(out), _stream(p.device)),
+               "bsr_values_dequantize_fp8")
+    return out
+
+
+def linear_fwd_fp8(p: Pattern, X: torch.Tensor, V8: torch.Tensor, se: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W8~^T + bias with fp8 block values, via bsr_linear_fwd_fp8."""
+    M = X.shape[0]
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_raw(V8, "V8", (p.nnzb, p.b, p.b), torch.uint8, p.device)
+    _check_raw(se, "se", (p.nnzb,), torch.int32, p.device)
+    if bias is not None:
+        _check_tensor(bias, "bias", (p.N,), p.device)
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, p.N), p.device)
+    _lib.check(lib().bsr_linear_fwd_fp8(p.handle, _ptr(X), M, _ptr(V8), _ptr(se), _ptr(bias), _ptr(out),
+                                        _stream(p.device)), "bsr_linear_fwd_fp8")
+    return out
+
+
+def _check_raw(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device.index != device:
+        raise ValueError(f"{name} must be on cuda:{device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "bsr_convert_internal.hpp"
+#include "bsr_fp8_internal.hpp"
 
 namespace bsr {
 
@@ -350,6 +351,46 @@ int32_t bsr_values_to_dense(const bsr_pattern *p, const bsr_bf16 *V, bsr_bf16 *W
     BSR_CHECK(check_ptr(W, "W"));
     if (p->R >= 65536) return fail(BSR_ERR_INVALID_ARG, "N/b must be below 65536");
     return launch_values_to_dense(*p, V, W, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_values_quantize_fp8(const bsr_pattern *p, const bsr_bf16 *V, uint8_t *V8, int32_t *se, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    BSR_CHECK(check_ptr(V8, "V8", p->nnzb == 0));
+    if (p->nnzb > 0 && (!se || ((uintptr_t)se & 3u)))
+        return fail(se ? BSR_ERR_MISALIGNED : BSR_ERR_INVALID_ARG, "se must be a 4-byte aligned device pointer");
+    return launch_quantize_fp8(*p, V, V8, se, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_values_dequantize_fp8(const bsr_pattern *p, const uint8_t *V8, const int32_t *se, bsr_bf16 *V,
+                                  void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(V8, "V8", p->nnzb == 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    if (p->nnzb > 0 && (!se || ((uintptr_t)se & 3u)))
+        return fail(se ? BSR_ERR_MISALIGNED : BSR_ERR_INVALID_ARG, "se must be a 4-byte aligned device pointer");
+    return launch_dequantize_fp8(*p, V8, se, V, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_linear_fwd_fp8(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint8_t *V8, const int32_t *se,
+                           const bsr_bf16 *bias, bsr_bf16 *Y, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(V8, "V8", p->nnzb == 0));
+    if (p->nnzb > 0 && (!se || ((uintptr_t)se & 3u)))
+        return fail(se ? BSR_ERR_MISALIGNED : BSR_ERR_INVALID_ARG, "se must be a 4-byte aligned device pointer");
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the fp8 forward takes M below 2^20");
+    if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
+    if (M == 0) return BSR_OK;
+    return launch_fwd_fp8(*p, X, M, V8, se, bias, Y, stream);
     BSR_TRY_END
 }
 
