@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <string>
 
 #include "bsr_fp8_internal.hpp"
@@ -289,23 +290,34 @@ int32_t launch_dequantize_fp8(const bsr_pattern &p, const uint8_t *V8, const int
     return launched("dequantize_fp8 launch");
 }
 
+template <int BS, int NW, int U, int PSW>
+void launch_fwd_fp8_cfg(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint8_t *V8, const int32_t *se,
+                        const uint16_t *bias, uint16_t *Y, hipStream_t st) {
+    const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)), (unsigned)((M + 15) / 16));
+    hipLaunchKernelGGL((k_fwd_fp8<BS, NW, U, PSW>), grid, dim3(NW * 64), 0, st, X, p.K, (int)M, V8, se, bias, Y, p.N,
+                       p.dev.col_idx, p.dev.small_m_rows);
+}
+
 int32_t launch_fwd_fp8(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint8_t *V8, const int32_t *se,
                        const uint16_t *bias, uint16_t *Y, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    const unsigned chunks = (unsigned)((M + 15) / 16);
-    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group; b = 64: 8 waves
-    // x 4 blocks (the same bytes in flight as the bf16 kernel's 2), two of the four slices per
-    // work-group, two work-groups per block row.
+    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group. b = 64: waves,
+    // blocks in flight per wave and 16-row slices per work-group (of 4) by configuration.
     if (p.b == 32) {
-        constexpr int NW = 8, U = 8, PSW = 2;
-        const dim3 grid((unsigned)(p.R * (2 / PSW)), chunks);
-        hipLaunchKernelGGL((k_fwd_fp8<32, NW, U, PSW>), grid, dim3(NW * 64), 0, st, X, p.K, (int)M, V8, se, bias, Y, p.N,
-                           p.dev.col_idx, p.dev.small_m_rows);
-    } else {
-        constexpr int NW = 8, U = 4, PSW = 2;
-        const dim3 grid((unsigned)(p.R * (4 / PSW)), chunks);
-        hipLaunchKernelGGL((k_fwd_fp8<64, NW, U, PSW>), grid, dim3(NW * 64), 0, st, X, p.K, (int)M, V8, se, bias, Y, p.N,
-                           p.dev.col_idx, p.dev.small_m_rows);
+        launch_fwd_fp8_cfg<32, 8, 8, 2>(p, X, M, V8, se, bias, Y, st);
+        return launched("fwd_fp8 launch");
+    }
+    int cfg = 0;
+    if (const char *f = std::getenv("BSR_FP8_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 7
+    switch (cfg) {
+        case 1: launch_fwd_fp8_cfg<64, 8, 4, 1>(p, X, M, V8, se, bias, Y, st); break;
+        case 2: launch_fwd_fp8_cfg<64, 8, 2, 1>(p, X, M, V8, se, bias, Y, st); break;
+        case 3: launch_fwd_fp8_cfg<64, 8, 8, 2>(p, X, M, V8, se, bias, Y, st); break;
+        case 4: launch_fwd_fp8_cfg<64, 4, 4, 1>(p, X, M, V8, se, bias, Y, st); break;
+        case 5: launch_fwd_fp8_cfg<64, 16, 2, 1>(p, X, M, V8, se, bias, Y, st); break;
+        case 6: launch_fwd_fp8_cfg<64, 16, 4, 2>(p, X, M, V8, se, bias, Y, st); break;
+        case 7: launch_fwd_fp8_cfg<64, 4, 8, 1>(p, X, M, V8, se, bias, Y, st); break;
+        default: launch_fwd_fp8_cfg<64, 8, 4, 2>(p, X, M, V8, se, bias, Y, st); break;
     }
     return launched("fwd_fp8 launch");
 }
