@@ -11,7 +11,8 @@ Parts:
   meta.py   CSR / CSC / perm metadata by direct scan of the block mask;
   brute.py  exact Fraction brute force over the dense zero-filled weight;
   oracle.c  also: fp8 (OCP E4M3) block values with a power-of-two scale per
-            block (quantise, dequantise);
+            block (quantise, dequantise); 2:4 sparsity inside each kept
+            block (compress by magnitude, decompress);
   convert.py dense <-> BSR conversion and block-magnitude pattern selection
             (block norms from oracle.c, top-k by a plain sort, gather and
             scatter of blocks by plain loops).
@@ -62,10 +63,12 @@ def lib():
         L.oracle_block_norms.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_quantize_fp8.argtypes = [i32, i32, P, P, P]
         L.oracle_dequantize_fp8.argtypes = [i32, i32, P, P, P]
+        L.oracle_compress_24.argtypes = [i32, i32, P, P, P]
+        L.oracle_decompress_24.argtypes = [i32, i32, P, P, P]
         L.oracle_e4m3_value.argtypes, L.oracle_e4m3_value.restype = [ctypes.c_uint8], ctypes.c_double
         L.oracle_e4m3_encode.argtypes, L.oracle_e4m3_encode.restype = [ctypes.c_double], ctypes.c_uint8
         for f in (L.oracle_fwd, L.oracle_dx, L.oracle_dw, L.oracle_db, L.oracle_block_norms, L.oracle_quantize_fp8,
-                  L.oracle_dequantize_fp8):
+                  L.oracle_dequantize_fp8, L.oracle_compress_24, L.oracle_decompress_24):
             f.restype = None
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -172,6 +175,27 @@ def dequantize_fp8(codes, se) -> np.ndarray:
     nnzb, b, _ = codes.shape
     out = np.empty((nnzb, b, b), dtype=np.float64)
     lib().oracle_dequantize_fp8(nnzb, b, _p(codes), _p(se), _p(out))
+    return out
+
+
+def compress_24(V):
+    """(Vc fp64 [nnzb, b, b/2], meta uint16 [nnzb, b, b/16]): the two largest magnitudes of every
+    group of 4 columns of every block row (ties to the lower position), see oracle.c."""
+    V = _f64(V)
+    nnzb, b, _ = V.shape
+    Vc = np.empty((nnzb, b, b // 2), dtype=np.float64)
+    meta_ = np.empty((nnzb, b, b // 16), dtype=np.uint16)
+    lib().oracle_compress_24(nnzb, b, _p(V), _p(Vc), _p(meta_))
+    return Vc, meta_
+
+
+def decompress_24(Vc, meta_) -> np.ndarray:
+    """fp64 [nnzb, b, b] dense blocks from the compressed form."""
+    Vc = _f64(Vc)
+    meta_ = np.ascontiguousarray(meta_, dtype=np.uint16)
+    nnzb, b, _ = Vc.shape
+    out = np.empty((nnzb, b, b), dtype=np.float64)
+    lib().oracle_decompress_24(nnzb, b, _p(Vc), _p(meta_), _p(out))
     return out
 
 

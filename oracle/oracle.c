@@ -265,6 +265,68 @@ void oracle_dequantize_fp8(int32_t nnzb, int32_t b, const uint8_t *codes, const 
             V[(int64_t)i * b * b + k] = ldexp(oracle_e4m3_value(codes[(int64_t)i * b * b + k]), se[i]);
 }
 
+/* ---- 2:4 sparsity inside each kept block ----
+ * (pytorch_block_sparse summary page, "Future Development Roadmap": the 50% sparse pattern within
+ * blocks; pytorch/ao sparsity README: 2:4 semi-structured means two of every four elements are
+ * zero, pruned by weight norm over 1 x 4 groups with two zeros per group, stored as a half-size
+ * compressed dense matrix plus 2-bit indices (Table 4.1).)
+ *
+ * Groups are 4 consecutive columns q = 4h .. 4h+3 of one row p of a block (the input dimension,
+ * which the forward sums over). In each group the two elements of largest magnitude are kept
+ * (ties to the lower position); they are stored in ascending position order:
+ *   Vc[i][p][2h + t]   the t-th kept value of group h (t = 0, 1),
+ *   meta[i][p][h / 4]  16 bits per 4 groups: group h at bits 4 (h % 4): the first kept position
+ *                      in the low 2 bits, the second in the next 2.
+ * V is [nnzb][b][b], Vc [nnzb][b][b/2], meta [nnzb][b][b/16]; b a multiple of 16. */
+void oracle_compress_24(int32_t nnzb, int32_t b, const double *V, double *Vc, uint16_t *meta)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t i = 0; i < nnzb; ++i) {
+        for (int32_t p = 0; p < b; ++p) {
+            const double *v = V + ((int64_t)i * b + p) * b;
+            double *vc = Vc + ((int64_t)i * b + p) * (b / 2);
+            uint16_t *mt = meta + ((int64_t)i * b + p) * (b / 16);
+            for (int32_t w = 0; w < b / 16; ++w) mt[w] = 0;
+            for (int32_t h = 0; h < b / 4; ++h) {
+                const double *g = v + 4 * h;
+                /* first: largest magnitude, lowest position among equals */
+                int first = 0;
+                for (int k = 1; k < 4; ++k)
+                    if (fabs(g[k]) > fabs(g[first])) first = k;
+                /* second: largest magnitude among the other three, lowest position among equals */
+                int second = -1;
+                for (int k = 0; k < 4; ++k) {
+                    if (k == first) continue;
+                    if (second < 0 || fabs(g[k]) > fabs(g[second])) second = k;
+                }
+                const int lo = first < second ? first : second, hi = first < second ? second : first;
+                vc[2 * h] = g[lo];
+                vc[2 * h + 1] = g[hi];
+                mt[h / 4] |= (uint16_t)((lo | (hi << 2)) << (4 * (h % 4)));
+            }
+        }
+    }
+}
+
+/* Dense blocks from the compressed form: zeros except the two kept positions of every group. */
+void oracle_decompress_24(int32_t nnzb, int32_t b, const double *Vc, const uint16_t *meta, double *V)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t i = 0; i < nnzb; ++i) {
+        for (int32_t p = 0; p < b; ++p) {
+            const double *vc = Vc + ((int64_t)i * b + p) * (b / 2);
+            const uint16_t *mt = meta + ((int64_t)i * b + p) * (b / 16);
+            double *v = V + ((int64_t)i * b + p) * b;
+            for (int32_t q = 0; q < b; ++q) v[q] = 0.0;
+            for (int32_t h = 0; h < b / 4; ++h) {
+                const int bits = (mt[h / 4] >> (4 * (h % 4))) & 15;
+                v[4 * h + (bits & 3)] = vc[2 * h];
+                v[4 * h + (bits >> 2)] = vc[2 * h + 1];
+            }
+        }
+    }
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_max_threads(void)
 {
