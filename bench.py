@@ -438,6 +438,35 @@ def fp8_leg(dev, reps: int) -> dict:
     return out
 
 
+def sparse24_leg(dev, reps: int) -> dict:
+    """The decode forward with 2:4 sparsity inside every kept block (bsr_linear_fwd_24, sparse
+    matrix cores) on the decode workload's pattern, its blocks pruned to 2:4, cold (rotated value
+    sets); algorithmic bytes: compressed values + indices + activations + CSR."""
+    import torch
+    from sparse_gemm_amd import binding, synth
+    w = synth.WORKLOADS[FP8_WORKLOAD]
+    host = synth.make_inputs(w, 0)
+    p = binding.Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    nnzb, R = p.nnzb, w.R
+    X = host["X"].to(dev)
+    Y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    c0 = binding.values_compress_24(p, host["V"].to(dev))
+    vc_bytes = nnzb * w.b * w.b
+    meta_bytes = nnzb * w.b * (w.b // 16) * 2
+    nsets = max(1, -(-ROTATE_BYTES // (vc_bytes + meta_bytes)))
+    cs = [c0] + [(a.clone(), m.clone()) for a, m in [c0] * (nsets - 1)]
+    by = vc_bytes + meta_bytes + 2 * w.M * w.K + 2 * w.M * w.N + 4 * (R + 1) + 4 * nnzb
+    ms = time_launches(lambda k: binding.linear_fwd_24(p, X, cs[k % nsets][0], cs[k % nsets][1], out=Y), nsets, reps)
+    F_kept = 2.0 * w.M * (w.b * w.b // 2) * nnzb
+    out = {"workload": w.name + " (blocks pruned to 2:4)", "buffers": f"cold ({nsets} rotated sets)",
+           "fwd_24": {"us": ms * 1e3, "bytes": by, "gbs": by / (ms * 1e-3) / 1e9,
+                      "pct_hbm_peak": 100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "tflops_on_kept_values": F_kept / (ms * 1e-3) / 1e12}}
+    del cs
+    p.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -583,6 +612,10 @@ def main():
         out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
         log("[bench] fp8 block values, decode forward")
         out["next_rows"]["fp8_decode"] = fp8_leg(dev, max(50, args.steps))
+        log("[bench] 2:4 inside blocks, decode forward")
+        out["next_rows"]["sparse24_decode"] = sparse24_leg(dev, max(50, args.steps))
+        out["next_rows"]["sparse24_decode"]["speedup_vs_bf16_dense_blocks"] = (
+            out["next_rows"]["fp8_decode"]["fwd_bf16"]["us"] / out["next_rows"]["sparse24_decode"]["fwd_24"]["us"])
 
     if args.calibrate_copy:
         src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev)

@@ -1,0 +1,58 @@
+/*
+ * bsr_sparse24.h -- 2:4 sparsity inside each kept block (C ABI, same library and conventions as
+ * bsr_linear.h: raw bf16 bits, caller-owned contiguous device buffers aligned to 16 bytes, a
+ * hipStream_t passed as void*, arguments checked before anything is enqueued, a bsr_status
+ * returned, no C++ exception across the interface).
+ *
+ * The block-sparse layer's roadmap adds the 50% sparse pattern inside blocks (pytorch_block_sparse
+ * summary page, "Future Development Roadmap"). 2:4 semi-structured sparsity keeps two of every
+ * four consecutive elements; the pytorch/ao sparsity README prunes it by weight norm over 1 x 4
+ * groups with two zeros per group (workflow example) and stores it as a half-size compressed
+ * matrix plus 2-bit indices (Table 4.1). Here the groups run along a block row's columns (the
+ * layer's input dimension, which the forward sums over), so the gfx950 sparse matrix cores can
+ * take the compressed block directly.
+ *
+ * Format of kept block i (CSR order, like V); b = 32 or 64:
+ *   Vc[i][p][2h + t]   bf16    the t-th kept value (ascending position) of group h = columns
+ *                              4h .. 4h + 3 of row p; [nnzb][b][b/2]
+ *   meta[i][p][h / 4]  uint16  group h at bits 4 (h % 4): the first kept position (0..3) in the
+ *                              low 2 bits, the second in the next 2; [nnzb][b][b/16]
+ * Compression keeps the two elements of largest magnitude of every group, ties to the lower
+ * position (for a block that already has at most two nonzeros per group it is lossless).
+ */
+#ifndef BSR_SPARSE24_H
+#define BSR_SPARSE24_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsr_linear.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Prune bf16 block values V [nnzb][b][b] (device, finite) to 2:4 inside every block row and
+ * compress: Vc [nnzb][b][b/2] bf16 and meta [nnzb][b][b/16] uint16 (device). Bit-exact
+ * (integer magnitude comparisons). Outputs must not overlap V. */
+int32_t bsr_values_compress_24(const bsr_pattern *p, const bsr_bf16 *V, bsr_bf16 *Vc, uint16_t *meta,
+                               void *stream);
+
+/* Dense blocks V [nnzb][b][b] from the compressed form: the kept values at their positions, +0.0
+ * elsewhere. */
+int32_t bsr_values_decompress_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint16_t *meta,
+                                 bsr_bf16 *V, void *stream);
+
+/* Forward with 2:4 block values on the sparse matrix cores: Y[M][N] = X[M][K] . W24~^T + bias,
+ * W24~ being the zero-filled weight of the decompressed blocks (the contract of bsr_linear_fwd;
+ * bf16 inputs and outputs, fp32 accumulation, one rounding per output). Built for few activation
+ * rows (decode; 16 rows per pass; M below 2^20). Every element of Y is written. Limits: the
+ * compressed values below 4 GiB; Y must not overlap the inputs. */
+int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *Vc,
+                          const uint16_t *meta, const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSR_SPARSE24_H */

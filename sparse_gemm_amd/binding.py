@@ -307,3 +307,48 @@ def _check_raw(t: torch.Tensor, name: str, shape, dtype, device) -> None:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+# ---- 2:4 sparsity inside each kept block (include/bsr_sparse24.h) ----
+
+def values_compress_24(p: Pattern, V: torch.Tensor, out=None):
+    """(Vc bf16 [nnzb, b, b/2], meta uint16-as-int16 [nnzb, b, b/16]) via bsr_values_compress_24."""
+    _check_tensor(V, "V", (p.nnzb, p.b, p.b), p.device)
+    if out is None:
+        out = (torch.empty((p.nnzb, p.b, p.b // 2), dtype=torch.bfloat16, device=V.device),
+               torch.empty((p.nnzb, p.b, p.b // 16), dtype=torch.int16, device=V.device))
+    Vc, mt = out
+    _check_tensor(Vc, "Vc", (p.nnzb, p.b, p.b // 2), p.device)
+    _check_raw(mt, "meta", (p.nnzb, p.b, p.b // 16), torch.int16, p.device)
+    _lib.check(lib().bsr_values_compress_24(p.handle, _ptr(V), _ptr(Vc), _ptr(mt), _stream(p.device)),
+               "bsr_values_compress_24")
+    return Vc, mt
+
+
+def values_decompress_24(p: Pattern, Vc: torch.Tensor, mt: torch.Tensor, out=None) -> torch.Tensor:
+    """Dense bf16 blocks [nnzb, b, b] via bsr_values_decompress_24."""
+    _check_tensor(Vc, "Vc", (p.nnzb, p.b, p.b // 2), p.device)
+    _check_raw(mt, "meta", (p.nnzb, p.b, p.b // 16), torch.int16, p.device)
+    if out is None:
+        out = torch.empty((p.nnzb, p.b, p.b), dtype=torch.bfloat16, device=Vc.device)
+    _check_tensor(out, "out", (p.nnzb, p.b, p.b), p.device)
+    _lib.check(lib().bsr_values_decompress_24(p.handle, _ptr(Vc), _ptr(mt), _ptr(out), _stream(p.device)),
+               "bsr_values_decompress_24")
+    return out
+
+
+def linear_fwd_24(p: Pattern, X: torch.Tensor, Vc: torch.Tensor, mt: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W24~^T + bias with 2:4-compressed block values, via bsr_linear_fwd_24."""
+    M = X.shape[0]
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_tensor(Vc, "Vc", (p.nnzb, p.b, p.b // 2), p.device)
+    _check_raw(mt, "meta", (p.nnzb, p.b, p.b // 16), torch.int16, p.device)
+    if bias is not None:
+        _check_tensor(bias, "bias", (p.N,), p.device)
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, p.N), p.device)
+    _lib.check(lib().bsr_linear_fwd_24(p.handle, _ptr(X), M, _ptr(Vc), _ptr(mt), _ptr(bias), _ptr(out),
+                                       _stream(p.device)), "bsr_linear_fwd_24")
+    return out

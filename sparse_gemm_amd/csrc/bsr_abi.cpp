@@ -10,6 +10,7 @@
 
 #include "bsr_convert_internal.hpp"
 #include "bsr_fp8_internal.hpp"
+#include "bsr_sparse24_internal.hpp"
 
 namespace bsr {
 
@@ -391,6 +392,45 @@ int32_t bsr_linear_fwd_fp8(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, c
     if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     if (M == 0) return BSR_OK;
     return launch_fwd_fp8(*p, X, M, V8, se, bias, Y, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_values_compress_24(const bsr_pattern *p, const bsr_bf16 *V, bsr_bf16 *Vc, uint16_t *meta, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    BSR_CHECK(check_ptr(Vc, "Vc", p->nnzb == 0));
+    BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
+    return launch_compress_24(*p, V, Vc, meta, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_values_decompress_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint16_t *meta, bsr_bf16 *V,
+                                 void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(Vc, "Vc", p->nnzb == 0));
+    BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
+    BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
+    return launch_decompress_24(*p, Vc, meta, V, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *Vc, const uint16_t *meta,
+                          const bsr_bf16 *bias, bsr_bf16 *Y, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(Vc, "Vc", p->nnzb == 0));
+    BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
+    if ((size_t)p->nnzb * p->b * p->b >= (size_t)0xFFFFFFF0u)
+        return fail(BSR_ERR_INVALID_ARG, "compressed block values above 4 GiB");
+    if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
+    if (M == 0) return BSR_OK;
+    return launch_fwd_24(*p, X, M, Vc, meta, bias, Y, stream);
     BSR_TRY_END
 }
 

@@ -1,0 +1,126 @@
+"""GPU parity of 2:4 sparsity inside kept blocks through the C ABI against the oracle: compression
+(values and index bits) and decompression are bit-exact; the forward on the sparse matrix cores
+meets the layer's tolerance rule |g - ref| <= 4e-3 * S against the oracle's fp64 forward on the
+oracle's decompressed blocks (exact where S = 0), and is bit-exact on integer inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import meta
+from sparse_gemm_amd import binding, synth
+from sparse_gemm_amd.binding import Pattern
+
+from gpu_util import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _values(nnzb, b, seed):
+    """N(0, 0.02) blocks with planted ties: equal magnitudes, zeros, negative zeros."""
+    V = synth.block_values(nnzb, b, seed)
+    if nnzb > 4:
+        V[0, 0, :8] = torch.tensor([1, -1, 1, -1, 0, 0, 0, 0], dtype=torch.bfloat16)
+        V[1, 2, 4:8] = torch.tensor([-0.0, 0.0, -0.0, 0.0], dtype=torch.bfloat16)
+        V[2, 3, :4] = torch.tensor([0.5, 0.25, 0.5, -0.5], dtype=torch.bfloat16)
+        V[3] = 0
+    return V
+
+
+@pytest.mark.parametrize("N,K,b,d,seed", [(256, 256, 32, 0.5, 0), (384, 640, 64, 0.4, 1), (14336, 4096, 64, 0.5, 2),
+                                          (3072, 768, 32, 0.25, 3)])
+def test_compress_decompress_bit_exact(N, K, b, d, seed):
+    say(f"case 2:4 compress N={N} K={K} b={b} d={d}")
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    D = binding.values_decompress_24(p, Vc, mt)
+    torch.cuda.synchronize()
+    Vc_ref, mt_ref = oracle.compress_24(V)
+    assert np.array_equal(mt.cpu().numpy().view(np.uint16), mt_ref)
+    assert np.array_equal(Vc.cpu().view(torch.int16).numpy(),
+                          torch.from_numpy(Vc_ref).to(torch.bfloat16).view(torch.int16).numpy())
+    D_ref = torch.from_numpy(oracle.decompress_24(Vc_ref, mt_ref)).to(torch.bfloat16)
+    assert np.array_equal(D.cpu().view(torch.int16).numpy(), D_ref.view(torch.int16).numpy())
+    p.close()
+
+
+@pytest.mark.parametrize("M,N,K,b,d,seed,bias", [
+    (1, 256, 256, 32, 0.5, 10, True), (5, 512, 384, 64, 0.4, 11, False), (8, 1024, 512, 32, 0.3, 12, True),
+    (16, 768, 512, 64, 0.5, 13, True), (17, 512, 256, 32, 0.6, 14, False), (40, 256, 512, 64, 0.5, 15, True),
+    (8, 512, 512, 32, 0.02, 16, True), (3, 320, 224, 32, 0.45, 17, True)])
+def test_fwd_24_matches_oracle(M, N, K, b, d, seed, bias):
+    say(f"case 2:4 fwd M={M} N={N} K={K} b={b} d={d} bias={bias}")
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    X = synth.activations(M, K, seed)
+    bb = synth.bias_vector(N, seed) if bias else None
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_24(p, X.to(dev()), Vc, mt, None if bb is None else bb.to(dev()), out=Y)
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, S = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, bias=bb)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    2:4 fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+def test_fwd_24_decode_workload_full():
+    """The decode workload at full size (X[8,4096], W[14336,4096], 64 x 64 blocks, density 0.5),
+    its blocks pruned to 2:4; every output element checked."""
+    w = synth.WORKLOADS[4]
+    say(f"case 2:4 fwd {w.name}")
+    host = synth.make_inputs(w, 0)
+    md = meta.scan(host["mask"])
+    p = Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    Vc, mt = binding.values_compress_24(p, host["V"].to(dev()))
+    Y = binding.linear_fwd_24(p, host["X"].to(dev()), Vc, mt)
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(host["V"]))
+    ref, S = oracle.fwd(host["X"], md["row_ptr"], md["col_idx"], D, w.N, w.b)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    2:4 fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_fwd_24_integer_inputs_bit_exact(b):
+    """Integers in {-1, 0, 1}: products and fp32 sums are exact and |y| <= 256, so the output
+    equals the oracle exactly."""
+    M, N, K = 12, 256, 512
+    g = np.random.default_rng(20 + b)
+    mask = synth.uniform_mask(N // b, K // b, 0.5, g)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    X = torch.from_numpy(g.integers(-1, 2, size=(M, K)).astype(np.float32)).to(torch.bfloat16)
+    V = torch.from_numpy(g.integers(-1, 2, size=(p.nnzb, b, b)).astype(np.float32)).to(torch.bfloat16)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Y = binding.linear_fwd_24(p, X.to(dev()), Vc, mt)
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, _ = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, want_s=False)
+    assert np.array_equal(Y.cpu().double().numpy(), ref)
+    p.close()
+
+
+def test_fwd_24_argument_errors():
+    mask = np.ones((2, 2), dtype=np.uint8)
+    p = Pattern.from_mask(mask, 64, 64, 32)
+    X = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev())
+    Vc = torch.zeros((4, 32, 16), dtype=torch.bfloat16, device=dev())
+    mt = torch.zeros((4, 32, 2), dtype=torch.int16, device=dev())
+    Y = torch.empty((4, 64), dtype=torch.bfloat16, device=dev())
+    L = binding.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.bsr_linear_fwd_24(p.handle, X.data_ptr(), 4, Vc.data_ptr(), None, None, Y.data_ptr(), st) == 1
+    assert L.bsr_linear_fwd_24(p.handle, X.data_ptr(), 4, Vc.data_ptr() + 2, mt.data_ptr(), None, Y.data_ptr(),
+                               st) == 3
+    assert L.bsr_linear_fwd_24(p.handle, X.data_ptr(), 1 << 20, Vc.data_ptr(), mt.data_ptr(), None, Y.data_ptr(),
+                               st) == 1
+    p.close()
