@@ -38,7 +38,7 @@ enum bsr_norm_kind {
 
 /* Block magnitudes of a dense weight.
  *   N, K   weight shape (out, in), positive multiples of b; b = 32 or 64
- *          (BSR_ERR_UNSUPPORTED otherwise); N/b below 2^31 / 8 blocks in all.
+ *          (BSR_ERR_UNSUPPORTED otherwise); N/b below 65536.
  *   W      device [N][K] bf16.
  *   kind   BSR_NORM_L1 or BSR_NORM_L2_SQUARED.
  *   norms  device [N/b][K/b] fp64 output, row-major over the block grid:

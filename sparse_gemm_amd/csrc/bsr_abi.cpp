@@ -291,7 +291,7 @@ int32_t bsr_block_norms(int32_t N, int32_t K, int32_t b, const bsr_bf16 *W, int3
     BSR_TRY_BEGIN
     BSR_CHECK(check_shape(N, K, b));
     if (kind != BSR_NORM_L1 && kind != BSR_NORM_L2_SQUARED) return fail(BSR_ERR_INVALID_ARG, "unknown norm kind");
-    if ((int64_t)(N / b) * (K / b) > (int64_t)INT32_MAX / 8) return fail(BSR_ERR_INVALID_ARG, "too many blocks");
+    if (N / b >= 65536) return fail(BSR_ERR_INVALID_ARG, "N/b must be below 65536");
     BSR_CHECK(check_ptr(W, "W"));
     BSR_CHECK(check_ptr(norms, "norms"));
     return launch_block_norms(N, K, b, W, kind, norms, stream);

@@ -9,10 +9,10 @@
 //
 // All three kernels are pure streams over HBM (each input byte read once, each output byte
 // written once), so they are shaped for coalescing, not for the matrix cores:
-//   k_block_norms     one thread per (block, row of the block): that row's 2b bytes as 16-byte
-//                     loads, summed left to right in fp64; the block's row sums are then added
-//                     in row order by one thread. Adjacent threads take adjacent blocks of the
-//                     same weight row, so a wave reads whole contiguous row segments.
+//   k_block_norms     one work-group per (block row, 256-column strip): the strip is read in
+//                     whole 512-byte row segments into LDS, one thread then sums one row of one
+//                     block left to right in fp64, and the block's row sums are added in row
+//                     order by one thread.
 //   k_dense_to_values a fixed number of kept blocks per work-group; each 16-byte piece of a
 //                     block is one load from the dense weight and one store into V.
 //   k_values_to_dense one work-group per (block row, 256-column strip): the strip's kept
@@ -36,29 +36,46 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)
 // t = |w| (KIND 1) or w*w (KIND 2), each sum left to right in fp64 from 0. The terms are exact in
 // fp64 (a bf16 magnitude; a product of two 8-bit significands), and the order is fixed, so the
 // result does not depend on the launch shape.
+// Work-group = one block row x a strip of kNormCols columns (T = kNormCols / BS blocks). The strip
+// is read with whole 512-byte row segments per 32 lanes (each byte once) into LDS; then thread
+// (block j, row p) sums its row of block j from LDS, and T threads add the row sums in row order.
+constexpr int kNormCols = 256;
+constexpr int kNormLd = kNormCols + 8;   // LDS row stride in bf16: 16 bytes of padding per row
+
 template <int BS, int KIND>
-__global__ __launch_bounds__(256) void k_block_norms(const uint16_t *__restrict__ W, int K, int C, int64_t nblocks,
+__global__ __launch_bounds__(256) void k_block_norms(const uint16_t *__restrict__ W, int K, int C,
                                                      double *__restrict__ norms) {
-    constexpr int T = 256 / BS;  // blocks per work-group
+    constexpr int T = kNormCols / BS;             // blocks per strip (8 or 4); T * BS = 256 threads
+    __shared__ __attribute__((aligned(16))) uint16_t tile[BS][kNormLd];
     __shared__ double rows[BS][T];
     const int t = threadIdx.x;
-    const int tl = t % T, p = t / T;
-    const int64_t blk = (int64_t)blockIdx.x * T + tl;
-    if (blk < nblocks) {
-        const int64_t r = blk / C, c = blk % C;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(W + (r * BS + p) * (int64_t)K + c * BS);
-        u32x4 v[BS / 8];
+    const int r = blockIdx.y, c0 = blockIdx.x * T;
+    const int ncols = min(kNormCols, (C - c0) * BS);   // columns of this strip inside W
+    // phase 1: rows of the strip, 32 lanes x 16 bytes per row, 8 rows per pass
+    const int seg = t & 31, prow = t >> 5;
 #pragma unroll
-        for (int j = 0; j < BS / 8; ++j) v[j] = __builtin_nontemporal_load(src + j);
+    for (int k = 0; k < BS / 8; ++k) {
+        const int p = k * 8 + prow;
+        if (seg * 8 < ncols) {
+            const u32x4 v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(W + ((int64_t)r * BS + p) * K + (int64_t)c0 * BS + seg * 8));
+            *reinterpret_cast<u32x4 *>(&tile[p][seg * 8]) = v;
+        }
+    }
+    __syncthreads();
+    // phase 2: thread (j, p) sums row p of block j left to right
+    const int j = t % T, p = t / T;
+    if (c0 + j < C) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(&tile[p][j * BS]);
         double acc = 0.0;
 #pragma unroll
-        for (int j = 0; j < BS / 8; ++j) {
-            const uint32_t w4[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+        for (int q8 = 0; q8 < BS / 8; ++q8) {
+            const u32x4 v = src[q8];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const double x = bf16_to_f64(e == 0 ? (w4[h] & 0xffffu) : (w4[h] >> 16));
+                    const double x = bf16_to_f64(e == 0 ? (v[h] & 0xffffu) : (v[h] >> 16));
                     if (KIND == 1)
                         acc += fabs(x);
                     else
@@ -66,17 +83,14 @@ __global__ __launch_bounds__(256) void k_block_norms(const uint16_t *__restrict_
                 }
             }
         }
-        rows[p][tl] = acc;
+        rows[p][j] = acc;
     }
     __syncthreads();
-    if (t < T) {
-        const int64_t b2 = (int64_t)blockIdx.x * T + t;
-        if (b2 < nblocks) {
-            double acc = 0.0;
+    if (t < T && c0 + t < C) {
+        double acc = 0.0;
 #pragma unroll 8
-            for (int q = 0; q < BS; ++q) acc += rows[q][t];
-            norms[b2] = acc;
-        }
+        for (int q = 0; q < BS; ++q) acc += rows[q][t];
+        norms[(int64_t)r * C + c0 + t] = acc;
     }
 }
 
@@ -181,21 +195,20 @@ int32_t after_launch(const char *what) {
 int32_t launch_block_norms(int32_t N, int32_t K, int32_t b, const uint16_t *W, int32_t kind, double *norms,
                            void *stream) {
     const int32_t R = N / b, C = K / b;
-    const int64_t nblocks = (int64_t)R * C;
-    if (nblocks == 0) return BSR_OK;
-    const int T = 256 / b;
-    const dim3 grid((unsigned)((nblocks + T - 1) / T));
+    if ((int64_t)R * C == 0) return BSR_OK;
+    const int T = kNormCols / b;
+    const dim3 grid((unsigned)((C + T - 1) / T), (unsigned)R);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (b == 32) {
         if (kind == 1)
-            hipLaunchKernelGGL((k_block_norms<32, 1>), grid, dim3(256), 0, st, W, K, C, nblocks, norms);
+            hipLaunchKernelGGL((k_block_norms<32, 1>), grid, dim3(256), 0, st, W, K, C, norms);
         else
-            hipLaunchKernelGGL((k_block_norms<32, 2>), grid, dim3(256), 0, st, W, K, C, nblocks, norms);
+            hipLaunchKernelGGL((k_block_norms<32, 2>), grid, dim3(256), 0, st, W, K, C, norms);
     } else {
         if (kind == 1)
-            hipLaunchKernelGGL((k_block_norms<64, 1>), grid, dim3(256), 0, st, W, K, C, nblocks, norms);
+            hipLaunchKernelGGL((k_block_norms<64, 1>), grid, dim3(256), 0, st, W, K, C, norms);
         else
-            hipLaunchKernelGGL((k_block_norms<64, 2>), grid, dim3(256), 0, st, W, K, C, nblocks, norms);
+            hipLaunchKernelGGL((k_block_norms<64, 2>), grid, dim3(256), 0, st, W, K, C, norms);
     }
     return after_launch("k_block_norms");
 }
