@@ -467,6 +467,27 @@ def sparse24_leg(dev, reps: int) -> dict:
     return out
 
 
+def rebuild_leg(dev, reps: int) -> dict:
+    """The on-device metadata rebuild (bsr_meta_rebuild: six small kernels) on the Zipf workload's
+    block mask (344 x 128)."""
+    import torch
+    from sparse_gemm_amd import binding, synth
+    w = synth.WORKLOADS[CONVERT_WORKLOAD]
+    mask = torch.from_numpy(synth.block_mask(w, 0)).to(dev)
+    out = binding.meta_rebuild(mask)
+    R, C = mask.shape
+    ws = out["_workspace"]
+    L = binding.lib()
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    def run(k):
+        L.bsr_meta_rebuild(R, C, mask.data_ptr(), out["row_ptr"].data_ptr(), out["col_idx"].data_ptr(),
+                           out["col_ptr"].data_ptr(), out["row_idx"].data_ptr(), out["perm"].data_ptr(), R * C,
+                           out["nnzb"].data_ptr(), ws.data_ptr(), ws.numel(), st)
+    ms = time_launches(run, 1, reps)
+    return {"grid": f"{R}x{C}", "nnzb": int(out["nnzb"].item()), "us_per_rebuild": ms * 1e3, "kernels": 6}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -612,6 +633,8 @@ def main():
         out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
         log("[bench] fp8 block values, decode forward")
         out["next_rows"]["fp8_decode"] = fp8_leg(dev, max(50, args.steps))
+        log("[bench] on-device metadata rebuild")
+        out["next_rows"]["meta_rebuild"] = rebuild_leg(dev, max(50, args.steps))
         log("[bench] 2:4 inside blocks, decode forward")
         out["next_rows"]["sparse24_decode"] = sparse24_leg(dev, max(50, args.steps))
         out["next_rows"]["sparse24_decode"]["speedup_vs_bf16_dense_blocks"] = (

@@ -1,4 +1,4 @@
-"""ctypes binding of libbsr_linear.so (the C ABI in include/bsr_linear.h, bsr_convert.h, bsr_fp8.h and bsr_sparse24.h).
+"""ctypes binding of libbsr_linear.so (the C ABI in include/*.h).
 
 Argument marshalling only: every step of the computation runs in the library's HIP
 kernels. There is no CPU fallback; if the library is missing, loading fails loudly.
@@ -26,7 +26,9 @@ EXPORTS = ("bsr_abi_version", "bsr_pattern_create_from_mask", "bsr_pattern_creat
            # include/bsr_fp8.h
            "bsr_values_quantize_fp8", "bsr_values_dequantize_fp8", "bsr_linear_fwd_fp8",
            # include/bsr_sparse24.h
-           "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24")
+           "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24",
+           # include/bsr_rebuild.h
+           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild")
 
 
 class BsrError(RuntimeError):
@@ -70,6 +72,8 @@ def load() -> ctypes.CDLL:
     L.bsr_values_compress_24.argtypes = [P, P, P, P, P]
     L.bsr_values_decompress_24.argtypes = [P, P, P, P, P]
     L.bsr_linear_fwd_24.argtypes = [P, P, i64, P, P, P, P, P]
+    L.bsr_meta_rebuild_workspace.argtypes, L.bsr_meta_rebuild_workspace.restype = [i32, i32], sz
+    L.bsr_meta_rebuild.argtypes = [i32, i32, P, P, P, P, P, P, i32, P, P, sz, P]
     for f in ("bsr_pattern_create_from_mask", "bsr_pattern_create_from_csr", "bsr_pattern_info",
               "bsr_pattern_export", "bsr_linear_fwd", "bsr_linear_bwd_input", "bsr_linear_bwd_weight",
               "bsr_block_norms", "bsr_mask_topk", "bsr_pattern_create_from_dense", "bsr_dense_to_values",
@@ -77,7 +81,9 @@ def load() -> ctypes.CDLL:
            # include/bsr_fp8.h
            "bsr_values_quantize_fp8", "bsr_values_dequantize_fp8", "bsr_linear_fwd_fp8",
            # include/bsr_sparse24.h
-           "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24"):
+           "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24",
+           # include/bsr_rebuild.h
+           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild"):
         getattr(L, f).restype = i32
     L.bsr_status_string.argtypes, L.bsr_status_string.restype = [i32], ctypes.c_char_p
     L.bsr_last_error.argtypes, L.bsr_last_error.restype = [], ctypes.c_char_p

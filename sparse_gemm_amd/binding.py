@@ -352,3 +352,28 @@ def linear_fwd_24(p: Pattern, X: torch.Tensor, Vc: torch.Tensor, mt: torch.Tenso
     _lib.check(lib().bsr_linear_fwd_24(p.handle, _ptr(X), M, _ptr(Vc), _ptr(mt), _ptr(bias), _ptr(out),
                                        _stream(p.device)), "bsr_linear_fwd_24")
     return out
+
+
+# ---- on-device metadata rebuild (include/bsr_rebuild.h) ----
+
+def meta_rebuild(mask: torch.Tensor, cap: Optional[int] = None) -> dict:
+    """CSR / CSC / perm of a device block mask [R, C] (uint8) via bsr_meta_rebuild, asynchronous
+    on the current stream. Returns device tensors row_ptr, col_idx, col_ptr, row_idx, perm (index
+    arrays of length cap, default R*C) and nnzb (a 1-element device tensor)."""
+    if mask.dtype != torch.uint8 or mask.dim() != 2 or not mask.is_cuda or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8 [R, C] device tensor")
+    R, C = mask.shape
+    cap = R * C if cap is None else int(cap)
+    d = mask.device
+    i32 = dict(dtype=torch.int32, device=d)
+    out = dict(row_ptr=torch.empty(R + 1, **i32), col_idx=torch.empty(max(cap, 1), **i32),
+               col_ptr=torch.empty(C + 1, **i32), row_idx=torch.empty(max(cap, 1), **i32),
+               perm=torch.empty(max(cap, 1), **i32), nnzb=torch.empty(1, **i32))
+    ws_bytes = int(lib().bsr_meta_rebuild_workspace(R, C))
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=d)
+    _lib.check(lib().bsr_meta_rebuild(R, C, _ptr(mask), _ptr(out["row_ptr"]), _ptr(out["col_idx"]),
+                                      _ptr(out["col_ptr"]), _ptr(out["row_idx"]), _ptr(out["perm"]), cap,
+                                      _ptr(out["nnzb"]), _ptr(ws), ws_bytes,
+                                      torch.cuda.current_stream(d).cuda_stream), "bsr_meta_rebuild")
+    out["_workspace"] = ws   # keeps the scratch alive until the caller synchronises
+    return out

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbsr_linear.so")
 ARCH = "gfx950"
 
-SOURCES = ["bsr_abi.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip"]
+SOURCES = ["bsr_abi.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip", "bsr_rebuild.hip"]
 
 # Packed-fp32 instructions are kept out of the generated code on purpose; the host pass
 # prints a harmless "not a recognized feature" warning for this flag.

@@ -10,6 +10,7 @@
 
 #include "bsr_convert_internal.hpp"
 #include "bsr_fp8_internal.hpp"
+#include "bsr_rebuild_internal.hpp"
 #include "bsr_sparse24_internal.hpp"
 
 namespace bsr {
@@ -431,6 +432,33 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
     if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     if (M == 0) return BSR_OK;
     return launch_fwd_24(*p, X, M, Vc, meta, bias, Y, stream);
+    BSR_TRY_END
+}
+
+size_t bsr_meta_rebuild_workspace(int32_t R, int32_t C) {
+    if (R <= 0 || C <= 0) return 0;
+    return rebuild_workspace_bytes(R, C);
+}
+
+int32_t bsr_meta_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row_ptr, int32_t *col_idx,
+                         int32_t *col_ptr, int32_t *row_idx, int32_t *perm, int32_t cap, int32_t *nnzb,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    BSR_TRY_BEGIN
+    if (R <= 0 || C <= 0) return fail(BSR_ERR_INVALID_ARG, "R and C must be positive");
+    if ((int64_t)R * C >= (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "R*C must be below 2^31");
+    if (cap < 0) return fail(BSR_ERR_INVALID_ARG, "cap must be >= 0");
+    if (!mask || !row_ptr || !col_ptr || !nnzb || !workspace)
+        return fail(BSR_ERR_INVALID_ARG, "mask, row_ptr, col_ptr, nnzb and workspace must not be NULL");
+    if (cap > 0 && (!col_idx || !row_idx || !perm))
+        return fail(BSR_ERR_INVALID_ARG, "col_idx, row_idx and perm must not be NULL when cap > 0");
+    for (const void *ptr : {(const void *)row_ptr, (const void *)col_idx, (const void *)col_ptr, (const void *)row_idx,
+                            (const void *)perm, (const void *)nnzb, (const void *)workspace})
+        if ((uintptr_t)ptr & 3u) return fail(BSR_ERR_MISALIGNED, "device pointers must be 4-byte aligned");
+    const size_t need = rebuild_workspace_bytes(R, C);
+    if (ws_bytes < need)
+        return fail(BSR_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(need));
+    return launch_rebuild(R, C, mask, row_ptr, col_idx, col_ptr, row_idx, perm, cap, nnzb, workspace, stream);
     BSR_TRY_END
 }
 

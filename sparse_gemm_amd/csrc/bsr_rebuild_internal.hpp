@@ -1,0 +1,17 @@
+// bsr_rebuild_internal.hpp -- launcher of the on-device metadata rebuild (include/bsr_rebuild.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "bsr_internal.hpp"
+#include "bsr_rebuild.h"
+
+namespace bsr {
+
+size_t rebuild_workspace_bytes(int32_t R, int32_t C);
+int32_t launch_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row_ptr, int32_t *col_idx,
+                       int32_t *col_ptr, int32_t *row_idx, int32_t *perm, int32_t cap, int32_t *nnzb, void *ws,
+                       void *stream);
+
+}  // namespace bsr

@@ -1,0 +1,123 @@
+"""GPU parity of the on-device metadata rebuild (bsr_meta_rebuild) against the oracle's scan of
+the mask: row_ptr, col_idx, col_ptr, row_idx, perm and nnzb bit-exact, for uniform and Zipf masks,
+empty rows and columns, all-zero and full masks, grids wider and taller than one work-group's
+pass, a capacity below nnzb, and replays of a captured HIP graph with the mask changed between
+them."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import meta
+from sparse_gemm_amd import binding, synth
+
+from gpu_util import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(mask: np.ndarray, out: dict) -> None:
+    ref = meta.scan(mask)
+    n = ref["nnzb"]
+    assert int(out["nnzb"].item()) == n
+    assert np.array_equal(out["row_ptr"].cpu().numpy(), ref["row_ptr"])
+    assert np.array_equal(out["col_ptr"].cpu().numpy(), ref["col_ptr"])
+    for k in ("col_idx", "row_idx", "perm"):
+        assert np.array_equal(out[k].cpu().numpy()[:n], ref[k]), k
+
+
+def _masks():
+    g = np.random.default_rng(0)
+    yield "uniform 96x24 d0.25", synth.uniform_mask(96, 24, 0.25, g)
+    yield "uniform 128x128 d0.10", synth.uniform_mask(128, 128, 0.10, g)
+    yield "zipf 344x128 d0.30", synth.zipf_mask(344, 128, 0.30, 1.1, g)
+    yield "uniform 224x64 d0.5", synth.uniform_mask(224, 64, 0.5, g)
+    yield "wide 3x700 d0.3", synth.uniform_mask(3, 700, 0.3, g)
+    yield "tall 600x5 d0.4", synth.uniform_mask(600, 5, 0.4, g)
+    m = synth.uniform_mask(40, 30, 0.4, g)
+    m[7] = 0
+    m[:, 11] = 0
+    yield "empty row and column", m
+    yield "all zero", np.zeros((17, 9), dtype=np.uint8)
+    yield "full", np.ones((33, 65), dtype=np.uint8)
+    yield "1x1 kept", np.ones((1, 1), dtype=np.uint8)
+    yield "1x1 empty", np.zeros((1, 1), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("name,mask", list(_masks()), ids=[n for n, _ in _masks()])
+def test_rebuild_bit_exact(name, mask):
+    say(f"case rebuild {name}")
+    out = binding.meta_rebuild(torch.from_numpy(mask).to(dev()))
+    torch.cuda.synchronize()
+    _check(mask, out)
+
+
+def test_rebuild_capacity_below_nnzb():
+    mask = synth.uniform_mask(20, 20, 0.5, np.random.default_rng(1))
+    n = int(mask.sum())
+    cap = n // 3
+    out = binding.meta_rebuild(torch.from_numpy(mask).to(dev()), cap=cap)
+    torch.cuda.synchronize()
+    ref = meta.scan(mask)
+    assert int(out["nnzb"].item()) == n
+    assert np.array_equal(out["row_ptr"].cpu().numpy(), ref["row_ptr"])
+    assert np.array_equal(out["col_idx"].cpu().numpy()[:cap], ref["col_idx"][:cap])
+    # CSC entries below cap are exact, the rest are not written (arrays have length cap)
+    assert np.array_equal(out["row_idx"].cpu().numpy()[:cap], ref["row_idx"][:cap])
+    assert np.array_equal(out["perm"].cpu().numpy()[:cap], ref["perm"][:cap])
+
+
+def test_rebuild_feeds_a_pattern():
+    """CSR rebuilt on the device, copied to the host, gives a pattern equal to the one built from
+    the mask (and usable by the compute calls)."""
+    w = synth.WORKLOADS[2]
+    mask = synth.block_mask(w, 3)
+    out = binding.meta_rebuild(torch.from_numpy(mask).to(dev()))
+    torch.cuda.synchronize()
+    n = int(out["nnzb"].item())
+    p = binding.Pattern.from_csr(w.N, w.K, w.b, out["row_ptr"].cpu().numpy(), out["col_idx"].cpu().numpy()[:n])
+    q = binding.Pattern.from_mask(mask, w.N, w.K, w.b)
+    a, b = p.export(), q.export()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    p.close()
+    q.close()
+
+
+def test_rebuild_in_a_captured_graph_with_changing_masks():
+    R, C = 96, 48
+    g = np.random.default_rng(2)
+    masks = [synth.uniform_mask(R, C, d, g) for d in (0.2, 0.5, 0.05, 0.9)]
+    buf = torch.from_numpy(masks[0]).to(dev())
+    out = binding.meta_rebuild(buf)          # eager run: also allocates the outputs
+    torch.cuda.synchronize()
+    _check(masks[0], out)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.meta_rebuild(buf)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        gout = binding.meta_rebuild(buf)
+    for m in masks[1:] + masks[:1]:
+        buf.copy_(torch.from_numpy(m).to(dev()))   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _check(m, gout)
+        eager = binding.meta_rebuild(buf)
+        torch.cuda.synchronize()
+        _check(m, eager)
+
+
+def test_rebuild_argument_errors():
+    L = binding.lib()
+    mask = torch.zeros((4, 4), dtype=torch.uint8, device=dev())
+    i32 = torch.zeros(64, dtype=torch.int32, device=dev())
+    ws = torch.zeros(int(L.bsr_meta_rebuild_workspace(4, 4)), dtype=torch.uint8, device=dev())
+    st = torch.cuda.current_stream().cuda_stream
+    p = i32.data_ptr()
+    assert L.bsr_meta_rebuild(0, 4, mask.data_ptr(), p, p, p, p, p, 16, p, ws.data_ptr(), ws.numel(), st) == 1
+    assert L.bsr_meta_rebuild(4, 4, mask.data_ptr(), p, p, p, p, p, 16, p, ws.data_ptr(), 8, st) == 4
+    assert L.bsr_meta_rebuild(4, 4, mask.data_ptr(), p + 2, p, p, p, p, 16, p, ws.data_ptr(), ws.numel(), st) == 3
+    assert L.bsr_meta_rebuild(4, 4, None, p, p, p, p, p, 16, p, ws.data_ptr(), ws.numel(), st) == 1
