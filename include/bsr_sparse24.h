@@ -51,6 +51,20 @@ int32_t bsr_values_decompress_24(const bsr_pattern *p, const bsr_bf16 *Vc, const
 int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *Vc,
                           const uint16_t *meta, const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
 
+/* Pack the compressed form into 2:4 block images for the large-M forward: img [nnzb][b][b]
+ * (16-bit units, the size of the bf16 blocks): row p of block i holds Vc[i][p][0 .. b/2) (b
+ * bytes), then meta[i][p][0 .. b/16) (b/8 bytes), then zeros. */
+int32_t bsr_values_pack_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint16_t *meta, uint16_t *img,
+                           void *stream);
+
+/* Forward with 2:4 block images on the sparse matrix cores inside the panel GEMM of
+ * bsr_linear_fwd (same work lists, staging and epilogue; one v_smfmac_f32_32x32x32_bf16 per 32
+ * columns of a block in place of two dense products): Y[M][N] = X . W24~^T + bias, the contract of
+ * bsr_linear_fwd_24, for any M >= 0 (the same limits as bsr_linear_fwd). Y must not overlap the
+ * inputs. */
+int32_t bsr_linear_fwd_24_image(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint16_t *img,
+                                const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

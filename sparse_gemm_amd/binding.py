@@ -377,3 +377,32 @@ def meta_rebuild(mask: torch.Tensor, cap: Optional[int] = None) -> dict:
                                       torch.cuda.current_stream(d).cuda_stream), "bsr_meta_rebuild")
     out["_workspace"] = ws   # keeps the scratch alive until the caller synchronises
     return out
+
+
+def values_pack_24(p: Pattern, Vc: torch.Tensor, mt: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """2:4 block images [nnzb, b, b] (int16 units) for the large-M forward, via bsr_values_pack_24."""
+    _check_tensor(Vc, "Vc", (p.nnzb, p.b, p.b // 2), p.device)
+    _check_raw(mt, "meta", (p.nnzb, p.b, p.b // 16), torch.int16, p.device)
+    if out is None:
+        out = torch.empty((p.nnzb, p.b, p.b), dtype=torch.int16, device=Vc.device)
+    _check_raw(out, "img", (p.nnzb, p.b, p.b), torch.int16, p.device)
+    _lib.check(lib().bsr_values_pack_24(p.handle, _ptr(Vc), _ptr(mt), _ptr(out), _stream(p.device)),
+               "bsr_values_pack_24")
+    return out
+
+
+def linear_fwd_24_image(p: Pattern, X: torch.Tensor, img: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W24~^T + bias from 2:4 block images on the sparse matrix cores (any M), via
+    bsr_linear_fwd_24_image."""
+    M = X.shape[0]
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_raw(img, "img", (p.nnzb, p.b, p.b), torch.int16, p.device)
+    if bias is not None:
+        _check_tensor(bias, "bias", (p.N,), p.device)
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, p.N), p.device)
+    _lib.check(lib().bsr_linear_fwd_24_image(p.handle, _ptr(X), M, _ptr(img), _ptr(bias), _ptr(out),
+                                             _stream(p.device)), "bsr_linear_fwd_24_image")
+    return out

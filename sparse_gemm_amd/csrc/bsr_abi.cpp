@@ -435,6 +435,30 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
     BSR_TRY_END
 }
 
+int32_t bsr_values_pack_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint16_t *meta, uint16_t *img, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(Vc, "Vc", p->nnzb == 0));
+    BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
+    BSR_CHECK(check_ptr(img, "img", p->nnzb == 0));
+    return launch_pack_24(*p, Vc, meta, img, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_linear_fwd_24_image(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint16_t *img,
+                                const bsr_bf16 *bias, bsr_bf16 *Y, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(img, "img", p->nnzb == 0));
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M == 0) return BSR_OK;
+    FwdArgs a{X, M, p->K, img, bias, Y, p->N};
+    return launch_group_gemm(*p, false, a, stream, true);
+    BSR_TRY_END
+}
+
 size_t bsr_meta_rebuild_workspace(int32_t R, int32_t C) {
     if (R <= 0 || C <= 0) return 0;
     return rebuild_workspace_bytes(R, C);

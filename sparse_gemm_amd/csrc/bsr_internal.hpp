@@ -117,7 +117,9 @@ struct FwdArgs {
     uint16_t *out;         // [M][out_ld]
     int out_ld;
 };
-int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream);
+// sparse24: forward only; a.V holds 2:4 block images (bsr_values_pack_24) instead of bf16 blocks.
+int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream,
+                          bool sparse24 = false);
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream);
 
 struct DwArgs {

@@ -30,6 +30,7 @@ namespace bsr {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -172,7 +173,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int BS, int G, int S, int NW, int NL, int NST, int MS, bool TRANS>
+template <int BS, int G, int S, int NW, int NL, int NST, int MS, bool TRANS, bool SP = false>
 __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
@@ -350,6 +351,35 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
                 const int slot = slot_of((wm * GW + t) * PB + h, map0, map1);
                 if (slot == 15) continue;
                 const unsigned char *wb = wt + slot * WBB;
+                if constexpr (SP) {
+                    // 2:4 image of the block: row n holds the row's kept values in 16-byte chunks
+                    // 0 .. BS/16 - 1 and its 16-bit index words at the start of chunk BS/16 (the
+                    // loaders stage it like a bf16 block of the same size). One sparse MFMA per
+                    // 32 columns: lane (n, half lh) takes the kept values of columns 32 kk + 16 lh ..
+                    // + 15 and their 16 index bits; the activation operand is the two 16-deep
+                    // fragments of those 32 columns, concatenated.
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int n = nt * 32 + l32;
+                        const int sw = BS == 32 ? swz4(n) : swz8(n);
+                        const unsigned char *row = wb + n * RB;
+#pragma unroll
+                        for (int kk = 0; kk < KCB / 2; ++kk) {
+                            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(row + (((2 * kk + lh) ^ sw) << 4));
+                            const uint32_t mw =
+                                *reinterpret_cast<const uint32_t *>(row + (((BS / 16) ^ sw) << 4) + 4 * kk);
+                            const int idx = (int)((mw >> (16 * lh)) & 0xFFFFu);
+#pragma unroll
+                            for (int rt = 0; rt < RW; ++rt) {
+                                const bf16x16 bx = __builtin_shufflevector(xf[rt][2 * kk], xf[rt][2 * kk + 1], 0, 1, 2, 3,
+                                                                           4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                                acc[rt][t][nt] =
+                                    __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, bx, acc[rt][t][nt], idx, 0, 0);
+                            }
+                        }
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     bf16x8 wf[KCB];
@@ -813,7 +843,7 @@ int tiles_per_chunk(int nmtiles) {
     return std::max(1, std::min(t, nmtiles));
 }
 
-template <int BS, int G, int S, int NW, bool TRANS>
+template <int BS, int G, int S, int NW, bool TRANS, bool SP = false>
 void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
     constexpr int BM = NW * 32;
     const int nmtiles = (int)((a.M + BM - 1) / BM);
@@ -827,30 +857,30 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     // products (Zipf 16384 x 4096 -> 11008: input gradient 631 -> 613 us, forward 579 -> 573 us; no
     // gain for the 128-row tiles)
     constexpr int MS = G == 4 && NW == 8 ? 2 : 1;
-    hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, MS, TRANS>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
+    hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, MS, TRANS, SP>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
                        (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles,
                        tiles_per_chunk(nmtiles));
 }
 
 // Dispatch on the block size and the variant to the instantiated kernels.
-template <bool TRANS>
+template <bool TRANS, bool SP = false>
 int32_t launch_pg_variant(const bsr_pattern &p, int k, const FwdArgs &a, hipStream_t st) {
     const GroupSchedule &s = (TRANS ? p.bwd : p.fwd)[k];
     const DevSchedule &d = (TRANS ? p.dev.bwd : p.dev.fwd)[k];
     if (p.b == 32) {
-        if (k == 0) launch_pg<32, 4, 8, 8, TRANS>(p, s, d, a, st);
-        else if (k == 1) launch_pg<32, 4, 4, 4, TRANS>(p, s, d, a, st);
-        else launch_pg<32, 2, 4, 4, TRANS>(p, s, d, a, st);
+        if (k == 0) launch_pg<32, 4, 8, 8, TRANS, SP>(p, s, d, a, st);
+        else if (k == 1) launch_pg<32, 4, 4, 4, TRANS, SP>(p, s, d, a, st);
+        else launch_pg<32, 2, 4, 4, TRANS, SP>(p, s, d, a, st);
     } else {
-        if (k == 0) launch_pg<64, 1, 1, 8, TRANS>(p, s, d, a, st);
-        else launch_pg<64, 1, 1, 4, TRANS>(p, s, d, a, st);
+        if (k == 0) launch_pg<64, 1, 1, 8, TRANS, SP>(p, s, d, a, st);
+        else launch_pg<64, 1, 1, 4, TRANS, SP>(p, s, d, a, st);
     }
     return BSR_OK;
 }
 
 }  // namespace
 
-int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {
+int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream, bool sparse24) {
     const hipStream_t st = (hipStream_t)stream;
     const int k = choose_variant(p, transposed, a.M);
     const GemmVariant v = gemm_variant(p.b, k);
@@ -862,7 +892,9 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
         return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
     if ((int64_t)rows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
-    const int32_t rc = transposed ? launch_pg_variant<true>(p, k, a, st) : launch_pg_variant<false>(p, k, a, st);
+    const int32_t rc = transposed ? launch_pg_variant<true>(p, k, a, st)
+                       : sparse24 ? launch_pg_variant<false, true>(p, k, a, st)
+                                  : launch_pg_variant<false>(p, k, a, st);
     if (rc != BSR_OK) return rc;
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }

@@ -200,6 +200,28 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_24(const uint16_t *__restrict__
     }
 }
 
+// 2:4 image of a block for the large-M forward: the size of a bf16 block ([b][b] 16-bit units,
+// 2b bytes per row), row n = the row's b/2 kept values (b bytes), then its b/16 index words
+// (b/8 bytes), then zeros. One thread per block row.
+template <int BS>
+__global__ __launch_bounds__(256) void k_pack_24(const uint16_t *__restrict__ Vc, const uint16_t *__restrict__ meta,
+                                                 int64_t nrows, uint16_t *__restrict__ img) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= nrows) return;
+    constexpr int VC = BS / 16;        // 16-byte chunks of kept values per row (2 or 4)
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(Vc + row * (BS / 2));
+    u32x4 *dst = reinterpret_cast<u32x4 *>(img + row * BS);
+#pragma unroll
+    for (int c = 0; c < VC; ++c) dst[c] = src[c];
+    const uint16_t *m = meta + row * (BS / 16);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < BS / 16; ++k) w[k / 2] |= (uint32_t)m[k] << (16 * (k % 2));
+    dst[VC] = u32x4{w[0], w[1], w[2], w[3]};
+#pragma unroll
+    for (int c = VC + 1; c < 2 * BS / 16; ++c) dst[c] = u32x4{0u, 0u, 0u, 0u};
+}
+
 int32_t launched(const char *what) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(BSR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
@@ -231,6 +253,18 @@ int32_t launch_decompress_24(const bsr_pattern &p, const uint16_t *Vc, const uin
     else
         hipLaunchKernelGGL((k_decompress_24<64>), grid, dim3(256), 0, st, Vc, meta, segments, V);
     return launched("decompress_24 launch");
+}
+
+int32_t launch_pack_24(const bsr_pattern &p, const uint16_t *Vc, const uint16_t *meta, uint16_t *img, void *stream) {
+    const int64_t nrows = (int64_t)p.nnzb * p.b;
+    if (nrows == 0) return BSR_OK;
+    const dim3 grid((unsigned)((nrows + 255) / 256));
+    const hipStream_t st = (hipStream_t)stream;
+    if (p.b == 32)
+        hipLaunchKernelGGL((k_pack_24<32>), grid, dim3(256), 0, st, Vc, meta, nrows, img);
+    else
+        hipLaunchKernelGGL((k_pack_24<64>), grid, dim3(256), 0, st, Vc, meta, nrows, img);
+    return launched("pack_24 launch");
 }
 
 int32_t launch_fwd_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint16_t *Vc, const uint16_t *meta,

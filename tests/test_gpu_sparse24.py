@@ -124,3 +124,98 @@ def test_fwd_24_argument_errors():
     assert L.bsr_linear_fwd_24(p.handle, X.data_ptr(), 1 << 20, Vc.data_ptr(), mt.data_ptr(), None, Y.data_ptr(),
                                st) == 1
     p.close()
+
+
+# ---- large-M forward on the sparse matrix cores (2:4 block images through the panel GEMM) ----
+
+def _image_ref(Vc_ref: np.ndarray, mt_ref: np.ndarray, b: int) -> np.ndarray:
+    """The documented image layout assembled from the oracle's compressed form (raw 16-bit units):
+    per block row, the b/2 kept values, the b/16 index words, zeros to b units."""
+    nnzb = Vc_ref.shape[0]
+    img = np.zeros((nnzb, b, b), dtype=np.uint16)
+    img[:, :, :b // 2] = torch.from_numpy(Vc_ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    img[:, :, b // 2:b // 2 + b // 16] = mt_ref
+    return img
+
+
+@pytest.mark.parametrize("N,K,b,d,seed", [(256, 256, 32, 0.5, 30), (384, 640, 64, 0.4, 31)])
+def test_pack_24_image_layout(N, K, b, d, seed):
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    img = binding.values_pack_24(p, Vc, mt)
+    torch.cuda.synchronize()
+    Vc_ref, mt_ref = oracle.compress_24(V)
+    assert np.array_equal(img.cpu().numpy().view(np.uint16), _image_ref(Vc_ref, mt_ref, b))
+    p.close()
+
+
+def _fwd_image(p, X, V, bias):
+    Vc, mt = binding.values_compress_24(p, V)
+    img = binding.values_pack_24(p, Vc, mt)
+    return binding.linear_fwd_24_image(p, X, img, bias)
+
+
+@pytest.mark.parametrize("variant", ["0", "1", "2"])
+@pytest.mark.parametrize("M,N,K,b,d,seed", [(300, 512, 480, 32, 0.4, 40), (300, 512, 448, 64, 0.4, 41),
+                                            (260, 768, 256, 32, 0.8, 42), (17, 256, 512, 32, 0.5, 43),
+                                            (513, 1024, 512, 32, 0.15, 44)])
+def test_fwd_24_image_every_variant(monkeypatch, variant, M, N, K, b, d, seed):
+    """Every panel-GEMM variant (256-row groups of 4 with 8 slots, 128-row groups of 4, 128-row
+    groups of 2) with 2:4 images, ragged row tails, half panels (K = 480), bias."""
+    monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
+    say(f"case 2:4 image fwd variant={variant} M={M} N={N} K={K} b={b} d={d}")
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    X = synth.activations(M, K, seed)
+    bb = synth.bias_vector(N, seed)
+    Y = _fwd_image(p, X.to(dev()), V.to(dev()), bb.to(dev()))
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, S = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, bias=bb)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    2:4 image fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_fwd_24_image_integer_inputs_bit_exact(b):
+    M, N, K = 200, 512, 512
+    g = np.random.default_rng(50 + b)
+    mask = synth.uniform_mask(N // b, K // b, 0.5, g)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    X = torch.from_numpy(g.integers(-1, 2, size=(M, K)).astype(np.float32)).to(torch.bfloat16)
+    V = torch.from_numpy(g.integers(-1, 2, size=(p.nnzb, b, b)).astype(np.float32)).to(torch.bfloat16)
+    Y = _fwd_image(p, X.to(dev()), V.to(dev()), None)
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, _ = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, want_s=False)
+    assert np.array_equal(Y.cpu().double().numpy(), ref)
+    p.close()
+
+
+@pytest.mark.parametrize("k,nrows", [(2, 4096), (3, 96), (5, 64)])
+def test_fwd_24_image_workloads(k, nrows):
+    """The BERT-base FFN-up, square and Zipf workloads at full size with their blocks pruned to
+    2:4; every row of the first, sampled rows (first, last and random) of the others."""
+    w = synth.WORKLOADS[k]
+    say(f"case 2:4 image fwd {w.name}")
+    host = synth.make_inputs(w, 0, with_dy=False)
+    md = meta.scan(host["mask"])
+    p = Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    Y = _fwd_image(p, host["X"].to(dev()), host["V"].to(dev()), None)
+    torch.cuda.synchronize()
+    g = np.random.default_rng([0, 78])
+    rows = np.unique(np.concatenate([[0, w.M - 1], g.choice(w.M, size=min(nrows, w.M), replace=False)]))
+    rows_t = torch.from_numpy(rows)
+    D = oracle.decompress_24(*oracle.compress_24(host["V"]))
+    ref, S = oracle.fwd(host["X"][rows_t], md["row_ptr"], md["col_idx"], D, w.N, w.b)
+    res = oracle.tolerance_check(Y.cpu()[rows_t], ref, S)
+    say(f"    2:4 image fwd ({rows.size} rows): max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
