@@ -62,11 +62,17 @@ OP_KERNELS = {"fwd": ("k_panel_gemm", "k_small_m"), "dx": ("k_panel_gemm",), "dw
 
 def op_of_kernel(name: str):
     """The op (fwd, dx, dw) a library kernel belongs to, from its (demangled) name: the panel GEMM
-    serves the forward (template flag false) and the input gradient (flag true)."""
+    serves the forward (TRANS false) and the input gradient (TRANS true)."""
     if "bsr" not in name:
         return None
     if "k_panel_gemm" in name:
-        return "dx" if "true>" in name else "fwd"
+        # template arguments <BS, G, S, NW, NL, NST, MS, TRANS, SP>: TRANS marks the input gradient,
+        # SP the 2:4 forward (not part of the step)
+        m = re.search(r"k_panel_gemm<([^>]*)>", name)
+        args = [a.strip() for a in m.group(1).split(",")] if m else []
+        if len(args) >= 9 and args[8] == "true":
+            return None
+        return "dx" if len(args) >= 8 and args[7] == "true" else "fwd"
     if "k_small_m" in name:
         return "fwd"
     if "k_dw_panel" in name or "k_dw_reduce" in name or "k_colsum" in name:
@@ -467,6 +473,34 @@ def sparse24_leg(dev, reps: int) -> dict:
     return out
 
 
+SPARSE24_LARGE_WORKLOAD = 5   # the matrix-core-bound Zipf layer
+
+
+def sparse24_large_leg(dev, reps: int) -> dict:
+    """The large-M forward with 2:4 block images on the sparse matrix cores (bsr_linear_fwd_24_image)
+    beside the bf16 forward on the same pattern (the Zipf workload, its blocks pruned to 2:4; one
+    buffer set, which already touches ~0.5 GB per launch). Useful FLOPs of the 2:4 forward count the
+    kept half of every block."""
+    import torch
+    from sparse_gemm_amd import binding, synth
+    w = synth.WORKLOADS[SPARSE24_LARGE_WORKLOAD]
+    host = synth.make_inputs(w, 0, with_dy=False)
+    p = binding.Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    X, V = host["X"].to(dev), host["V"].to(dev)
+    Y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    Vc, mt = binding.values_compress_24(p, V)
+    img = binding.values_pack_24(p, Vc, mt)
+    ms16 = time_launches(lambda k: binding.linear_fwd(p, X, V, out=Y), 1, reps)
+    ms24 = time_launches(lambda k: binding.linear_fwd_24_image(p, X, img, out=Y), 1, reps)
+    F = 2.0 * w.M * w.b * w.b * p.nnzb
+    out = {"workload": w.name + " (blocks pruned to 2:4)", "fwd_24_image_us": ms24 * 1e3, "fwd_bf16_us": ms16 * 1e3,
+           "tflops_on_kept_values": F / 2 / (ms24 * 1e-3) / 1e12,
+           "bf16_tflops": F / (ms16 * 1e-3) / 1e12, "speedup_vs_bf16": ms16 / ms24}
+    del X, V, Y, Vc, mt, img
+    p.close()
+    return out
+
+
 def rebuild_leg(dev, reps: int) -> dict:
     """The on-device metadata rebuild (bsr_meta_rebuild: six small kernels) on the Zipf workload's
     block mask (344 x 128)."""
@@ -633,6 +667,8 @@ def main():
         out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
         log("[bench] fp8 block values, decode forward")
         out["next_rows"]["fp8_decode"] = fp8_leg(dev, max(50, args.steps))
+        log("[bench] 2:4 inside blocks, large-M forward")
+        out["next_rows"]["sparse24_large"] = sparse24_large_leg(dev, max(10, args.steps // 2))
         log("[bench] on-device metadata rebuild")
         out["next_rows"]["meta_rebuild"] = rebuild_leg(dev, max(50, args.steps))
         log("[bench] 2:4 inside blocks, decode forward")
