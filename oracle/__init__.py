@@ -159,22 +159,25 @@ def e4m3_encode(x: float) -> int:
 
 
 def quantize_fp8(V):
-    """(codes uint8 [nnzb, b, b], scale exponents int32 [nnzb]) of block values V [nnzb, b, b]."""
+    """(codes uint8, scale exponents int32 [nnzb]) of per-block values V [nnzb, ...] (one scale per
+    leading index: dense blocks [nnzb, b, b], or the kept values of 2:4 blocks [nnzb, b, b/2])."""
     V = _f64(V)
-    nnzb, b, _ = V.shape
-    codes = np.empty((nnzb, b, b), dtype=np.uint8)
+    nnzb = V.shape[0]
+    n = int(np.prod(V.shape[1:]))
+    codes = np.empty(V.shape, dtype=np.uint8)
     se = np.empty((nnzb,), dtype=np.int32)
-    lib().oracle_quantize_fp8(nnzb, b, _p(V), _p(codes), _p(se))
+    lib().oracle_quantize_fp8(nnzb, n, _p(V), _p(codes), _p(se))
     return codes, se
 
 
 def dequantize_fp8(codes, se) -> np.ndarray:
-    """fp64 [nnzb, b, b]: code value * 2^se per block."""
+    """fp64 values of the same shape as codes: code value * 2^se per leading index."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     se = _i32(se)
-    nnzb, b, _ = codes.shape
-    out = np.empty((nnzb, b, b), dtype=np.float64)
-    lib().oracle_dequantize_fp8(nnzb, b, _p(codes), _p(se), _p(out))
+    nnzb = codes.shape[0]
+    n = int(np.prod(codes.shape[1:]))
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib().oracle_dequantize_fp8(nnzb, n, _p(codes), _p(se), _p(out))
     return out
 
 

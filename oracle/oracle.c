@@ -234,16 +234,17 @@ uint8_t oracle_e4m3_encode(double x)
     return s | (uint8_t)((e + 7) << 3) | (uint8_t)m;
 }
 
-/* Per block i: amax = max |V[i]|; scale exponent se[i] = the smallest integer e >= -126 with
- * amax <= 448 * 2^e (0 for an all-zero block); codes = E4M3 code of V / 2^se[i] for every
- * element. V is [nnzb][b][b] (fp64 values of bf16 inputs). */
-void oracle_quantize_fp8(int32_t nnzb, int32_t b, const double *V, uint8_t *codes, int32_t *se)
+/* Per block i of n values: amax = max |V[i]|; scale exponent se[i] = the smallest integer
+ * e >= -126 with amax <= 448 * 2^e (0 for an all-zero block); codes = E4M3 code of V / 2^se[i]
+ * for every value. V is [nnzb][n] (fp64 values of bf16 inputs): n = b*b for dense blocks, b*b/2
+ * for the kept values of 2:4 blocks. */
+void oracle_quantize_fp8(int32_t nnzb, int32_t n, const double *V, uint8_t *codes, int32_t *se)
 {
 #pragma omp parallel for schedule(static)
     for (int32_t i = 0; i < nnzb; ++i) {
-        const double *v = V + (int64_t)i * b * b;
+        const double *v = V + (int64_t)i * n;
         double amax = 0.0;
-        for (int32_t k = 0; k < b * b; ++k)
+        for (int32_t k = 0; k < n; ++k)
             if (fabs(v[k]) > amax) amax = fabs(v[k]);
         int32_t e = 0;
         if (amax > 0.0) {
@@ -251,18 +252,18 @@ void oracle_quantize_fp8(int32_t nnzb, int32_t b, const double *V, uint8_t *code
             while (amax > ldexp(448.0, e)) ++e;
         }
         se[i] = e;
-        for (int32_t k = 0; k < b * b; ++k)
-            codes[(int64_t)i * b * b + k] = oracle_e4m3_encode(ldexp(v[k], -e));
+        for (int32_t k = 0; k < n; ++k)
+            codes[(int64_t)i * n + k] = oracle_e4m3_encode(ldexp(v[k], -e));
     }
 }
 
-/* Dequantised values: code value * 2^se[i], as fp64. */
-void oracle_dequantize_fp8(int32_t nnzb, int32_t b, const uint8_t *codes, const int32_t *se, double *V)
+/* Dequantised values: code value * 2^se[i], as fp64; [nnzb][n]. */
+void oracle_dequantize_fp8(int32_t nnzb, int32_t n, const uint8_t *codes, const int32_t *se, double *V)
 {
 #pragma omp parallel for schedule(static)
     for (int32_t i = 0; i < nnzb; ++i)
-        for (int32_t k = 0; k < b * b; ++k)
-            V[(int64_t)i * b * b + k] = ldexp(oracle_e4m3_value(codes[(int64_t)i * b * b + k]), se[i]);
+        for (int32_t k = 0; k < n; ++k)
+            V[(int64_t)i * n + k] = ldexp(oracle_e4m3_value(codes[(int64_t)i * n + k]), se[i]);
 }
 
 /* ---- 2:4 sparsity inside each kept block ----

@@ -129,3 +129,21 @@ def test_fwd_fp8_argument_errors():
                                 st) == 1
     assert L.bsr_linear_fwd_fp8(p.handle, X.data_ptr(), 0, V8.data_ptr(), se.data_ptr(), None, Y.data_ptr(), st) == 0
     p.close()
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_fp8_empty_pattern_and_zero_rows(b):
+    """No kept block: quantisation does nothing and the forward gives the bias exactly (NaN-poisoned
+    output); M = 0 enqueues nothing."""
+    N, K, M = 4 * b, 3 * b, 5
+    mask = np.zeros((N // b, K // b), dtype=np.uint8)
+    p = Pattern.from_mask(mask, N, K, b)
+    V = torch.empty((0, b, b), dtype=torch.bfloat16, device=dev())
+    V8, se = binding.values_quantize_fp8(p, V)
+    bb = synth.bias_vector(N, 3).to(dev())
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_fp8(p, synth.activations(M, K, 3).to(dev()), V8, se, bb, out=Y)
+    binding.linear_fwd_fp8(p, torch.empty((0, K), dtype=torch.bfloat16, device=dev()), V8, se, bb)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.cpu(), bb.cpu().expand(M, N))
+    p.close()

@@ -219,3 +219,30 @@ def test_fwd_24_image_workloads(k, nrows):
     say(f"    2:4 image fwd ({rows.size} rows): max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
     assert res["violations"] == 0, res
     p.close()
+
+
+@pytest.mark.parametrize("b", [32, 64])
+def test_24_empty_pattern_and_zero_rows(b):
+    """No kept block: both 2:4 forwards give the bias exactly (NaN-poisoned outputs, small and large
+    M); M = 0 enqueues nothing."""
+    N, K = 4 * b, 3 * b
+    mask = np.zeros((N // b, K // b), dtype=np.uint8)
+    p = Pattern.from_mask(mask, N, K, b)
+    V = torch.empty((0, b, b), dtype=torch.bfloat16, device=dev())
+    Vc, mt = binding.values_compress_24(p, V)
+    img = binding.values_pack_24(p, Vc, mt)
+    bb = synth.bias_vector(N, 4).to(dev())
+    for M in (5, 300):
+        X = synth.activations(M, K, 4).to(dev())
+        Y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+        Y2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+        binding.linear_fwd_24(p, X, Vc, mt, bb, out=Y1)
+        binding.linear_fwd_24_image(p, X, img, bb, out=Y2)
+        torch.cuda.synchronize()
+        assert torch.equal(Y1.cpu(), bb.cpu().expand(M, N))
+        assert torch.equal(Y2.cpu(), bb.cpu().expand(M, N))
+    X0 = torch.empty((0, K), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_24(p, X0, Vc, mt, bb)
+    binding.linear_fwd_24_image(p, X0, img, bb)
+    torch.cuda.synchronize()
+    p.close()

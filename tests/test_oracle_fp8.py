@@ -128,3 +128,24 @@ def test_planted_mistakes_fail_a_pin():
     def scale_pin(e):
         return amax <= 448 * 2.0 ** e and amax > 448 * 2.0 ** (e - 1)
     assert scale_pin(0) and not scale_pin(-1) and not scale_pin(1)
+
+
+def test_fp8_of_24_kept_values():
+    """fp8 codes of the kept values of 2:4 blocks: every group keeps its largest magnitude, so a
+    block's scale exponent is the same whether taken over the block or over its kept values; the
+    forward with the dequantised, decompressed blocks equals the dense product with them."""
+    N, K, b, M = 256, 256, 32, 6
+    mask = synth.uniform_mask(N // b, K // b, 0.5, np.random.default_rng(5))
+    md = meta.scan(mask)
+    V = synth.block_values(int(mask.sum()), b, 5)
+    V[0] *= 1e3
+    V[1] = V[1] * 2.0 ** -20
+    Vc, mt = oracle.compress_24(V)
+    codes, se = oracle.quantize_fp8(Vc)
+    assert codes.shape == Vc.shape
+    assert np.array_equal(se, oracle.quantize_fp8(V)[1])
+    D = oracle.decompress_24(oracle.dequantize_fp8(codes, se), mt)
+    X = synth.activations(M, K, 5)
+    Y, S = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b)
+    W = meta.dense_weight(md["row_ptr"], md["col_idx"], D, N, K, b)
+    assert np.all(np.abs(Y - X.double().numpy() @ W.T) <= 1e-12 * np.maximum(S, 1e-300))
