@@ -469,6 +469,16 @@ def sparse24_leg(dev, reps: int) -> dict:
                       "pct_hbm_peak": 100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "tflops_on_kept_values": F_kept / (ms * 1e-3) / 1e12}}
     del cs
+    # the kept values as fp8 codes with a power-of-two scale per block (bsr_linear_fwd_fp8_24)
+    q0 = binding.values_quantize_fp8_24(p, c0[0])
+    by8 = vc_bytes // 2 + 4 * nnzb + meta_bytes + 2 * w.M * w.K + 2 * w.M * w.N + 4 * (R + 1) + 4 * nnzb
+    nsets8 = max(1, -(-ROTATE_BYTES // (vc_bytes // 2 + meta_bytes)))
+    qs = [(q0[0], q0[1], c0[1])] + [(q0[0].clone(), q0[1].clone(), c0[1].clone()) for _ in range(nsets8 - 1)]
+    ms8 = time_launches(lambda k: binding.linear_fwd_fp8_24(p, X, *qs[k % nsets8], out=Y), nsets8, reps)
+    out["fwd_fp8_24"] = {"us": ms8 * 1e3, "bytes": by8, "gbs": by8 / (ms8 * 1e-3) / 1e9,
+                         "pct_hbm_peak": 100 * by8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "buffers": f"cold ({nsets8} rotated sets)"}
+    del qs
     p.close()
     return out
 

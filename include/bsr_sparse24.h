@@ -65,6 +65,23 @@ int32_t bsr_values_pack_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint1
 int32_t bsr_linear_fwd_24_image(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint16_t *img,
                                 const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
 
+/* ---- 2:4 combined with fp8 (Lecture 11 summary, 30:31: combining sparsity with quantization) ----
+ * The kept values of the compressed form stored as E4M3 codes with one power-of-two scale per
+ * block, exactly as in bsr_fp8.h (codes Vc8 [nnzb][b][b/2] uint8, scale exponents se [nnzb] int32,
+ * the scale taken over the block's kept values, whose largest magnitude is the block's); the
+ * indices stay in meta. */
+
+/* Quantise the kept values Vc [nnzb][b][b/2] (device, finite) into codes Vc8 and exponents se
+ * (device, se 4-byte aligned). Bit-exact. */
+int32_t bsr_values_quantize_fp8_24(const bsr_pattern *p, const bsr_bf16 *Vc, uint8_t *Vc8, int32_t *se,
+                                   void *stream);
+
+/* Forward for few rows with 2:4 blocks of fp8 kept values: the contract of bsr_linear_fwd_24 with
+ * the kept values code * 2^se[i] (same limits). */
+int32_t bsr_linear_fwd_fp8_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint8_t *Vc8,
+                              const int32_t *se, const uint16_t *meta, const bsr_bf16 *bias, bsr_bf16 *Y,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ EXPORTS = ("bsr_abi_version", "bsr_pattern_create_from_mask", "bsr_pattern_creat
            "bsr_values_quantize_fp8", "bsr_values_dequantize_fp8", "bsr_linear_fwd_fp8",
            # include/bsr_sparse24.h
            "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24", "bsr_values_pack_24",
-           "bsr_linear_fwd_24_image",
+           "bsr_linear_fwd_24_image", "bsr_values_quantize_fp8_24", "bsr_linear_fwd_fp8_24",
            # include/bsr_rebuild.h
            "bsr_meta_rebuild_workspace", "bsr_meta_rebuild")
 
@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     L.bsr_values_decompress_24.argtypes = [P, P, P, P, P]
     L.bsr_linear_fwd_24.argtypes = [P, P, i64, P, P, P, P, P]
     L.bsr_values_pack_24.argtypes = [P, P, P, P, P]
+    L.bsr_values_quantize_fp8_24.argtypes = [P, P, P, P, P]
+    L.bsr_linear_fwd_fp8_24.argtypes = [P, P, i64, P, P, P, P, P, P]
     L.bsr_linear_fwd_24_image.argtypes = [P, P, i64, P, P, P, P]
     L.bsr_meta_rebuild_workspace.argtypes, L.bsr_meta_rebuild_workspace.restype = [i32, i32], sz
     L.bsr_meta_rebuild.argtypes = [i32, i32, P, P, P, P, P, P, i32, P, P, sz, P]
@@ -85,7 +87,7 @@ def load() -> ctypes.CDLL:
            "bsr_values_quantize_fp8", "bsr_values_dequantize_fp8", "bsr_linear_fwd_fp8",
            # include/bsr_sparse24.h
            "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24", "bsr_values_pack_24",
-           "bsr_linear_fwd_24_image",
+           "bsr_linear_fwd_24_image", "bsr_values_quantize_fp8_24", "bsr_linear_fwd_fp8_24",
            # include/bsr_rebuild.h
            "bsr_meta_rebuild_workspace", "bsr_meta_rebuild"):
         getattr(L, f).restype = i32

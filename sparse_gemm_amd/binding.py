@@ -406,3 +406,36 @@ def linear_fwd_24_image(p: Pattern, X: torch.Tensor, img: torch.Tensor, bias: Op
     _lib.check(lib().bsr_linear_fwd_24_image(p.handle, _ptr(X), M, _ptr(img), _ptr(bias), _ptr(out),
                                              _stream(p.device)), "bsr_linear_fwd_24_image")
     return out
+
+
+def values_quantize_fp8_24(p: Pattern, Vc: torch.Tensor, out=None):
+    """(codes uint8 [nnzb, b, b/2], scale exponents int32 [nnzb]) of 2:4 kept values, via
+    bsr_values_quantize_fp8_24."""
+    _check_tensor(Vc, "Vc", (p.nnzb, p.b, p.b // 2), p.device)
+    if out is None:
+        out = (torch.empty((p.nnzb, p.b, p.b // 2), dtype=torch.uint8, device=Vc.device),
+               torch.empty((p.nnzb,), dtype=torch.int32, device=Vc.device))
+    Vc8, se = out
+    _check_raw(Vc8, "Vc8", (p.nnzb, p.b, p.b // 2), torch.uint8, p.device)
+    _check_raw(se, "se", (p.nnzb,), torch.int32, p.device)
+    _lib.check(lib().bsr_values_quantize_fp8_24(p.handle, _ptr(Vc), _ptr(Vc8), _ptr(se), _stream(p.device)),
+               "bsr_values_quantize_fp8_24")
+    return Vc8, se
+
+
+def linear_fwd_fp8_24(p: Pattern, X: torch.Tensor, Vc8: torch.Tensor, se: torch.Tensor, mt: torch.Tensor,
+                      bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W~^T + bias with 2:4 blocks of fp8 kept values, via bsr_linear_fwd_fp8_24."""
+    M = X.shape[0]
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_raw(Vc8, "Vc8", (p.nnzb, p.b, p.b // 2), torch.uint8, p.device)
+    _check_raw(se, "se", (p.nnzb,), torch.int32, p.device)
+    _check_raw(mt, "meta", (p.nnzb, p.b, p.b // 16), torch.int16, p.device)
+    if bias is not None:
+        _check_tensor(bias, "bias", (p.N,), p.device)
+    if out is None:
+        out = torch.empty((M, p.N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, p.N), p.device)
+    _lib.check(lib().bsr_linear_fwd_fp8_24(p.handle, _ptr(X), M, _ptr(Vc8), _ptr(se), _ptr(mt), _ptr(bias),
+                                           _ptr(out), _stream(p.device)), "bsr_linear_fwd_fp8_24")
+    return out

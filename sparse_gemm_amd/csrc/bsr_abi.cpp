@@ -435,6 +435,37 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
     BSR_TRY_END
 }
 
+int32_t bsr_values_quantize_fp8_24(const bsr_pattern *p, const bsr_bf16 *Vc, uint8_t *Vc8, int32_t *se, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0));
+    BSR_CHECK(check_ptr(Vc, "Vc", p->nnzb == 0));
+    BSR_CHECK(check_ptr(Vc8, "Vc8", p->nnzb == 0));
+    if (p->nnzb > 0 && (!se || ((uintptr_t)se & 3u)))
+        return fail(se ? BSR_ERR_MISALIGNED : BSR_ERR_INVALID_ARG, "se must be a 4-byte aligned device pointer");
+    return launch_quantize_fp8(*p, Vc, Vc8, se, stream, true);
+    BSR_TRY_END
+}
+
+int32_t bsr_linear_fwd_fp8_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const uint8_t *Vc8, const int32_t *se,
+                              const uint16_t *meta, const bsr_bf16 *bias, bsr_bf16 *Y, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(Vc8, "Vc8", p->nnzb == 0));
+    if (p->nnzb > 0 && (!se || ((uintptr_t)se & 3u)))
+        return fail(se ? BSR_ERR_MISALIGNED : BSR_ERR_INVALID_ARG, "se must be a 4-byte aligned device pointer");
+    BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
+    if ((size_t)p->nnzb * p->b * p->b >= (size_t)0xFFFFFFF0u)
+        return fail(BSR_ERR_INVALID_ARG, "compressed block values above 4 GiB");
+    if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
+    if (M == 0) return BSR_OK;
+    return launch_fwd_fp8_24(*p, X, M, Vc8, se, meta, bias, Y, stream);
+    BSR_TRY_END
+}
+
 int32_t bsr_values_pack_24(const bsr_pattern *p, const bsr_bf16 *Vc, const uint16_t *meta, uint16_t *img, void *stream) {
     BSR_TRY_BEGIN
     BSR_CHECK(check_call(p, 0));

@@ -88,17 +88,20 @@ __device__ __forceinline__ int scale_exponent(uint32_t amax_bits) {
     return max(-126, m <= 96 ? E - 135 : E - 134);
 }
 
-// One thread per 16 consecutive values; threads per block TPB = BS*BS/16 (64 or 256); a work-group
-// of 256 threads covers 256/TPB blocks.
-template <int BS>
+// One thread per 16 consecutive values of a block of VPB values (b*b for dense blocks, b*b/2 for
+// the kept values of 2:4 blocks): TPB = VPB/16 threads per block (32 .. 256); a work-group of 256
+// threads covers 256/TPB blocks. The block's largest magnitude is reduced with wave shuffles
+// inside groups of min(TPB, 64) lanes, then across the block's waves in LDS.
+template <int VPB>
 __global__ __launch_bounds__(256) void k_quantize_fp8(const uint16_t *__restrict__ V, int nnzb, uint8_t *__restrict__ V8,
                                                       int32_t *__restrict__ se) {
-    constexpr int TPB = BS * BS / 16, NBW = 256 / TPB, WPB = TPB / 64;
+    constexpr int TPB = VPB / 16, NBW = 256 / TPB, WPB = TPB / 64;
+    constexpr int LANES = TPB < 64 ? TPB : 64;
     __shared__ uint32_t wmax[4];
     const int t = threadIdx.x, wave = t >> 6;
     const int i = blockIdx.x * NBW + t / TPB;
     const bool valid = i < nnzb;
-    const int64_t off = (int64_t)min(i, nnzb - 1) * BS * BS + (int64_t)(t % TPB) * 16;
+    const int64_t off = (int64_t)min(i, nnzb - 1) * VPB + (int64_t)(t % TPB) * 16;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(V + off);
     u32x4 v0 = src[0], v1 = src[1];
     uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -106,12 +109,13 @@ __global__ __launch_bounds__(256) void k_quantize_fp8(const uint16_t *__restrict
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
-    if (WPB > 1) {
+    for (int o = LANES / 2; o >= 1; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+    if constexpr (WPB > 1) {
         if ((t & 63) == 0) wmax[wave] = amax;
         __syncthreads();
+        const int w0 = wave / WPB * WPB;
 #pragma unroll
-        for (int k = 0; k < WPB; ++k) amax = max(amax, wmax[k]);
+        for (int k = 0; k < WPB; ++k) amax = max(amax, wmax[w0 + k]);
     }
     const int e = scale_exponent(amax);
     const float inv = pow2f(-e);
@@ -264,15 +268,23 @@ int blocks_per_wg() {
 
 }  // namespace
 
-int32_t launch_quantize_fp8(const bsr_pattern &p, const uint16_t *V, uint8_t *V8, int32_t *se, void *stream) {
+template <int VPB>
+void launch_quantize_vpb(int nnzb, const uint16_t *V, uint8_t *V8, int32_t *se, hipStream_t st) {
+    constexpr int NBW = 256 / (VPB / 16);
+    hipLaunchKernelGGL((k_quantize_fp8<VPB>), dim3((unsigned)((nnzb + NBW - 1) / NBW)), dim3(256), 0, st, V, nnzb, V8,
+                       se);
+}
+
+int32_t launch_quantize_fp8(const bsr_pattern &p, const uint16_t *V, uint8_t *V8, int32_t *se, void *stream,
+                            bool kept24) {
     if (p.nnzb == 0) return BSR_OK;
     const hipStream_t st = (hipStream_t)stream;
     if (p.b == 32) {
-        const dim3 grid((unsigned)((p.nnzb + blocks_per_wg<32>() - 1) / blocks_per_wg<32>()));
-        hipLaunchKernelGGL((k_quantize_fp8<32>), grid, dim3(256), 0, st, V, p.nnzb, V8, se);
+        if (kept24) launch_quantize_vpb<32 * 16>(p.nnzb, V, V8, se, st);
+        else launch_quantize_vpb<32 * 32>(p.nnzb, V, V8, se, st);
     } else {
-        const dim3 grid((unsigned)((p.nnzb + blocks_per_wg<64>() - 1) / blocks_per_wg<64>()));
-        hipLaunchKernelGGL((k_quantize_fp8<64>), grid, dim3(256), 0, st, V, p.nnzb, V8, se);
+        if (kept24) launch_quantize_vpb<64 * 32>(p.nnzb, V, V8, se, st);
+        else launch_quantize_vpb<64 * 64>(p.nnzb, V, V8, se, st);
     }
     return launched("quantize_fp8 launch");
 }

@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
 
@@ -47,6 +48,16 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a buffer offset past every bu
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBuffer);
+}
+
+// Eight E4M3 codes (ascending in the bytes of d0, then d1) -> eight bf16 values code * scale (the
+// gfx950 scaled conversion uses only the exponent of the scale, a power of two here).
+__device__ __forceinline__ bf16x8 expand8(uint32_t d0, uint32_t d1, float scale) {
+    const u32x4 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -110,9 +121,12 @@ __global__ __launch_bounds__(256) void k_decompress_24(const uint16_t *__restric
 
 // Forward: grid (R * BS / 16 / PSW, ceil(M / 16)). A unit is what one sparse MFMA contracts:
 // 64 columns = UB = 64 / BS consecutive kept blocks of the row.
-template <int BS, int NW, int U, int PSW>
+// F8: the kept values are E4M3 codes with one power-of-two scale per block (se), expanded to bf16
+// by the gfx950 scaled conversion (two codes per instruction) before the product.
+template <int BS, int NW, int U, int PSW, bool F8>
 __global__ __launch_bounds__(NW * 64) void k_fwd_24(const uint16_t *__restrict__ X, int K, int M,
-                                                    const uint16_t *__restrict__ Vc, const uint16_t *__restrict__ meta,
+                                                    const void *__restrict__ Vc, const int32_t *__restrict__ se,
+                                                    const uint16_t *__restrict__ meta,
                                                     uint32_t vc_bytes, uint32_t meta_bytes,
                                                     const uint16_t *__restrict__ bias, uint16_t *__restrict__ Y, int N,
                                                     const int32_t *__restrict__ col_idx,
@@ -144,7 +158,9 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_24(const uint16_t *__restrict__
     for (int i0 = e.y; i0 < i1; i0 += NW * U * UB) {
         const int ib = i0 + wave * U * UB;
         bf16x8 a[U][PS];
+        u32x2 code[U][PS];
         int idx[U][PS];
+        int ex[U];
         bf16x16 bx[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -153,11 +169,21 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_24(const uint16_t *__restrict__
             for (int s = 0; s < PS; ++s) {
                 const int p = (s0 + s) * 16 + l16;
                 const uint32_t row = (uint32_t)ia * BS + p;
-                const uint32_t vo = ia < i1 ? (row * (BS / 2) + a_chunk * 8) * 2 : kOutOfRange;
+                constexpr uint32_t VB = F8 ? 1 : 2;   // bytes per kept value
+                const uint32_t vo = ia < i1 ? (row * (BS / 2) + a_chunk * 8) * VB : kOutOfRange;
                 const uint32_t mo = ia < i1 ? (row * CPR + a_chunk) * 2 : kOutOfRange;
-                a[u][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
+                if constexpr (F8) {
+                    const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(rv, vo, 0, 0);
+                    code[u][s] = c;
+                } else {
+                    a[u][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0));
+                }
                 idx[u][s] = (int)(uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rm, mo, 0, 0);
             }
+        }
+        if constexpr (F8) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) ex[u] = se[min(ib + u * UB + a_blk, i1 - 1)];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -172,10 +198,16 @@ __global__ __launch_bounds__(NW * 64) void k_fwd_24(const uint16_t *__restrict__
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the products after every load
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            if constexpr (F8) {
+                const float scale = __uint_as_float((uint32_t)(ex[u] + 127) << 23);
+#pragma unroll
+                for (int s = 0; s < PS; ++s) a[u][s] = expand8(code[u][s][0], code[u][s][1], scale);
+            }
 #pragma unroll
             for (int s = 0; s < PS; ++s)
                 acc[s] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[u][s], bx[u], acc[s], idx[u][s], 0, 0);
+        }
     }
 #pragma unroll
     for (int s = 0; s < PS; ++s) red[wave][s][lane] = acc[s];
@@ -267,24 +299,34 @@ int32_t launch_pack_24(const bsr_pattern &p, const uint16_t *Vc, const uint16_t 
     return launched("pack_24 launch");
 }
 
-int32_t launch_fwd_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint16_t *Vc, const uint16_t *meta,
-                      const uint16_t *bias, uint16_t *Y, void *stream) {
-    const hipStream_t st = (hipStream_t)stream;
-    const uint32_t vc_bytes = (uint32_t)((size_t)p.nnzb * p.b * p.b);          // b/2 bf16 per row
+template <bool F8>
+int32_t launch_fwd_24_impl(const bsr_pattern &p, const uint16_t *X, int64_t M, const void *Vc, const int32_t *se,
+                           const uint16_t *meta, const uint16_t *bias, uint16_t *Y, hipStream_t st) {
+    const uint32_t vc_bytes = (uint32_t)((size_t)p.nnzb * p.b * (p.b / 2) * (F8 ? 1 : 2));
     const uint32_t meta_bytes = (uint32_t)((size_t)p.nnzb * p.b * (p.b / 16) * 2);
     const unsigned chunks = (unsigned)((M + 15) / 16);
     // 8 waves x 4 units (4 blocks for b = 64, 8 for b = 32) in flight, two of the b/16 slices per
     // work-group
     if (p.b == 32) {
         const dim3 grid((unsigned)(p.R * (2 / 2)), chunks);
-        hipLaunchKernelGGL((k_fwd_24<32, 8, 4, 2>), grid, dim3(512), 0, st, X, p.K, (int)M, Vc, meta, vc_bytes, meta_bytes,
-                           bias, Y, p.N, p.dev.col_idx, p.dev.small_m_rows);
+        hipLaunchKernelGGL((k_fwd_24<32, 8, 4, 2, F8>), grid, dim3(512), 0, st, X, p.K, (int)M, Vc, se, meta, vc_bytes,
+                           meta_bytes, bias, Y, p.N, p.dev.col_idx, p.dev.small_m_rows);
     } else {
         const dim3 grid((unsigned)(p.R * (4 / 2)), chunks);
-        hipLaunchKernelGGL((k_fwd_24<64, 8, 4, 2>), grid, dim3(512), 0, st, X, p.K, (int)M, Vc, meta, vc_bytes, meta_bytes,
-                           bias, Y, p.N, p.dev.col_idx, p.dev.small_m_rows);
+        hipLaunchKernelGGL((k_fwd_24<64, 8, 4, 2, F8>), grid, dim3(512), 0, st, X, p.K, (int)M, Vc, se, meta, vc_bytes,
+                           meta_bytes, bias, Y, p.N, p.dev.col_idx, p.dev.small_m_rows);
     }
-    return launched("fwd_24 launch");
+    return launched(F8 ? "fwd_fp8_24 launch" : "fwd_24 launch");
+}
+
+int32_t launch_fwd_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint16_t *Vc, const uint16_t *meta,
+                      const uint16_t *bias, uint16_t *Y, void *stream) {
+    return launch_fwd_24_impl<false>(p, X, M, Vc, nullptr, meta, bias, Y, (hipStream_t)stream);
+}
+
+int32_t launch_fwd_fp8_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint8_t *Vc8, const int32_t *se,
+                          const uint16_t *meta, const uint16_t *bias, uint16_t *Y, void *stream) {
+    return launch_fwd_24_impl<true>(p, X, M, Vc8, se, meta, bias, Y, (hipStream_t)stream);
 }
 
 }  // namespace bsr

@@ -15,4 +15,7 @@ int32_t launch_pack_24(const bsr_pattern &p, const uint16_t *Vc, const uint16_t 
 int32_t launch_fwd_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint16_t *Vc, const uint16_t *meta,
                       const uint16_t *bias, uint16_t *Y, void *stream);
 
+int32_t launch_fwd_fp8_24(const bsr_pattern &p, const uint16_t *X, int64_t M, const uint8_t *Vc8, const int32_t *se,
+                          const uint16_t *meta, const uint16_t *bias, uint16_t *Y, void *stream);
+
 }  // namespace bsr

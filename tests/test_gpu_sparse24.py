@@ -246,3 +246,62 @@ def test_24_empty_pattern_and_zero_rows(b):
     binding.linear_fwd_24_image(p, X0, img, bb)
     torch.cuda.synchronize()
     p.close()
+
+
+# ---- 2:4 combined with fp8 kept values (decode forward) ----
+
+@pytest.mark.parametrize("N,K,b,d,seed", [(256, 256, 32, 0.5, 60), (384, 640, 64, 0.4, 61), (14336, 4096, 64, 0.5, 62)])
+def test_quantize_fp8_24_bit_exact(N, K, b, d, seed):
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Vc8, se = binding.values_quantize_fp8_24(p, Vc)
+    torch.cuda.synchronize()
+    codes_ref, se_ref = oracle.quantize_fp8(oracle.compress_24(V)[0])
+    assert np.array_equal(se.cpu().numpy(), se_ref)
+    assert np.array_equal(Vc8.cpu().numpy(), codes_ref)
+    p.close()
+
+
+@pytest.mark.parametrize("M,N,K,b,d,seed,bias", [
+    (1, 256, 256, 32, 0.5, 70, True), (8, 1024, 512, 32, 0.3, 71, True), (16, 768, 512, 64, 0.5, 72, False),
+    (17, 512, 256, 32, 0.6, 73, False), (3, 320, 224, 32, 0.45, 74, True), (40, 256, 512, 64, 0.5, 75, True)])
+def test_fwd_fp8_24_matches_oracle(M, N, K, b, d, seed, bias):
+    say(f"case fp8 2:4 fwd M={M} N={N} K={K} b={b} d={d}")
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    V = _values(p.nnzb, b, seed)
+    X = synth.activations(M, K, seed)
+    bb = synth.bias_vector(N, seed) if bias else None
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Vc8, se = binding.values_quantize_fp8_24(p, Vc)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_fp8_24(p, X.to(dev()), Vc8, se, mt, None if bb is None else bb.to(dev()), out=Y)
+    torch.cuda.synchronize()
+    Vc_ref, mt_ref = oracle.compress_24(V)
+    D = oracle.decompress_24(oracle.dequantize_fp8(*oracle.quantize_fp8(Vc_ref)), mt_ref)
+    ref, S = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, bias=bb)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    fp8 2:4 fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+def test_fwd_fp8_24_decode_workload_full():
+    w = synth.WORKLOADS[4]
+    say(f"case fp8 2:4 fwd {w.name}")
+    host = synth.make_inputs(w, 0)
+    md = meta.scan(host["mask"])
+    p = Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    Vc, mt = binding.values_compress_24(p, host["V"].to(dev()))
+    Vc8, se = binding.values_quantize_fp8_24(p, Vc)
+    Y = binding.linear_fwd_fp8_24(p, host["X"].to(dev()), Vc8, se, mt)
+    torch.cuda.synchronize()
+    Vc_ref, mt_ref = oracle.compress_24(host["V"])
+    D = oracle.decompress_24(oracle.dequantize_fp8(*oracle.quantize_fp8(Vc_ref)), mt_ref)
+    ref, S = oracle.fwd(host["X"], md["row_ptr"], md["col_idx"], D, w.N, w.b)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    assert res["violations"] == 0, res
+    p.close()
