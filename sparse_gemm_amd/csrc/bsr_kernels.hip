@@ -499,7 +499,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 // products are summed in LDS in wave order (deterministic).
 //   slice s:  A[p][k] = V[i][s*16 + p][k]   B[k][m] = X[m][c*BS + k]   (m < 16; rows past M are 0)
 // ------------------------------------------------------------------------------------------
-template <int BS, int NW, int U, int PSW>
+template <int BS, int NW, int U, int PSW, bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
                                                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
@@ -522,11 +522,10 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     f32x4 acc[PS];
 #pragma unroll
     for (int s = 0; s < PS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i0 = e.y; i0 < i1; i0 += NW * U) {
-        const int ib = i0 + wave * U;
-        // the value loads need only the block index: requested before the column indices, whose
-        // read would otherwise delay them
-        bf16x8 a[U][PS][KC], b[U][KC];
+    // the loads of one pass (this wave's blocks ib .. ib + U - 1): the value loads need only the
+    // block index, so they are requested before the column indices, whose read would otherwise delay
+    // them
+    auto load_pass = [&](int ib, bf16x8 (&a)[U][PS][KC], bf16x8 (&b)[U][KC]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int iu = ib + u;
@@ -548,13 +547,40 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) b[u][kc] = buf_load16(rx, xo + kc * 64, (uint32_t)col[u] * BS * 2);
         }
-        __builtin_amdgcn_sched_barrier(0);   // keep the products after every load
+    };
+    auto compute_pass = [&](const bf16x8 (&a)[U][PS][KC], const bf16x8 (&b)[U][KC]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int s = 0; s < PS; ++s)
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) acc[s] = mfma(a[u][s][kc], b[u][kc], acc[s]);
+    };
+    if constexpr (!PIPE) {
+        for (int i0 = e.y; i0 < i1; i0 += NW * U) {
+            bf16x8 a[U][PS][KC], b[U][KC];
+            load_pass(i0 + wave * U, a, b);
+            __builtin_amdgcn_sched_barrier(0);   // keep the products after every load
+            compute_pass(a, b);
+        }
+    } else {
+        // two register sets: the loads of the next pass are requested before the products of the
+        // current one, so a row's passes overlap their memory latency instead of chaining it
+        bf16x8 aA[U][PS][KC], bA[U][KC], aB[U][PS][KC], bB[U][KC];
+        int i0 = e.y;
+        if (i0 < i1) load_pass(i0 + wave * U, aA, bA);
+        while (i0 < i1) {
+            const int n1 = i0 + NW * U;
+            if (n1 < i1) load_pass(n1 + wave * U, aB, bB);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pass(aA, bA);
+            if (n1 >= i1) break;
+            const int n2 = n1 + NW * U;
+            if (n2 < i1) load_pass(n2 + wave * U, aA, bA);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pass(aB, bB);
+            i0 = n2;
+        }
     }
 #pragma unroll
     for (int s = 0; s < PS; ++s) red[wave][s][lane] = acc[s];
@@ -899,22 +925,38 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }
 
+template <int BS, int NW, int U, int PSW, bool PIPE>
+void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)));
+    hipLaunchKernelGGL((k_small_m<BS, NW, U, PSW, PIPE>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias,
+                       a.out, p.N, p.dev.col_idx, p.dev.small_m_rows);
+}
+
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    const DeviceMeta &d = p.dev;
-    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group; b = 64: 8 waves x
-    // 2 blocks, two of the four slices per work-group (two work-groups per block row spread the
-    // heavier rows over more compute units; measured best among 4-16 waves, 2-4 blocks, 1-4 slices)
+    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group. b = 64: two of
+    // the four slices per work-group (two work-groups per block row spread the heavier rows over more
+    // compute units), 8 waves x 1 block per pass with the next pass's loads requested before the
+    // current products. Measured on the decode shape 8 x 4096 -> 14336 (cold, HIP events): 14.45 us
+    // against 14.95 (8 x 2 blocks, no overlap), 14.9 (8 x 2, overlapped), 15.2 (16 x 1, overlapped),
+    // 15.9 (8 x 4), 16.2 (one slice per work-group).
+    int cfg = -1;
+    if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 5
     if (p.b == 32) {
-        constexpr int NW = 8, U = 8, PSW = 2;
-        const dim3 grid((unsigned)(p.R * (2 / PSW)));
-        hipLaunchKernelGGL((k_small_m<32, NW, U, PSW>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out,
-                           p.N, d.col_idx, d.small_m_rows);
+        switch (cfg) {
+            case 1: launch_small_m_cfg<32, 8, 4, 2, true>(p, a, st); break;
+            case 2: launch_small_m_cfg<32, 8, 8, 2, true>(p, a, st); break;
+            default: launch_small_m_cfg<32, 8, 8, 2, false>(p, a, st); break;
+        }
     } else {
-        constexpr int NW = 8, U = 2, PSW = 2;
-        const dim3 grid((unsigned)(p.R * (4 / PSW)));
-        hipLaunchKernelGGL((k_small_m<64, NW, U, PSW>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias, a.out,
-                           p.N, d.col_idx, d.small_m_rows);
+        switch (cfg) {
+            case 0: launch_small_m_cfg<64, 8, 2, 2, false>(p, a, st); break;
+            case 1: launch_small_m_cfg<64, 8, 2, 2, true>(p, a, st); break;
+            case 3: launch_small_m_cfg<64, 8, 2, 1, true>(p, a, st); break;
+            case 4: launch_small_m_cfg<64, 16, 1, 2, true>(p, a, st); break;
+            case 5: launch_small_m_cfg<64, 8, 4, 2, false>(p, a, st); break;
+            default: launch_small_m_cfg<64, 8, 1, 2, true>(p, a, st); break;
+        }
     }
     return launched("fwd small-M launch");
 }

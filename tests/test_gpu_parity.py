@@ -302,3 +302,15 @@ def test_workload_sampled(k, nrows, nblocks):
     w = synth.WORKLOADS[k]
     say(f"case workload {w.name} (sampled oracle)")
     _sampled_parity(w, 0, nrows, nblocks)
+
+
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5"])
+@pytest.mark.parametrize("M,N,K,b,d,seed", [(8, 512, 512, 64, 0.5, 90), (16, 384, 640, 64, 0.45, 91),
+                                            (3, 256, 512, 32, 0.4, 92), (13, 640, 320, 32, 0.6, 93)])
+def test_every_small_m_config(monkeypatch, cfg, M, N, K, b, d, seed):
+    """Every small-M forward configuration (waves, blocks per pass, slices per work-group, loads of
+    the next pass overlapped or not), whichever the default is, with bias and rows past M."""
+    monkeypatch.setenv("BSR_SMALLM_CONFIG", cfg)
+    say(f"case small-M config={cfg} M={M} N={N} K={K} b={b} d={d}")
+    host = case_inputs(M, N, K, b, seed, density=d, bias=True, dy=False)
+    full_parity(M, N, K, b, host, ops=("fwd",))
