@@ -42,6 +42,22 @@ int32_t bsr_meta_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row
                          int32_t *col_ptr, int32_t *row_idx, int32_t *perm, int32_t cap, int32_t *nnzb,
                          void *workspace, size_t ws_bytes, void *stream);
 
+/* Forward for few activation rows straight from device CSR metadata (for example the output of
+ * bsr_meta_rebuild), with no pattern object and no host round trip: Y[M][N] = X[M][K] . W~^T + bias
+ * where block row r keeps the blocks row_ptr[r] .. row_ptr[r+1]-1 with columns col_idx[...] and
+ * values V[...] in that order (the contract of bsr_linear_fwd). The work-groups take the block rows
+ * in natural order (the host-built pattern deals them heaviest first).
+ *   N, K, b   as for a pattern (b = 32 or 64, N and K positive multiples of b).
+ *   row_ptr   device int32 [N/b + 1], col_idx device int32 [row_ptr[N/b]]: canonical CSR (columns
+ *             ascending and in range inside each row); not validated on the host, since they live
+ *             on the device: malformed metadata is the caller's error.
+ *   X [M][K], V [row_ptr[N/b]][b][b], bias [N] or NULL, Y [M][N]: bf16 device buffers, 16-byte
+ *             aligned; 1 <= M <= 16 (M = 0 is a no-op); the values below 4 GiB.
+ * Every element of Y is written. */
+int32_t bsr_linear_fwd_small_m_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr,
+                                   const int32_t *col_idx, const bsr_bf16 *X, int64_t M, const bsr_bf16 *V,
+                                   const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -439,3 +439,24 @@ def linear_fwd_fp8_24(p: Pattern, X: torch.Tensor, Vc8: torch.Tensor, se: torch.
     _lib.check(lib().bsr_linear_fwd_fp8_24(p.handle, _ptr(X), M, _ptr(Vc8), _ptr(se), _ptr(mt), _ptr(bias),
                                            _ptr(out), _stream(p.device)), "bsr_linear_fwd_fp8_24")
     return out
+
+
+def linear_fwd_small_m_csr(N: int, K: int, b: int, row_ptr: torch.Tensor, col_idx: torch.Tensor, X: torch.Tensor,
+                           V: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X . W~^T + bias for M <= 16 rows from device CSR metadata (e.g. meta_rebuild's), via
+    bsr_linear_fwd_small_m_csr; V holds row_ptr[-1] blocks (any larger leading size is allowed)."""
+    M = X.shape[0]
+    d = X.device.index
+    _check_tensor(X, "X", (M, K), d)
+    if V.dtype != torch.bfloat16 or not V.is_contiguous() or V.shape[1:] != (b, b):
+        raise ValueError("V must be a contiguous bf16 [n, b, b] tensor")
+    if bias is not None:
+        _check_tensor(bias, "bias", (N,), d)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _check_tensor(out, "out", (M, N), d)
+    _lib.check(lib().bsr_linear_fwd_small_m_csr(N, K, b, _ptr(row_ptr), _ptr(col_idx), _ptr(X), M, _ptr(V),
+                                                _ptr(bias), _ptr(out), torch.cuda.current_stream(d).cuda_stream),
+               "bsr_linear_fwd_small_m_csr")
+    return out

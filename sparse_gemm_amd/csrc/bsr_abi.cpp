@@ -490,6 +490,25 @@ int32_t bsr_linear_fwd_24_image(const bsr_pattern *p, const bsr_bf16 *X, int64_t
     BSR_TRY_END
 }
 
+int32_t bsr_linear_fwd_small_m_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
+                                   const bsr_bf16 *X, int64_t M, const bsr_bf16 *V, const bsr_bf16 *bias, bsr_bf16 *Y,
+                                   void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_shape(N, K, b));
+    if (M < 0 || M > kSmallM) return fail(BSR_ERR_INVALID_ARG, "M must lie in [0, 16]");
+    if (!row_ptr || !col_idx || ((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u))
+        return fail(BSR_ERR_INVALID_ARG, "row_ptr and col_idx must be 4-byte aligned device pointers");
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(V, "V", true));
+    BSR_CHECK(check_ptr(bias, "bias", true));
+    BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M == 0) return BSR_OK;
+    if (!V) return fail(BSR_ERR_INVALID_ARG, "V is NULL");
+    FwdArgs a{X, M, K, V, bias, Y, N};
+    return launch_small_m_fwd_csr(N, K, b, row_ptr, col_idx, a, stream);
+    BSR_TRY_END
+}
+
 size_t bsr_meta_rebuild_workspace(int32_t R, int32_t C) {
     if (R <= 0 || C <= 0) return 0;
     return rebuild_workspace_bytes(R, C);

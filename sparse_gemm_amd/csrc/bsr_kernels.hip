@@ -499,7 +499,9 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 // products are summed in LDS in wave order (deterministic).
 //   slice s:  A[p][k] = V[i][s*16 + p][k]   B[k][m] = X[m][c*BS + k]   (m < 16; rows past M are 0)
 // ------------------------------------------------------------------------------------------
-template <int BS, int NW, int U, int PSW, bool PIPE = false>
+// ROWPTR: `rows` is a CSR row pointer (block row r = work-group / PARTS, blocks row_ptr[r] ..
+// row_ptr[r+1]) instead of the host-built list; used with metadata rebuilt on the device.
+template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false>
 __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
                                                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
@@ -510,7 +512,13 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     __shared__ f32x4 red[NW][PS][64];
 
     // work-group entry {block row, first block, end block}: one read ahead of the first value loads
-    const int4 e = reinterpret_cast<const int4 *>(rows)[blockIdx.x / PARTS];
+    int4 e;
+    if constexpr (ROWPTR) {
+        const int rr = (int)(blockIdx.x / PARTS);
+        e = int4{rr, rows[rr], rows[rr + 1], 0};
+    } else {
+        e = reinterpret_cast<const int4 *>(rows)[blockIdx.x / PARTS];
+    }
     const int r = e.x, i1 = e.z, s0 = (int)(blockIdx.x % PARTS) * PSW;   // first slice
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lq = lane >> 4;
@@ -925,6 +933,17 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }
 
+template <int BS>
+void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_ptr, const int32_t *col_idx,
+                           const FwdArgs &a, hipStream_t st) {
+    // the configurations of the host-scheduled forward, in natural row order
+    constexpr int NW = 8, U = BS == 32 ? 8 : 1, PSW = 2;
+    constexpr bool PIPE = BS == 64;
+    const dim3 grid((unsigned)(R * (BS / 16 / PSW)));
+    hipLaunchKernelGGL((k_small_m<BS, NW, U, PSW, PIPE, true>), grid, dim3(NW * 64), 0, st, a.act, K, (int)a.M, a.V,
+                       a.bias, a.out, N, col_idx, row_ptr);
+}
+
 template <int BS, int NW, int U, int PSW, bool PIPE>
 void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)));
@@ -959,6 +978,14 @@ int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream)
         }
     }
     return launched("fwd small-M launch");
+}
+
+int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
+                               const FwdArgs &a, void *stream) {
+    const hipStream_t st = (hipStream_t)stream;
+    if (b == 32) launch_small_m_rowptr<32>(N / b, N, K, row_ptr, col_idx, a, st);
+    else launch_small_m_rowptr<64>(N / b, N, K, row_ptr, col_idx, a, st);
+    return launched("fwd small-M (device CSR) launch");
 }
 
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan_dw(p, M).total : 0; }

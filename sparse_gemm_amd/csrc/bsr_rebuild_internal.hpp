@@ -14,4 +14,8 @@ int32_t launch_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row_p
                        int32_t *col_ptr, int32_t *row_idx, int32_t *perm, int32_t cap, int32_t *nnzb, void *ws,
                        void *stream);
 
+// bsr_kernels.hip: the small-M forward reading a device CSR row pointer in natural row order.
+int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
+                               const FwdArgs &a, void *stream);
+
 }  // namespace bsr
