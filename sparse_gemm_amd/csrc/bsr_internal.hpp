@@ -86,13 +86,15 @@ struct DeviceMeta {
     const int32_t *dw_items = nullptr;
     const int32_t *small_m_rows = nullptr;  // small-M forward: [R][4] {block row, first block, end
                                             // block, 0}, most blocks first
+    const int32_t *small_m_work = nullptr;  // balanced small-M work list: [n][4] {block row, first
+                                            // block, end block, first slice | slices << 8}
 };
 
 }  // namespace bsr
 
 struct bsr_pattern {
     int32_t N = 0, K = 0, b = 0, R = 0, C = 0, nnzb = 0;
-    std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, small_m_rows;
+    std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, small_m_rows, small_m_work;
     bsr::GroupSchedule fwd[bsr::kGemmVariants], bwd[bsr::kGemmVariants];
     bsr::DwSchedule dw;
     bsr::DeviceMeta dev;
@@ -133,6 +135,9 @@ struct DwArgs {
 };
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M);
 int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream);
+
+// Compute units the balanced small-M work list is laid out for (one MI355X).
+constexpr int kSmallMUnits = 256;
 
 // Rows at or below this count take the small-M (streaming) forward kernel.
 constexpr int64_t kSmallM = 16;

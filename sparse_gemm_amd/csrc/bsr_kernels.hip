@@ -501,7 +501,9 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 // ------------------------------------------------------------------------------------------
 // ROWPTR: `rows` is a CSR row pointer (block row r = work-group / PARTS, blocks row_ptr[r] ..
 // row_ptr[r+1]) instead of the host-built list; used with metadata rebuilt on the device.
-template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false>
+// WORK: `rows` is the balanced work list, one entry per work-group {row, first, end, first slice |
+// slices << 8} with 1 or 2 slices (PSW = 2).
+template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false, bool WORK = false>
 __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
                                                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
@@ -516,10 +518,14 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     if constexpr (ROWPTR) {
         const int rr = (int)(blockIdx.x / PARTS);
         e = int4{rr, rows[rr], rows[rr + 1], 0};
+    } else if constexpr (WORK) {
+        e = reinterpret_cast<const int4 *>(rows)[blockIdx.x];
     } else {
         e = reinterpret_cast<const int4 *>(rows)[blockIdx.x / PARTS];
     }
-    const int r = e.x, i1 = e.z, s0 = (int)(blockIdx.x % PARTS) * PSW;   // first slice
+    const int r = e.x, i1 = e.z;
+    const int s0 = WORK ? (e.w & 0xff) : (int)(blockIdx.x % PARTS) * PSW;   // first slice
+    const int ns = WORK ? (e.w >> 8) : PS;                                  // slices (uniform)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lq = lane >> 4;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * K * 2);   // rows past M read as zero
@@ -541,8 +547,10 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
                 make_rsrc(V + (size_t)min(iu, i1 - 1) * BS * BS, iu < i1 ? BS * BS * 2 : 0);
 #pragma unroll
             for (int s = 0; s < PS; ++s)
+                if (s < ns) {
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) a[u][s][kc] = buf_load16(rv, voff + (s * 16 * BS + kc * 32) * 2, 0);
+                    for (int kc = 0; kc < KC; ++kc) a[u][s][kc] = buf_load16(rv, voff + (s * 16 * BS + kc * 32) * 2, 0);
+                }
         }
         int col[U];
 #pragma unroll
@@ -561,8 +569,10 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int s = 0; s < PS; ++s)
+                if (s < ns) {
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) acc[s] = mfma(a[u][s][kc], b[u][kc], acc[s]);
+                    for (int kc = 0; kc < KC; ++kc) acc[s] = mfma(a[u][s][kc], b[u][kc], acc[s]);
+                }
     };
     if constexpr (!PIPE) {
         for (int i0 = e.y; i0 < i1; i0 += NW * U) {
@@ -595,7 +605,7 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     __syncthreads();
     // wave w < PS sums slice w over the waves; lane l holds output rows n = 4 (l / 16) .. + 3 of the
     // slice for activation row l % 16
-    if (wave < PS) {
+    if (wave < ns) {
         f32x4 v = red[0][wave][lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) v += red[w][wave][lane];
@@ -944,6 +954,13 @@ void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_p
                        a.bias, a.out, N, col_idx, row_ptr);
 }
 
+template <int BS, int NW, int U, bool PIPE>
+void launch_small_m_work(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(p.small_m_work.size() / 4));
+    hipLaunchKernelGGL((k_small_m<BS, NW, U, 2, PIPE, false, true>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M,
+                       a.V, a.bias, a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
+}
+
 template <int BS, int NW, int U, int PSW, bool PIPE>
 void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)));
@@ -953,28 +970,31 @@ void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) 
 
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    // b = 32: 8 waves x 8 blocks in flight, both slices of a block per work-group. b = 64: two of
-    // the four slices per work-group (two work-groups per block row spread the heavier rows over more
-    // compute units), 8 waves x 1 block per pass with the next pass's loads requested before the
-    // current products. Measured on the decode shape 8 x 4096 -> 14336 (cold, HIP events): 14.45 us
-    // against 14.95 (8 x 2 blocks, no overlap), 14.9 (8 x 2, overlapped), 15.2 (16 x 1, overlapped),
-    // 15.9 (8 x 4), 16.2 (one slice per work-group).
+    // Default: the balanced work list (items of one or two 16-row slices, a whole number of rounds
+    // of one work-group per compute unit, heavy and light items paired over the rounds). b = 32:
+    // 8 waves x 8 blocks in flight; b = 64: 8 waves x 1 block per pass with the next pass's loads
+    // requested before the current products. Measured on the decode shape 8 x 4096 -> 14336 (cold,
+    // HIP events): 13.5 us; on the row list (two slices per work-group, configurations 0-5): 14.45
+    // (8 x 1 overlapped), 14.95 (8 x 2, no overlap), 14.9 (8 x 2 overlapped), 15.2 (16 x 1
+    // overlapped), 15.9 (8 x 4), 16.2 (one slice per work-group) -- with heaviest-first rows.
     int cfg = -1;
-    if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 5
+    if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 6
     if (p.b == 32) {
         switch (cfg) {
+            case 0: launch_small_m_cfg<32, 8, 8, 2, false>(p, a, st); break;
             case 1: launch_small_m_cfg<32, 8, 4, 2, true>(p, a, st); break;
             case 2: launch_small_m_cfg<32, 8, 8, 2, true>(p, a, st); break;
-            default: launch_small_m_cfg<32, 8, 8, 2, false>(p, a, st); break;
+            default: launch_small_m_work<32, 8, 8, false>(p, a, st); break;
         }
     } else {
         switch (cfg) {
             case 0: launch_small_m_cfg<64, 8, 2, 2, false>(p, a, st); break;
             case 1: launch_small_m_cfg<64, 8, 2, 2, true>(p, a, st); break;
+            case 2: launch_small_m_cfg<64, 8, 1, 2, true>(p, a, st); break;
             case 3: launch_small_m_cfg<64, 8, 2, 1, true>(p, a, st); break;
             case 4: launch_small_m_cfg<64, 16, 1, 2, true>(p, a, st); break;
             case 5: launch_small_m_cfg<64, 8, 4, 2, false>(p, a, st); break;
-            default: launch_small_m_cfg<64, 8, 1, 2, true>(p, a, st); break;
+            default: launch_small_m_work<64, 8, 1, true>(p, a, st); break;
         }
     }
     return launched("fwd small-M launch");
