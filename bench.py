@@ -183,6 +183,63 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops) -> st
     return path
 
 
+MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"
+SIMDS = 1024        # 256 compute units x 4 SIMDs
+XCCS = 8            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; their counts agree to within a cycle
+
+
+def mfma_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"mfma_counters_{workload_name}.txt")
+
+
+def summarize_mfma(pmc_dir: str, workload_name: str, seed: int = 0) -> str:
+    """Executed bf16 MFMA work and MFMA busy time per library kernel from one rocprofv3 --pmc run
+    (MFMA_COUNTERS), against the op's useful flops 2*M*b*b*nnzb. Executed flops = MOPS_BF16 * 512
+    (the counter counts multiply and add operations in units of 512); busy = MFMA busy cycles
+    summed over the SIMDs / (active cycles x SIMDs). Writes the summary under profiles/."""
+    import csv
+    import glob
+    from sparse_gemm_amd import synth
+    w = synth.WORKLOADS[[k for k, x in synth.WORKLOADS.items() if x.name == workload_name][0]]
+    nnzb = int(synth.block_mask(w, seed).sum())
+    useful = 2.0 * w.M * w.b * w.b * nnzb
+    rows = {}
+    for fn in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            if "bsr" not in r["Kernel_Name"]:
+                continue
+            d = rows.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# MFMA counters per launch, {workload_name}", "",
+             "One rocprofv3 counter run of the benchmark, run from the repository root on one MI355X:", "",
+             "```",
+             f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d <dir> -o run -- python3 bench.py "
+             "--workload <k> --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
+             "python3 bench.py --workload <k> --mfma-summary <dir>",
+             "```", "",
+             f"Useful flops per op (2*M*b*b*nnzb): {useful:.6e}. Executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512;",
+             f"busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCCS} * {SIMDS}) over the kernel's run.", "",
+             "| Kernel | op | dispatches | executed bf16 MFMA flops / launch | executed / useful | MFMA busy |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(rows):
+        ds = list(rows[k].values())
+        ex = sum(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds) / len(ds) * 512.0
+        busy = [d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, d.get("GRBM_GUI_ACTIVE", 0.0) / XCCS * SIMDS)
+                for d in ds]
+        op = op_of_kernel(k)
+        ratio = f"{ex / useful:.3f}" if op and ex else "-"
+        short = re.sub(r"\(.*$", "", k.replace("void ", "").replace("bsr::(anonymous namespace)::", ""))
+        lines.append(f"| `{short}` | {op or '-'} | {len(ds)} | {ex:.6e} | {ratio} | "
+                     f"{100.0 * sum(busy) / len(busy):.1f}% |")
+    lines.append("")
+    lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
+    path = mfma_path(workload_name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -547,8 +604,14 @@ def main():
                     help=f"also run one plain {COPY_BYTES}-byte device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="summarize one rocprofv3 --pmc run of the MFMA counters into profiles/ and exit")
     args = ap.parse_args()
 
+    if args.mfma_summary:
+        from sparse_gemm_amd import synth
+        print(summarize_mfma(args.mfma_summary, synth.WORKLOADS[args.workload].name, args.seed))
+        return
     if args.pmc_summary:
         from sparse_gemm_amd import synth
         w = synth.WORKLOADS[args.workload]
