@@ -23,12 +23,13 @@ constexpr int kPanelCols = 64;
 // variant has its own work lists, since S decides how panels split into sub-steps):
 //   0: G = 4, S = 8 (all 8 units of a panel), 8 waves (256 activation rows) -- large problems;
 //   1: G = 4, S = 4, 4 waves (128 rows, three LDS stages: 2 work-groups per CU);
-//   2: G = 2, S = 4 (all 4 units), 4 waves (two LDS stages: 3 work-groups per CU).
+//   2: G = 2, S = 4 (all 4 units), 4 waves (two LDS stages: 3 work-groups per CU);
+//   3: G = 1, S = 2 (both units), 4 waves (two LDS stages) -- when too few groups of 2 to fill.
 // For b = 64 every variant has G = S = 1 (one 64 x 64 block per panel). Every work-group also has
 // waves that only issue the loads: panel_loader_waves(compute waves) of them. Each load into LDS
 // takes a wave tens of cycles to issue while the memory system is busy, so more issuing waves
 // deliver more bytes per clock (measured: 2 -> 4 -> 8 loaders for 8 compute waves).
-constexpr int kGemmVariants = 3;
+constexpr int kGemmVariants = 4;
 constexpr int panel_loader_waves(int compute_waves) { return compute_waves == 8 ? 8 : 4; }
 // Loader waves of the weight-gradient kernel.
 constexpr int kLoaderWaves = 2;
@@ -37,7 +38,7 @@ struct GemmVariant {
 };
 inline GemmVariant gemm_variant(int b, int k) {
     if (b == 64) return GemmVariant{1, 1, k == 0 ? 8 : 4};
-    return k == 0 ? GemmVariant{4, 8, 8} : k == 1 ? GemmVariant{4, 4, 4} : GemmVariant{2, 4, 4};
+    return k == 0 ? GemmVariant{4, 8, 8} : k == 1 ? GemmVariant{4, 4, 4} : k == 2 ? GemmVariant{2, 4, 4} : GemmVariant{1, 2, 4};
 }
 
 // Sub-step record, kRecInts ints: [0] panel index; [1 + k] value block in slot k (-1 = empty),

@@ -819,7 +819,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 // Variant of a panel GEMM call (see gemm_variant); "fills" = at least two work-groups per compute
 // unit, so that one work-group's prologue and epilogue overlap another's main loop.
 int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
-    if (const char *f = std::getenv("BSR_GEMM_VARIANT")) {   // tuning knob: 0 | 1 | 2
+    if (const char *f = std::getenv("BSR_GEMM_VARIANT")) {   // tuning knob: 0 | 1 | 2 | 3
         const int k = std::atoi(f);
         if (k >= 0 && k < kGemmVariants) return k;
     }
@@ -839,7 +839,13 @@ int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
     const bool splits = (double)nsub1 > 1.15 * (double)std::max<int64_t>(1, s[1].npanels);
     if (splits) return fills(0) ? 0 : fills(1) ? 1 : 2;
     const bool long_chains = nsub1 >= 16 * (int64_t)std::max(1, s[1].ngroups);
-    return long_chains && fills(1) ? 1 : 2;
+    if (long_chains && fills(1)) return 1;
+    // When even the 2-member tile leaves CUs with fewer than two work-groups, single-member groups
+    // double the work-groups and shorten every chain (each walks only its own block's panels), at
+    // the price of staging each panel for one output block (BERT-base FFN-up input gradient, 12
+    // two-member groups x 32 tiles: 24.8 -> 19.4 us; where the 2-member tile fills the chip, e.g.
+    // its forward, single members are slower: 19.1 -> 24.4 us).
+    return fills(2) || p.b != 32 ? 2 : 3;
 }
 
 // Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage, at least 256 rows)
@@ -896,7 +902,7 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     constexpr int NL = panel_loader_waves(NW);
     // three LDS stages (two sub-steps of loads in flight); two for the 2-member groups, which then
     // fit three work-groups per CU
-    constexpr int NST = NW == 4 && G == 2 ? 2 : 3;
+    constexpr int NST = NW == 4 && G <= 2 ? 2 : 3;
     // the 256-row 4-member tile: waves of 64 rows x 2 members, each value fragment feeding two
     // products (Zipf 16384 x 4096 -> 11008: input gradient 631 -> 613 us, forward 579 -> 573 us; no
     // gain for the 128-row tiles)
@@ -914,7 +920,8 @@ int32_t launch_pg_variant(const bsr_pattern &p, int k, const FwdArgs &a, hipStre
     if (p.b == 32) {
         if (k == 0) launch_pg<32, 4, 8, 8, TRANS, SP>(p, s, d, a, st);
         else if (k == 1) launch_pg<32, 4, 4, 4, TRANS, SP>(p, s, d, a, st);
-        else launch_pg<32, 2, 4, 4, TRANS, SP>(p, s, d, a, st);
+        else if (k == 2) launch_pg<32, 2, 4, 4, TRANS, SP>(p, s, d, a, st);
+        else launch_pg<32, 1, 2, 4, TRANS, SP>(p, s, d, a, st);
     } else {
         if (k == 0) launch_pg<64, 1, 1, 8, TRANS, SP>(p, s, d, a, st);
         else launch_pg<64, 1, 1, 4, TRANS, SP>(p, s, d, a, st);

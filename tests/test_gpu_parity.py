@@ -41,7 +41,7 @@ def test_shapes(M, N, K, b, d, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
 @pytest.mark.parametrize("M,N,K,b,seed", [
     (300, 512, 480, 32, 11),   # 15 block columns: the last 64-column panel is half a panel
     (300, 512, 448, 64, 12),
@@ -49,7 +49,7 @@ def test_shapes(M, N, K, b, d, seed):
 ])
 def test_every_gemm_variant(monkeypatch, variant, M, N, K, b, seed):
     """Every forward / input-gradient kernel variant (256-row work-groups with 8 slots, 128-row
-    with 4, 128-row with half-width groups), whichever the automatic choice would take for this
+    with 4, 128-row with half-width and single-member groups), whichever the automatic choice would take for this
     size, over a ragged row tail."""
     monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
     say(f"case variant={variant} M={M} N={N} K={K} b={b} seed={seed}")
@@ -57,7 +57,7 @@ def test_every_gemm_variant(monkeypatch, variant, M, N, K, b, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
 @pytest.mark.parametrize("M", [9, 300])
 def test_nonfinite_activation_stays_in_its_blocks(monkeypatch, variant, M):
     """The layer sums over kept blocks only: an infinite activation in input block 1 reaches the
