@@ -157,13 +157,13 @@ def _fwd_image(p, X, V, bias):
     return binding.linear_fwd_24_image(p, X, img, bias)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
 @pytest.mark.parametrize("M,N,K,b,d,seed", [(300, 512, 480, 32, 0.4, 40), (300, 512, 448, 64, 0.4, 41),
                                             (260, 768, 256, 32, 0.8, 42), (17, 256, 512, 32, 0.5, 43),
                                             (513, 1024, 512, 32, 0.15, 44)])
 def test_fwd_24_image_every_variant(monkeypatch, variant, M, N, K, b, d, seed):
     """Every panel-GEMM variant (256-row groups of 4 with 8 slots, 128-row groups of 4, 128-row
-    groups of 2) with 2:4 images, ragged row tails, half panels (K = 480), bias."""
+    groups of 2 and of 1) with 2:4 images, ragged row tails, half panels (K = 480), bias."""
     monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
     say(f"case 2:4 image fwd variant={variant} M={M} N={N} K={K} b={b} d={d}")
     mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
