@@ -779,8 +779,9 @@ __global__ __launch_bounds__((kDwWaves + NL) * 64) void k_dw_panel(
 
 // dV[b][e] = bf16(sum over chunks of partial[chunk][b][e]), 4 elements per thread. The partials are
 // read once: streaming (nontemporal) loads keep them from displacing cached activations (square
-// 8192 x 4096 -> 4096 at density 0.1: weight gradient 101.6 -> 94.5 us; issuing 8 chunks' loads
-// before their sums was slower on BERT-base FFN-up, 25.0 -> 26.4 us).
+// 8192 x 4096 -> 4096 at density 0.1, weight gradients launched back to back: 101.6 -> 94.5 us; no
+// change inside a full training step. Issuing 8 chunks' loads before their sums was slower on
+// BERT-base FFN-up, 25.0 -> 26.4 us).
 __global__ __launch_bounds__(256) void k_dw_reduce(const float *__restrict__ partial, int nchunks, size_t count,
                                                    uint16_t *__restrict__ dV) {
     const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
