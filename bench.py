@@ -285,6 +285,13 @@ def time_ops(run_step, nsteps: int, warmup: int, ops, hold_ms: float):
     torch.cuda.synchronize()
     step_ms = first.elapsed_time(last) / nsteps
     op_ms = {op: sum(a.elapsed_time(b) for a, b in evs[op]) / max(1, len(evs[op])) for op in ops}
+    global _OP_PERCENTILES_MS
+    _OP_PERCENTILES_MS = {}
+    for op in ops:
+        ts = sorted(a.elapsed_time(b) for a, b in evs[op])
+        if ts:
+            q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+            _OP_PERCENTILES_MS[op] = (q(0.1), q(0.5), q(0.9))
     if enqueue_s * 1e3 > hold_ms:
         log(f"[bench] warning: host enqueue took {enqueue_s * 1e3:.1f} ms > hold {hold_ms:.1f} ms; "
             "op times may include host gaps")
@@ -320,6 +327,7 @@ def time_graph(run_step, nsets: int, reps: int):
 
 
 _CYC_PER_MS = 1.0
+_OP_PERCENTILES_MS = {}   # op -> (p10, median, p90) of the per-call times of the last time_ops
 
 
 def build_sets(w, host, nsets: int, dev):
@@ -664,6 +672,9 @@ def main():
         per_op[op] = {"us": op_ms[op] * 1e3, "tflops": F / t / 1e12, "pct_mfma_peak": 100 * F / t / 1e12 / PEAK_BF16_TFLOPS,
                       "gbs": by / t / 1e9, "pct_hbm_peak": 100 * by / t / 1e9 / PEAK_HBM_GBS, "bytes": by,
                       "pct_roofline": 100 * t_roof / t}
+        if op in _OP_PERCENTILES_MS:
+            p10, p50, p90 = _OP_PERCENTILES_MS[op]
+            per_op[op].update({"p10_us": p10 * 1e3, "median_us": p50 * 1e3, "p90_us": p90 * 1e3})
     dom = max(w.ops, key=lambda o: op_ms[o])
     dom_bytes = op_bytes(w, nnzb, dom, w.bias)
     # the dominant op's launch duration: back-to-back launches over the rotated sets, one event pair
