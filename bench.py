@@ -116,7 +116,7 @@ def read_traffic(workload_name: str):
     return out
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops) -> str:
+def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops, out_path=None) -> str:
     """Per-op HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB
     per dispatch) of `bench.py --calibrate-copy`, each scaled by what the same counter reads for a
     plain copy of COPY_BYTES bytes. Writes the summary under profiles/ and returns its path."""
@@ -176,7 +176,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload_name: str, ops) -> st
         names = sorted({k for k in set(fetch) | set(write) if op_of_kernel(k) == op})
         per = sum(sf * avg(fetch, lambda k, n=n: k == n) + sw * avg(write, lambda k, n=n: k == n) for n in names)
         lines.append(f"{op}_hbm_bytes_per_launch: {per:.0f}")
-    path = traffic_path(workload_name)
+    path = out_path or traffic_path(workload_name)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -192,7 +192,7 @@ def mfma_path(workload_name: str) -> str:
     return os.path.join(ROOT, "profiles", f"mfma_counters_{workload_name}.txt")
 
 
-def summarize_mfma(pmc_dir: str, workload_name: str, seed: int = 0) -> str:
+def summarize_mfma(pmc_dir: str, workload_name: str, seed: int = 0, out_path=None) -> str:
     """Executed bf16 MFMA work and MFMA busy time per library kernel from one rocprofv3 --pmc run
     (MFMA_COUNTERS), against the op's useful flops 2*M*b*b*nnzb. Executed flops = MOPS_BF16 * 512
     (the counter counts multiply and add operations in units of 512); busy = MFMA busy cycles
@@ -233,7 +233,7 @@ def summarize_mfma(pmc_dir: str, workload_name: str, seed: int = 0) -> str:
                      f"{100.0 * sum(busy) / len(busy):.1f}% |")
     lines.append("")
     lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
-    path = mfma_path(workload_name)
+    path = out_path or mfma_path(workload_name)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
