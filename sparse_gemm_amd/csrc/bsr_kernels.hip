@@ -792,25 +792,65 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float *__restrict__ par
     store4_bf16(dV + e, s[0], s[1], s[2], s[3]);
 }
 
-// Bias gradient, pass 1: column sums of dY over one chunk of rows -> fp32 partials.
+// Bias gradient, pass 1: fp32 column sums of dY over one chunk of rows. Work-group = 64 columns x one
+// chunk; thread t takes row lane t / 8 (rows m0 + lane, + 32, ...) and the 8 columns 8 (t % 8) ..,
+// so 8 threads read one row's 128-byte segment with 16-byte loads. A thread issues the loads of 8
+// of its rows before adding them in row order; the 32 row lanes are then added in lane order through
+// LDS. (A thread per column reading 2 bytes per row, one row at a time, took 66 us beside a 25 us
+// weight gradient on BERT-base FFN-up.)
 __global__ __launch_bounds__(256) void k_colsum_partial(const uint16_t *__restrict__ dY, int N, int64_t M,
                                                         int64_t rows_per, float *__restrict__ partial) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
-    const int ch = blockIdx.y;
-    if (n >= N) return;
-    const int64_t m0 = (int64_t)ch * rows_per, m1 = std::min<int64_t>(M, m0 + rows_per);
-    float s = 0.f;
-    for (int64_t m = m0; m < m1; ++m) s += from_bf16(dY[m * N + n]);
-    partial[(size_t)ch * N + n] = s;
+    constexpr int RL = 32, U = 8;
+    __shared__ float red[RL][64];
+    const int t = threadIdx.x, lr = t >> 3, piece = t & 7;
+    const int n0 = blockIdx.x * 64 + piece * 8;
+    const int64_t m0 = (int64_t)blockIdx.y * rows_per, m1 = std::min<int64_t>(M, m0 + rows_per);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (n0 < N) {   // N is a multiple of 32: a thread's 8 columns are all inside or all outside
+        for (int64_t mb = m0 + lr; mb < m1; mb += (int64_t)RL * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t m = mb + (int64_t)RL * u;
+                v[u] = m < m1 ? *reinterpret_cast<const u32x4 *>(dY + m * N + n0) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (mb + (int64_t)RL * u >= m1) break;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[2 * j] += from_bf16((uint16_t)(v[u][j] & 0xffffu));
+                    s[2 * j + 1] += from_bf16((uint16_t)(v[u][j] >> 16));
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[lr][piece * 8 + j] = s[j];
+    __syncthreads();
+    const int n = blockIdx.x * 64 + t;
+    if (t < 64 && n < N) {
+        float c = red[0][t];
+        for (int l = 1; l < RL; ++l) c += red[l][t];
+        partial[(size_t)blockIdx.y * N + n] = c;
+    }
 }
 
-// Bias gradient, pass 2: sum the partials in chunk order.
+// Bias gradient, pass 2: sum the partials in chunk order (the loads of 8 chunks issued together).
 __global__ __launch_bounds__(256) void k_colsum_final(const float *__restrict__ partial, int nchunks, int N,
                                                       uint16_t *__restrict__ db) {
+    constexpr int U = 8;
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     float s = 0.f;
-    for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * N + n];
+    for (int c0 = 0; c0 < nchunks; c0 += U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunks ? partial[(size_t)(c0 + u) * N + n] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u < nchunks) s += v[u];
+    }
     db[n] = to_bf16(s);
 }
 
@@ -1055,7 +1095,7 @@ int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream) {
     }
     if (a.dbias) {
         float *bp = reinterpret_cast<float *>(ws + pl.bias_off);
-        hipLaunchKernelGGL(k_colsum_partial, dim3((unsigned)((p.N + 255) / 256), (unsigned)pl.bchunks), dim3(256), 0,
+        hipLaunchKernelGGL(k_colsum_partial, dim3((unsigned)((p.N + 63) / 64), (unsigned)pl.bchunks), dim3(256), 0,
                            st, a.dY, p.N, a.M, pl.brows, bp);
         hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, st, bp, pl.bchunks, p.N,
                            a.dbias);
