@@ -41,6 +41,20 @@ def test_shapes(M, N, K, b, d, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
+@pytest.mark.parametrize("M,N,K,b,d,seed", [
+    (300, 96, 256, 32, 0.5, 14),    # 96 columns: a 64-column group of the bias sums is half outside
+    (1000, 160, 128, 32, 0.5, 15),  # 3 row chunks of 334 rows (not a multiple of the 32 row lanes)
+    (5000, 224, 64, 32, 0.6, 16),   # 19 chunks of 264 rows: a second, partial batch of 8 rows per lane
+    (33, 192, 128, 64, 0.5, 17),
+])
+def test_bias_gradient_ragged(M, N, K, b, d, seed):
+    """The bias gradient's column sums over ragged row chunks and column groups, with the rest of
+    the step."""
+    say(f"case bias gradient M={M} N={N} K={K} b={b} d={d}")
+    host = case_inputs(M, N, K, b, seed, density=d, bias=True)
+    full_parity(M, N, K, b, host, dbias=True)
+
+
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
 @pytest.mark.parametrize("M,N,K,b,seed", [
     (300, 512, 480, 32, 11),   # 15 block columns: the last 64-column panel is half a panel
