@@ -489,7 +489,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 }
 
 // ------------------------------------------------------------------------------------------
-// Small-M forward (M <= 16): a streaming pass over the block values, the memory-bound regime
+// Small-M forward (M <= 32, 16 rows per grid row y): a streaming pass over the block values, the memory-bound regime
 // where the kept blocks are loaded once and expanded into dense matrix-core products (GPU MODE
 // lecture 11 summary, 48:12, "load and sparse expand"). Work-group = PSW consecutive 16-row slices
 // of one block row (rows are dealt heaviest first); its NW waves take the row's kept blocks U at a
@@ -528,9 +528,11 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     const int ns = WORK ? (e.w >> 8) : PS;                                  // slices (uniform)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lq = lane >> 4;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * K * 2);   // rows past M read as zero
+    // this work-group's 16 activation rows m0 .. m0 + 15 (grid row y); rows past M read as zero
+    const int m0 = blockIdx.y * 16, Mc = min(16, M - m0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)m0 * K, (uint32_t)Mc * K * 2);
     const uint32_t xoff = (uint32_t)(l16 * K + lq * 8) * 2;
-    const uint32_t xend = (uint32_t)M * K * 2;   // past the activations: reads zeros
+    const uint32_t xend = (uint32_t)Mc * K * 2;   // past this chunk's activations: reads zeros
     const uint32_t voff = (uint32_t)((s0 * 16 + l16) * BS + lq * 8) * 2;   // + s * 16 rows + kc * 32 columns
 
     f32x4 acc[PS];
@@ -609,10 +611,10 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
         f32x4 v = red[0][wave][lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) v += red[w][wave][lane];
-        if (l16 < M) {
+        if (l16 < Mc) {
             const int n = r * BS + (s0 + wave) * 16 + lq * 4;
             if (bias) v = add_bias4(v, bias + n);
-            store4_bf16(Y + (int64_t)l16 * N + n, v[0], v[1], v[2], v[3]);
+            store4_bf16(Y + (int64_t)(m0 + l16) * N + n, v[0], v[1], v[2], v[3]);
         }
     }
 }
@@ -1001,21 +1003,21 @@ void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_p
     // the configurations of the host-scheduled forward, in natural row order
     constexpr int NW = 8, U = BS == 32 ? 8 : 1, PSW = 2;
     constexpr bool PIPE = BS == 64;
-    const dim3 grid((unsigned)(R * (BS / 16 / PSW)));
+    const dim3 grid((unsigned)(R * (BS / 16 / PSW)), (unsigned)((a.M + 15) / 16));
     hipLaunchKernelGGL((k_small_m<BS, NW, U, PSW, PIPE, true>), grid, dim3(NW * 64), 0, st, a.act, K, (int)a.M, a.V,
                        a.bias, a.out, N, col_idx, row_ptr);
 }
 
 template <int BS, int NW, int U, bool PIPE>
 void launch_small_m_work(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(p.small_m_work.size() / 4));
+    const dim3 grid((unsigned)(p.small_m_work.size() / 4), (unsigned)((a.M + 15) / 16));
     hipLaunchKernelGGL((k_small_m<BS, NW, U, 2, PIPE, false, true>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M,
                        a.V, a.bias, a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
 }
 
 template <int BS, int NW, int U, int PSW, bool PIPE>
 void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)));
+    const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)), (unsigned)((a.M + 15) / 16));
     hipLaunchKernelGGL((k_small_m<BS, NW, U, PSW, PIPE>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias,
                        a.out, p.N, p.dev.col_idx, p.dev.small_m_rows);
 }

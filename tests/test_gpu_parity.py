@@ -320,11 +320,26 @@ def test_workload_sampled(k, nrows, nblocks):
 
 @pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5"])
 @pytest.mark.parametrize("M,N,K,b,d,seed", [(8, 512, 512, 64, 0.5, 90), (16, 384, 640, 64, 0.45, 91),
-                                            (3, 256, 512, 32, 0.4, 92), (13, 640, 320, 32, 0.6, 93)])
+                                            (3, 256, 512, 32, 0.4, 92), (13, 640, 320, 32, 0.6, 93),
+                                            (29, 512, 512, 64, 0.5, 96), (32, 384, 256, 32, 0.5, 97)])
 def test_every_small_m_config(monkeypatch, cfg, M, N, K, b, d, seed):
     """Every small-M forward configuration (waves, blocks per pass, slices per work-group, loads of
     the next pass overlapped or not), whichever the default is, with bias and rows past M."""
     monkeypatch.setenv("BSR_SMALLM_CONFIG", cfg)
     say(f"case small-M config={cfg} M={M} N={N} K={K} b={b} d={d}")
+    host = case_inputs(M, N, K, b, seed, density=d, bias=True, dy=False)
+    full_parity(M, N, K, b, host, ops=("fwd",))
+
+
+@pytest.mark.parametrize("limit,M,N,K,b,d,seed", [
+    ("", 17, 512, 512, 64, 0.5, 100), ("", 32, 512, 384, 32, 0.45, 101), ("", 25, 3584, 1024, 64, 0.5, 102),
+    ("80", 48, 384, 512, 64, 0.5, 103), ("80", 80, 640, 320, 32, 0.4, 104), ("80", 71, 256, 256, 32, 0.6, 105),
+])
+def test_small_m_row_chunks(monkeypatch, limit, M, N, K, b, d, seed):
+    """The small-M forward over several 16-row chunks (grid rows), with a ragged last chunk and bias:
+    by default up to 32 rows, and up to 80 rows with the dispatch limit raised."""
+    if limit:
+        monkeypatch.setenv("BSR_SMALLM_MAX", limit)
+    say(f"case small-M row chunks limit={limit or 'default'} M={M} N={N} K={K} b={b} d={d}")
     host = case_inputs(M, N, K, b, seed, density=d, bias=True, dy=False)
     full_parity(M, N, K, b, host, ops=("fwd",))
