@@ -245,10 +245,11 @@ int32_t bsr_linear_fwd(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const
     BSR_CHECK(check_ptr(Y, "Y", M == 0));
     if (M == 0) return BSR_OK;
     FwdArgs a{X, M, p->K, V, bias, Y, p->N};
-    // Up to 32 rows (two 16-row chunks) the streaming small-M kernel beats the panel GEMM (decode shape
-    // 8 x 4096 -> 14336, b = 64: 17 rows 36.5 -> 24.5 us, 32 rows 36.9 -> 27.8 us; BERT-base FFN-up
-    // weight, 17 and 32 rows: 6.2 -> 4.3 us); from 48 rows on, re-reading the values per chunk loses.
-    int64_t small_max = 2 * kSmallM;
+    // The streaming small-M kernel (up to four 16-row tiles per work-group) beats the panel GEMM up to
+    // 64 rows for b = 64 (decode weight 8 x 4096 -> 14336: 17 rows 36.8 -> 16.1 us, 32 rows 37.1 ->
+    // 19.2, 64 rows 37.4 -> 29.5; 96 rows 46.8 against 37.5) and up to 32 rows for b = 32 (BERT-base
+    // FFN-up weight: 6.2 -> 4.1-4.4 us; even at 48 rows, behind from 64).
+    int64_t small_max = p->b == 64 ? 4 * kSmallM : 2 * kSmallM;
     if (const char *f = std::getenv("BSR_SMALLM_MAX")) small_max = std::atoll(f);   // tuning knob
     if (M <= small_max) return launch_small_m_fwd(*p, a, stream);
     return launch_group_gemm(*p, false, a, stream);

@@ -489,7 +489,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 }
 
 // ------------------------------------------------------------------------------------------
-// Small-M forward (M <= 32, 16 rows per grid row y): a streaming pass over the block values, the memory-bound regime
+// Small-M forward (M <= 64, MT tiles of 16 rows per grid row y): a streaming pass over the block values, the memory-bound regime
 // where the kept blocks are loaded once and expanded into dense matrix-core products (GPU MODE
 // lecture 11 summary, 48:12, "load and sparse expand"). Work-group = PSW consecutive 16-row slices
 // of one block row (rows are dealt heaviest first); its NW waves take the row's kept blocks U at a
@@ -503,7 +503,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 // row_ptr[r+1]) instead of the host-built list; used with metadata rebuilt on the device.
 // WORK: `rows` is the balanced work list, one entry per work-group {row, first, end, first slice |
 // slices << 8} with 1 or 2 slices (PSW = 2).
-template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false, bool WORK = false>
+template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false, bool WORK = false, int MT = 1>
 __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
                                                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     constexpr int PS = PSW;       // 16-row slices of each block handled by this work-group
     constexpr int KC = BS / 32;   // 32-deep k chunks per block
     constexpr int PARTS = BS / 16 / PSW;
-    __shared__ f32x4 red[NW][PS][64];
+    __shared__ f32x4 red[NW][MT * PS][64];
 
     // work-group entry {block row, first block, end block}: one read ahead of the first value loads
     int4 e;
@@ -528,20 +528,23 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     const int ns = WORK ? (e.w >> 8) : PS;                                  // slices (uniform)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lq = lane >> 4;
-    // this work-group's 16 activation rows m0 .. m0 + 15 (grid row y); rows past M read as zero
-    const int m0 = blockIdx.y * 16, Mc = min(16, M - m0);
+    // this work-group's MT tiles of 16 activation rows, m0 .. m0 + 16 MT - 1 (grid row y); rows past M
+    // read as zero. Each value fragment feeds the products of all MT tiles.
+    const int m0 = blockIdx.y * 16 * MT, Mc = min(16 * MT, M - m0);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)m0 * K, (uint32_t)Mc * K * 2);
     const uint32_t xoff = (uint32_t)(l16 * K + lq * 8) * 2;
     const uint32_t xend = (uint32_t)Mc * K * 2;   // past this chunk's activations: reads zeros
     const uint32_t voff = (uint32_t)((s0 * 16 + l16) * BS + lq * 8) * 2;   // + s * 16 rows + kc * 32 columns
 
-    f32x4 acc[PS];
+    f32x4 acc[MT][PS];
 #pragma unroll
-    for (int s = 0; s < PS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < PS; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the loads of one pass (this wave's blocks ib .. ib + U - 1): the value loads need only the
     // block index, so they are requested before the column indices, whose read would otherwise delay
     // them
-    auto load_pass = [&](int ib, bf16x8 (&a)[U][PS][KC], bf16x8 (&b)[U][KC]) __attribute__((always_inline)) {
+    auto load_pass = [&](int ib, bf16x8 (&a)[U][PS][KC], bf16x8 (&b)[U][MT][KC]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int iu = ib + u;
@@ -563,22 +566,27 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
             // non-finite activation would not be zero)
             const uint32_t xo = ib + u < i1 ? xoff : xend;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) b[u][kc] = buf_load16(rx, xo + kc * 64, (uint32_t)col[u] * BS * 2);
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+                    b[u][t][kc] = buf_load16(rx, xo + (uint32_t)t * 16u * (uint32_t)K * 2u + kc * 64, (uint32_t)col[u] * BS * 2);
         }
     };
-    auto compute_pass = [&](const bf16x8 (&a)[U][PS][KC], const bf16x8 (&b)[U][KC]) __attribute__((always_inline)) {
+    auto compute_pass = [&](const bf16x8 (&a)[U][PS][KC], const bf16x8 (&b)[U][MT][KC]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int s = 0; s < PS; ++s)
                 if (s < ns) {
 #pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) acc[s] = mfma(a[u][s][kc], b[u][kc], acc[s]);
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int kc = 0; kc < KC; ++kc) acc[t][s] = mfma(a[u][s][kc], b[u][t][kc], acc[t][s]);
                 }
     };
     if constexpr (!PIPE) {
         for (int i0 = e.y; i0 < i1; i0 += NW * U) {
-            bf16x8 a[U][PS][KC], b[U][KC];
+            bf16x8 a[U][PS][KC], b[U][MT][KC];
             load_pass(i0 + wave * U, a, b);
             __builtin_amdgcn_sched_barrier(0);   // keep the products after every load
             compute_pass(a, b);
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     } else {
         // two register sets: the loads of the next pass are requested before the products of the
         // current one, so a row's passes overlap their memory latency instead of chaining it
-        bf16x8 aA[U][PS][KC], bA[U][KC], aB[U][PS][KC], bB[U][KC];
+        bf16x8 aA[U][PS][KC], bA[U][MT][KC], aB[U][PS][KC], bB[U][MT][KC];
         int i0 = e.y;
         if (i0 < i1) load_pass(i0 + wave * U, aA, bA);
         while (i0 < i1) {
@@ -603,18 +611,24 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
         }
     }
 #pragma unroll
-    for (int s = 0; s < PS; ++s) red[wave][s][lane] = acc[s];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < PS; ++s) red[wave][t * PS + s][lane] = acc[t][s];
     __syncthreads();
     // wave w < PS sums slice w over the waves; lane l holds output rows n = 4 (l / 16) .. + 3 of the
     // slice for activation row l % 16
     if (wave < ns) {
-        f32x4 v = red[0][wave][lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][wave][lane];
-        if (l16 < Mc) {
-            const int n = r * BS + (s0 + wave) * 16 + lq * 4;
-            if (bias) v = add_bias4(v, bias + n);
-            store4_bf16(Y + (int64_t)(m0 + l16) * N + n, v[0], v[1], v[2], v[3]);
+        for (int t = 0; t < MT; ++t) {
+            f32x4 v = red[0][t * PS + wave][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += red[w][t * PS + wave][lane];
+            const int row = t * 16 + l16;
+            if (row < Mc) {
+                const int n = r * BS + (s0 + wave) * 16 + lq * 4;
+                if (bias) v = add_bias4(v, bias + n);
+                store4_bf16(Y + (int64_t)(m0 + row) * N + n, v[0], v[1], v[2], v[3]);
+            }
         }
     }
 }
@@ -1008,11 +1022,11 @@ void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_p
                        a.bias, a.out, N, col_idx, row_ptr);
 }
 
-template <int BS, int NW, int U, bool PIPE>
+template <int BS, int NW, int U, bool PIPE, int MT = 1>
 void launch_small_m_work(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)(p.small_m_work.size() / 4), (unsigned)((a.M + 15) / 16));
-    hipLaunchKernelGGL((k_small_m<BS, NW, U, 2, PIPE, false, true>), grid, dim3(NW * 64), 0, st, a.act, p.K, (int)a.M,
-                       a.V, a.bias, a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
+    const dim3 grid((unsigned)(p.small_m_work.size() / 4), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+    hipLaunchKernelGGL((k_small_m<BS, NW, U, 2, PIPE, false, true, MT>), grid, dim3(NW * 64), 0, st, a.act, p.K,
+                       (int)a.M, a.V, a.bias, a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
 }
 
 template <int BS, int NW, int U, int PSW, bool PIPE>
@@ -1038,7 +1052,11 @@ int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream)
             case 0: launch_small_m_cfg<32, 8, 8, 2, false>(p, a, st); break;
             case 1: launch_small_m_cfg<32, 8, 4, 2, true>(p, a, st); break;
             case 2: launch_small_m_cfg<32, 8, 8, 2, true>(p, a, st); break;
-            default: launch_small_m_work<32, 8, 8, false>(p, a, st); break;
+            default:
+                // rows above 16: two 16-row tiles per work-group, each value fragment loaded once
+                if (a.M > 16) launch_small_m_work<32, 8, 8, false, 2>(p, a, st);
+                else launch_small_m_work<32, 8, 8, false>(p, a, st);
+                break;
         }
     } else {
         switch (cfg) {
@@ -1048,7 +1066,11 @@ int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream)
             case 3: launch_small_m_cfg<64, 8, 2, 1, true>(p, a, st); break;
             case 4: launch_small_m_cfg<64, 16, 1, 2, true>(p, a, st); break;
             case 5: launch_small_m_cfg<64, 8, 4, 2, false>(p, a, st); break;
-            default: launch_small_m_work<64, 8, 1, true>(p, a, st); break;
+            default:
+                if (a.M > 32) launch_small_m_work<64, 8, 1, true, 4>(p, a, st);
+                else if (a.M > 16) launch_small_m_work<64, 8, 1, true, 2>(p, a, st);
+                else launch_small_m_work<64, 8, 1, true>(p, a, st);
+                break;
         }
     }
     return launched("fwd small-M launch");

@@ -333,11 +333,13 @@ def test_every_small_m_config(monkeypatch, cfg, M, N, K, b, d, seed):
 
 @pytest.mark.parametrize("limit,M,N,K,b,d,seed", [
     ("", 17, 512, 512, 64, 0.5, 100), ("", 32, 512, 384, 32, 0.45, 101), ("", 25, 3584, 1024, 64, 0.5, 102),
+    ("", 57, 512, 512, 64, 0.5, 106), ("", 64, 896, 640, 64, 0.4, 107),
     ("80", 48, 384, 512, 64, 0.5, 103), ("80", 80, 640, 320, 32, 0.4, 104), ("80", 71, 256, 256, 32, 0.6, 105),
 ])
 def test_small_m_row_chunks(monkeypatch, limit, M, N, K, b, d, seed):
-    """The small-M forward over several 16-row chunks (grid rows), with a ragged last chunk and bias:
-    by default up to 32 rows, and up to 80 rows with the dispatch limit raised."""
+    """The small-M forward with 2 or 4 activation tiles of 16 rows per work-group and several grid rows,
+    a ragged last tile and bias: by default up to 64 rows (b = 64) or 32 (b = 32), and up to 80 rows
+    with the dispatch limit raised."""
     if limit:
         monkeypatch.setenv("BSR_SMALLM_MAX", limit)
     say(f"case small-M row chunks limit={limit or 'default'} M={M} N={N} K={K} b={b} d={d}")
