@@ -6,13 +6,18 @@ bsr_linear_bwd_input and bsr_linear_bwd_weight (the ops the workload lists), on 
 synthetic bf16 inputs already resident in HBM. Useful FLOPs per op are 2*M*b^2*nnzb (work
 on zero blocks is never counted).
 
-Default workload: BERT-base FFN-up, X[4096,768] -> Y[4096,3072], 32x32 blocks at density
-0.25. By default every step uses the next of several distinct buffer sets, together at least
-512 MB (twice the 256 MB Infinity Cache), so each step reads its inputs from HBM; --warm
-reuses one set.
+Headline workload (default): the largest configuration, X[16384,4096] -> Y[16384,11008],
+32x32 blocks at overall density 0.3 with Zipf-distributed blocks per block row, fwd + dX +
+dW. The headline value is 3F / (time of one step), the step timed over exactly --steps
+HIP-graph replays after --warmup eager steps. Buffers are cold: steps rotate over distinct
+buffer sets that together hold at least 512 MiB (twice the 256 MB Infinity Cache); one set
+of the headline workload is already ~1 GB. --warm reuses one set.
 
-Prints ONE JSON line. Extra legs: the same kernels on the density-1.0 pattern of the same
-shape, hipBLASLt dense (torch.matmul) as context, and the fp64 oracle on the host cores.
+Prints ONE JSON line. Besides the headline: per-op times and the dominant op's roofline,
+the same kernels on the density-1.0 pattern of the same shape, hipBLASLt dense
+(torch.matmul) as context, the other reference workloads (BERT-base FFN-up, the square
+layer at density 0.1, the decode shape) with their own per-op times and rooflines, the
+NEXT-row kernels, and the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -267,8 +272,9 @@ def time_ops(run_step, nsteps: int, warmup: int, ops, hold_ms: float):
     """Per-op GPU durations with HIP events on the launch stream (torch's current stream).
 
     A spin kernel holds the GPU while the host enqueues all timed steps, so back-to-back
-    kernels run with no host gaps and each event pair brackets GPU execution only (what
-    rocprofv3's kernel trace reports). Returns (GPU ms per step, {op: avg ms}, enqueue s)."""
+    kernels run with no host gaps and each event pair brackets GPU execution plus the
+    dispatch of the op's first kernel. Returns (GPU ms per step, {op: avg ms},
+    {op: (p10, median, p90) ms}, host enqueue s)."""
     import torch
     for k in range(warmup):
         run_step(k, None)
@@ -284,65 +290,87 @@ def time_ops(run_step, nsteps: int, warmup: int, ops, hold_ms: float):
     enqueue_s = time.perf_counter() - t
     torch.cuda.synchronize()
     step_ms = first.elapsed_time(last) / nsteps
-    op_ms = {op: sum(a.elapsed_time(b) for a, b in evs[op]) / max(1, len(evs[op])) for op in ops}
-    global _OP_PERCENTILES_MS
-    _OP_PERCENTILES_MS = {}
+    op_ms, pct = {}, {}
     for op in ops:
         ts = sorted(a.elapsed_time(b) for a, b in evs[op])
+        op_ms[op] = sum(ts) / max(1, len(ts))
         if ts:
             q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
-            _OP_PERCENTILES_MS[op] = (q(0.1), q(0.5), q(0.9))
+            pct[op] = (q(0.1), q(0.5), q(0.9))
     if enqueue_s * 1e3 > hold_ms:
         log(f"[bench] warning: host enqueue took {enqueue_s * 1e3:.1f} ms > hold {hold_ms:.1f} ms; "
             "op times may include host gaps")
-    return step_ms, op_ms, enqueue_s
+    return step_ms, op_ms, pct, enqueue_s
 
 
-def time_graph(run_step, nsets: int, reps: int):
-    """Whole-step throughput: the steps over all buffer sets captured once as a HIP graph,
-    replayed `reps` times; wall clock and HIP events bracketed by synchronize."""
+def time_graph_steps(run_step, nsets: int, nsteps: int, hold_ms: float = 20.0):
+    """Exactly `nsteps` timed steps: one HIP graph holding steps 0 .. nsteps-1 (step k on buffer
+    set k % nsets), captured after an eager pass on the capture stream and replayed once untimed,
+    then replayed once between two synchronizes with HIP events and the wall clock around it.
+    Returns (event ms per step, wall ms per step)."""
     import torch
-    g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for k in range(nsets):            # one eager pass on the capture stream first
+        for k in range(min(nsets, nsteps)):
             run_step(k, None)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for k in range(nsets):
+        for k in range(nsteps):
             run_step(k, None)
     g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(hold_ms * _CYC_PER_MS))
     t = time.perf_counter()
     a.record()
-    for _ in range(reps):
-        g.replay()
+    g.replay()
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t
-    steps = reps * nsets
-    return a.elapsed_time(b) / steps, wall / steps * 1e3, steps
+    del g
+    return a.elapsed_time(b) / nsteps, wall / nsteps * 1e3
 
 
 _CYC_PER_MS = 1.0
-_OP_PERCENTILES_MS = {}   # op -> (p10, median, p90) of the per-call times of the last time_ops
 
 
-def build_sets(w, host, nsets: int, dev):
+def set_bytes(w, nnzb: int) -> int:
+    """Distinct bytes of one buffer set: every tensor the step reads or writes, once."""
+    b2 = 2 * nnzb * w.b * w.b
+    by = 2 * w.M * w.K + b2 + 2 * w.M * w.N + (2 * w.N if w.bias else 0)
+    if "dx" in w.ops or "dw" in w.ops:
+        by += 2 * w.M * w.N
+    if "dx" in w.ops:
+        by += 2 * w.M * w.K
+    if "dw" in w.ops:
+        by += b2
+    return by
+
+
+def rotation_sets(w, nnzb: int, warm: bool) -> int:
+    return 1 if warm else max(1, -(-ROTATE_BYTES // max(1, set_bytes(w, nnzb))))
+
+
+def build_sets(w, host, nsets: int, dev, share=None):
+    """nsets buffer sets on the device. With `share` (sets of another pattern of the same shape),
+    only the block values and their gradient are new; activations and outputs are reused."""
     import torch
-    from sparse_gemm_amd import binding
     sets = []
     for k in range(nsets):
         s = {}
-        for key in ("X", "V", "dY"):
-            if host.get(key) is not None:
-                s[key] = host[key].to(dev) if k == 0 else host[key].to(dev).clone()
-        s["bias"] = host["bias"].to(dev) if host.get("bias") is not None else None
-        s["Y"] = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-        if "dx" in w.ops:
-            s["dX"] = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+        if share is not None:
+            s.update({key: share[k % len(share)][key] for key in ("X", "dY", "bias", "Y", "dX") if key in share[0]})
+        else:
+            for key in ("X", "dY"):
+                if host.get(key) is not None:
+                    s[key] = host[key].to(dev) if k == 0 else sets[0][key].clone()
+            s["bias"] = host["bias"].to(dev) if host.get("bias") is not None else None
+            s["Y"] = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+            if "dx" in w.ops:
+                s["dX"] = torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+        s["V"] = host["V"].to(dev) if k == 0 else sets[0]["V"].clone()
         if "dw" in w.ops:
             s["dV"] = torch.empty_like(s["V"])
         sets.append(s)
@@ -371,46 +399,6 @@ def make_runner(p, w, sets, ws, only=None):
     return run_step
 
 
-def cpu_baseline(w, host, seconds: float) -> dict:
-    """The fp64 oracle, as it stands, on the same workload and the host's cores."""
-    import oracle
-    from oracle import meta
-    md = meta.scan(host["mask"])
-    nnzb = md["nnzb"]
-    # bounded sample: the first rows of the workload, sized to about `seconds` of CPU work
-    F_row = 2.0 * w.b * w.b * nnzb * len(w.ops)
-    X64 = oracle._f64(host["X"])
-    dY64 = oracle._f64(host["dY"]) if host.get("dY") is not None else None
-    probe_rows = min(w.M, 64)
-    t = time.perf_counter()
-    _run_oracle(w, md, host, X64, dY64, probe_rows)
-    per_row = max(1e-6, (time.perf_counter() - t) / probe_rows)
-    rows = int(min(w.M, max(probe_rows, seconds / per_row)))
-    reps = max(1, int(round(seconds / (per_row * rows)))) if rows == w.M else 1
-    t = time.perf_counter()
-    for _ in range(reps):
-        _run_oracle(w, md, host, X64, dY64, rows)
-    dt = time.perf_counter() - t
-    flops = F_row * rows * reps
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{reps} pass(es) over the first {rows} of {w.M} rows of the workload, ops "
-                      f"{'+'.join(w.ops)}, fp64 with no tolerance sums, {dt:.1f} s wall, "
-                      f"{flops / dt / 1e9:.2f} GFLOP/s",
-            "cpu_model": cpu_model(), "seconds": dt}
-
-
-def _run_oracle(w, md, host, X64, dY64, rows):
-    import oracle
-    for op in w.ops:
-        if op == "fwd":
-            oracle.fwd(X64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.N, w.b,
-                       bias=host["bias"], want_s=False)
-        elif op == "dx":
-            oracle.dx(dY64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.K, w.b, want_s=False)
-        elif op == "dw":
-            oracle.dw(dY64[:rows], X64[:rows], md["row_ptr"], md["col_idx"], w.b, want_s=False)
-
-
 def time_launches(fn, nsets: int, reps: int) -> float:
     """Average ms per launch of fn(k) over reps launches cycling nsets buffer sets, HIP events
     on the launch stream with the queue pre-filled behind a spin kernel."""
@@ -426,6 +414,195 @@ def time_launches(fn, nsets: int, reps: int) -> float:
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def op_kernels(w, op: str):
+    """Library kernels one launch of the op runs at this workload (the dispatch of bsr_abi.cpp)."""
+    if op == "fwd":
+        small = (w.M <= 64) if w.b == 64 else (w.M <= 32)
+        return ["k_small_m"] if small else ["k_panel_gemm"]
+    if op == "dx":
+        return ["k_panel_gemm"]
+    return list(OP_KERNELS["dw"])
+
+
+def roofline_of(w, nnzb: int, op: str, t_s: float, traffic) -> dict:
+    F = 2.0 * w.M * w.b * w.b * nnzb
+    by = op_bytes(w, nnzb, op, w.bias)
+    if F / by < RIDGE:
+        r = {"bound": "hbm", "achieved": by / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": F / t_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = traffic
+    return r
+
+
+def measure(w, host, dev, nsteps: int, warmup: int, warm: bool, extras: bool, label: str) -> dict:
+    """One workload: the whole step (fwd [+ dX + dW]) over rotated cold buffer sets, per-op
+    times, the dominant op's roofline, a cache-warm step, and (extras) the same kernels at
+    density 1.0 and hipBLASLt dense GEMMs of the same shapes."""
+    import numpy as np
+    import torch
+    from sparse_gemm_amd import binding, synth
+    mask = host["mask"]
+    nnzb = int(mask.sum())
+    p = binding.Pattern.from_mask(mask, w.N, w.K, w.b)
+    F = 2.0 * w.M * w.b * w.b * nnzb
+    nsets = rotation_sets(w, nnzb, warm)
+    sets = build_sets(w, host, nsets, dev)
+    ws_bytes = binding.bwd_weight_workspace_bytes(p, w.M) if "dw" in w.ops else 0
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
+    dist = set_bytes(w, nnzb)
+    log(f"[bench] {label}: {w.name}, nnzb {nnzb}, {nsets} buffer set(s) of {dist / 1e6:.1f} MB")
+    run = make_runner(p, w, sets, ws)
+    eager_ms, op_in_step, pct, enq = time_ops(run, nsteps, warmup, w.ops, hold_ms=50.0 + 2.0 * nsteps)
+    step_ms, wall_ms = time_graph_steps(run, nsets, nsteps)
+    nops = len(w.ops)
+    # each op alone, launched back to back over the rotated sets: the kernels' own durations
+    op_alone = {op: time_launches(lambda k, r=make_runner(p, w, sets, ws, only=op): r(k, None), nsets,
+                                  max(20, nsteps)) for op in w.ops}
+    log(f"[bench] {label}: step {step_ms * 1e3:.1f} us (graph), " +
+        ", ".join(f"{o} {t * 1e3:.1f} us" for o, t in op_alone.items()))
+    tr = read_traffic(w.name)
+    per_op = {}
+    for op in w.ops:
+        t = op_alone[op] * 1e-3
+        by = op_bytes(w, nnzb, op, w.bias)
+        t_roof = max(F / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        per_op[op] = {"us": op_alone[op] * 1e3, "us_in_step": op_in_step[op] * 1e3,
+                      "tflops": F / t / 1e12, "pct_mfma_peak": 100 * F / t / 1e12 / PEAK_BF16_TFLOPS,
+                      "gbs": by / t / 1e9, "pct_hbm_peak": 100 * by / t / 1e9 / PEAK_HBM_GBS, "bytes": by,
+                      "pct_roofline": 100 * t_roof / t, "kernels": op_kernels(w, op)}
+        if op in pct:
+            per_op[op].update({"p10_us_in_step": pct[op][0] * 1e3, "median_us_in_step": pct[op][1] * 1e3,
+                               "p90_us_in_step": pct[op][2] * 1e3})
+    dom = max(w.ops, key=lambda o: op_alone[o])
+    roof = roofline_of(w, nnzb, dom, op_alone[dom] * 1e-3, tr.get(dom) if tr else None)
+    roof["kernel"] = {"fwd": "bsr_linear_fwd", "dx": "bsr_linear_bwd_input", "dw": "bsr_linear_bwd_weight"}[dom]
+    roof["per_launch"] = {"flops": F, "algorithmic_bytes": op_bytes(w, nnzb, dom, w.bias),
+                          "avg_us": op_alone[dom] * 1e3, "kernels": op_kernels(w, dom),
+                          "timing": "back-to-back launches over the rotated buffer sets, HIP events on the "
+                                    "launch stream, queue pre-filled behind a spin kernel"}
+    res = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.b, "density": w.density, "nnzb": nnzb,
+           "pattern": w.pattern, "ops": "+".join(w.ops),
+           "buffers": (f"cold ({nsets} rotated sets of {dist} distinct bytes, {nsets * dist} in all)" if not warm
+                       else "warm (1 set)"),
+           "rotated_bytes": nsets * dist,
+           "pattern_sha256": synth.mask_digest(mask), "rows": synth.row_histogram(mask),
+           "ms_per_step": step_ms, "steps": nsteps,
+           "tflops": nops * F / (step_ms * 1e-3) / 1e12,
+           "pct_bf16_mfma_peak": 100 * nops * F / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "ops": per_op, "roofline": roof,
+           "timing": {"ms_per_step": "one HIP graph of exactly `steps` steps (buffer sets in rotation) replayed "
+                                     "between two synchronizes, HIP events",
+                      "graph_wall_ms_per_step": wall_ms, "eager_gpu_ms_per_step": eager_ms,
+                      "eager_host_enqueue_ms_per_step": enq * 1e3 / nsteps,
+                      "ops.us": "each op alone, back-to-back launches over the rotated sets (kernel durations)",
+                      "ops.us_in_step": "HIP events around each call inside eager steps (includes the "
+                                        "dispatch of the op's first kernel)"}}
+    if not warm and nsets > 1:
+        res["warm_ms_per_step"], _ = time_graph_steps(make_runner(p, w, sets[:1], ws), 1, nsteps)
+    elif not warm:
+        res["warm_ms_per_step"] = None   # one set already exceeds the rotation size: no warm variant
+    if extras:
+        # the same kernels on the density-1.0 pattern of the same shape (activations shared)
+        full = np.ones_like(mask)
+        host_d = {"mask": full, "V": synth.block_values(int(full.sum()), w.b, 0)}
+        pd = binding.Pattern.from_mask(full, w.N, w.K, w.b)
+        nnzd = int(full.sum())
+        nsets_d = min(nsets, rotation_sets(w, nnzd, warm))
+        sets_d = build_sets(w, host_d, nsets_d, dev, share=sets)
+        wsd_b = binding.bwd_weight_workspace_bytes(pd, w.M) if "dw" in w.ops else 0
+        wsd = torch.empty((wsd_b,), dtype=torch.uint8, device=dev) if wsd_b else None
+        run_d = make_runner(pd, w, sets_d, wsd)
+        nd = max(10, nsteps // 2)
+        for k in range(3):
+            run_d(k, None)
+        d_ms, _ = time_graph_steps(run_d, nsets_d, nd)
+        d_alone = {op: time_launches(lambda k, r=make_runner(pd, w, sets_d, wsd, only=op): r(k, None), nsets_d, nd)
+                   for op in w.ops}
+        res["density_1.0_same_kernels"] = {
+            "ms_per_step": d_ms, "speedup_of_sparse": d_ms / step_ms,
+            "ops_us": {o: t * 1e3 for o, t in d_alone.items()},
+            "ops_speedup_of_sparse": {o: d_alone[o] / op_alone[o] for o in w.ops},
+            "tflops": nops * 2.0 * w.M * w.b * w.b * nnzd / (d_ms * 1e-3) / 1e12,
+            "buffers": f"{nsets_d} rotated set(s)"}
+        log(f"[bench] {label}: density 1.0 step {d_ms * 1e3:.1f} us ({d_ms / step_ms:.2f}x the sparse step)")
+        del sets_d, wsd
+        pd.close()
+        # hipBLASLt dense GEMMs of the same shapes (torch.matmul; context only)
+        dense_w = [s_["V"].new_empty((w.N, w.K)).normal_() for s_ in sets[:max(1, min(nsets, 2))]]
+
+        def dense_step(k, evs):
+            s_ = sets[k % len(dense_w)]
+            Wd = dense_w[k % len(dense_w)]
+            torch.matmul(s_["X"], Wd.t(), out=s_["Y"])
+            if "dx" in w.ops:
+                torch.matmul(s_["dY"], Wd, out=s_["dX"])
+            if "dw" in w.ops:
+                torch.matmul(s_["dY"].t(), s_["X"])
+        for k in range(3):
+            dense_step(k, None)
+        h_ms, _ = time_graph_steps(dense_step, len(dense_w), max(10, nsteps // 2))
+        res["hipblaslt_dense_context"] = {"ms_per_step": h_ms, "speedup_of_sparse": h_ms / step_ms,
+                                          "dense_tflops": nops * 2.0 * w.M * w.N * w.K / (h_ms * 1e-3) / 1e12}
+        del dense_w
+    del sets, ws
+    p.close()
+    return res
+
+
+def cpu_baseline(w, host, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload (the first rows of
+    X and dY, the whole pattern) on the host's cores: each op gets about seconds / ops of wall
+    time. Threads: the cores this process may run on, capped by OMP_NUM_THREADS when set."""
+    import oracle
+    from oracle import meta
+    threads = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        threads = min(threads, int(env))
+    oracle.set_threads(threads)
+    md = meta.scan(host["mask"])
+    nnzb = md["nnzb"]
+    F_row = 2.0 * w.b * w.b * nnzb        # useful flops per activation row and op
+    X64 = oracle._f64(host["X"])
+    dY64 = oracle._f64(host["dY"]) if host.get("dY") is not None else None
+    budget = seconds / len(w.ops)
+    ops = {}
+    tot_f = tot_t = 0.0
+    for op in w.ops:
+        probe = min(w.M, 32)
+        t = time.perf_counter()
+        _run_oracle(w, md, host, X64, dY64, probe, op)
+        per_row = max(1e-6, (time.perf_counter() - t) / probe)
+        rows = int(min(w.M, max(probe, budget / per_row)))
+        reps = max(1, int(round(budget / (per_row * rows)))) if rows == w.M else 1
+        t = time.perf_counter()
+        for _ in range(reps):
+            _run_oracle(w, md, host, X64, dY64, rows, op)
+        dt = time.perf_counter() - t
+        f = F_row * rows * reps
+        ops[op] = {"rows": rows, "reps": reps, "wall_s": dt, "gflops": f / dt / 1e9,
+                   "ms_full_workload": dt / (rows * reps) * w.M * 1e3}
+        tot_f += f
+        tot_t += dt
+    return {"value": tot_f / tot_t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": (f"the first rows of {w.M} (per op: " +
+                       ", ".join(f"{o} {v['rows']} rows x {v['reps']}" for o, v in ops.items()) +
+                       f") of the workload with its whole pattern, fp64, no tolerance sums, {tot_t:.1f} s wall"),
+            "ops": ops, "cpu_model": cpu_model(), "seconds": tot_t}
+
+
+def _run_oracle(w, md, host, X64, dY64, rows, op):
+    import oracle
+    if op == "fwd":
+        oracle.fwd(X64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.N, w.b, bias=host["bias"], want_s=False)
+    elif op == "dx":
+        oracle.dx(dY64[:rows], md["row_ptr"], md["col_idx"], host["V"], w.K, w.b, want_s=False)
+    elif op == "dw":
+        oracle.dw(dY64[:rows], X64[:rows], md["row_ptr"], md["col_idx"], w.b, want_s=False)
 
 
 CONVERT_WORKLOAD = 5   # the largest weight of the reference workloads: 11008 x 4096, Zipf rows
@@ -597,17 +774,23 @@ def rebuild_leg(dev, reps: int) -> dict:
     return {"grid": f"{R}x{C}", "nnzb": int(out["nnzb"].item()), "us_per_rebuild": ms * 1e3, "kernels": 6}
 
 
+HEADLINE_WORKLOAD = 5   # the largest configuration: 16384 x 4096 -> 11008, Zipf rows, fwd + dX + dW
+OTHER_WORKLOADS = (2, 3, 4)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="reference workload 1..5 (default 2)")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=HEADLINE_WORKLOAD,
+                    help=f"reference workload 1..5 of the headline line (default {HEADLINE_WORKLOAD})")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the density-1.0 and hipBLASLt legs")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline workload: no density-1.0, hipBLASLt, other-workload or NEXT legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help=f"also run one plain {COPY_BYTES}-byte device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -631,129 +814,66 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this build has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
-    import numpy as np
     import torch
-    from sparse_gemm_amd import binding, synth
+    from sparse_gemm_amd import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}; generating inputs")
-    host = synth.make_inputs(w, args.seed)
-    nnzb = int(host["mask"].sum())
-    p = binding.Pattern.from_mask(host["mask"], w.N, w.K, w.b)
-    F = 2.0 * w.M * w.b * w.b * nnzb
-    set_bytes = sum(op_bytes(w, nnzb, op, w.bias) for op in w.ops)
-    nsets = 1 if args.warm else max(1, -(-ROTATE_BYTES // max(1, set_bytes)))
-    sets = build_sets(w, host, nsets, dev)
-    ws_bytes = binding.bwd_weight_workspace_bytes(p, w.M) if "dw" in w.ops else 0
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
-    log(f"[bench] nnzb {nnzb}, {nsets} buffer set(s), timing {args.steps} steps after {args.warmup} warmup")
     global _CYC_PER_MS
     _CYC_PER_MS = _sleep_cycles_per_ms()
-    run = make_runner(p, w, sets, ws)
-    gpu_step_ms, op_ms, enq = time_ops(run, args.steps, args.warmup, w.ops, hold_ms=50.0 + 2.0 * args.steps)
-    reps = max(1, -(-args.steps // nsets))
-    step_ms, wall_ms, nsteps_graph = time_graph(run, nsets, reps)
-    log(f"[bench] graph step {step_ms * 1e3:.1f} us (wall {wall_ms * 1e3:.1f} us); eager GPU step "
-        f"{gpu_step_ms * 1e3:.1f} us; " + ", ".join(f"{o} {t * 1e3:.1f} us" for o, t in op_ms.items()))
+    extras = not args.no_extras
 
-    nops = len(w.ops)
-    value = nops * F / (step_ms * 1e-3) / 1e12
-    per_op = {}
-    for op in w.ops:
-        t = op_ms[op] * 1e-3
-        by = op_bytes(w, nnzb, op, w.bias)
-        t_roof = max(F / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
-        per_op[op] = {"us": op_ms[op] * 1e3, "tflops": F / t / 1e12, "pct_mfma_peak": 100 * F / t / 1e12 / PEAK_BF16_TFLOPS,
-                      "gbs": by / t / 1e9, "pct_hbm_peak": 100 * by / t / 1e9 / PEAK_HBM_GBS, "bytes": by,
-                      "pct_roofline": 100 * t_roof / t}
-        if op in _OP_PERCENTILES_MS:
-            p10, p50, p90 = _OP_PERCENTILES_MS[op]
-            per_op[op].update({"p10_us": p10 * 1e3, "median_us": p50 * 1e3, "p90_us": p90 * 1e3})
-    dom = max(w.ops, key=lambda o: op_ms[o])
-    dom_bytes = op_bytes(w, nnzb, dom, w.bias)
-    # the dominant op's launch duration: back-to-back launches over the rotated sets, one event pair
-    # (events around every call inside the step also hold the dispatch of the op's first kernel)
-    one_op = make_runner(p, w, sets, ws, only=dom)
-    t_dom = time_launches(lambda k: one_op(k, None), nsets, max(20, args.steps))
-    log(f"[bench] {dom} back to back: {t_dom * 1e3:.1f} us per launch")
-    t_dom *= 1e-3
-    ai = F / dom_bytes
-    if ai < RIDGE:
-        roofline = {"bound": "hbm", "achieved": dom_bytes / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] headline workload {w.name}; generating inputs")
+    host = synth.make_inputs(w, args.seed)
+    head = measure(w, host, dev, args.steps, args.warmup, args.warm, extras, "headline")
+    small = "dx" not in w.ops and "dw" not in w.ops and w.M <= 64
+    if small:
+        # memory-bound decode shape: the metric is HBM GB/s of the forward
+        by = op_bytes(w, head["nnzb"], "fwd", w.bias)
+        value, unit = by / (head["ms_per_step"] * 1e-3) / 1e9, "GB/s"
     else:
-        roofline = {"bound": "mfma", "achieved": F / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    tr = read_traffic(w.name)
-    roofline["traffic"] = tr.get(dom) if tr else None
-    roofline["kernel"] = {"fwd": "bsr_linear_fwd", "dx": "bsr_linear_bwd_input", "dw": "bsr_linear_bwd_weight"}[dom]
-    roofline["per_launch"] = {"flops": F, "algorithmic_bytes": dom_bytes, "avg_us": t_dom * 1e6,
-                              "avg_us_in_step": op_ms[dom] * 1e3, "kernels": list(OP_KERNELS[dom]),
-                              "timing": "back-to-back launches over the rotated buffer sets, HIP events on the "
-                                        "launch stream, queue pre-filled behind a spin kernel"}
+        value, unit = head["tflops"], "TFLOP/s"
+    out = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) activations and output gradients, N(0,0.02) blocks)",
+           "config": {k: head[k] for k in ("workload", "M", "K", "N", "block", "density", "nnzb", "pattern", "ops",
+                                           "buffers", "rotated_bytes", "pattern_sha256", "rows")},
+           "pct_bf16_mfma_peak": head["pct_bf16_mfma_peak"],
+           "ops": head["ops"], "roofline": head["roofline"], "timing": head["timing"],
+           "warm_ms_per_step": head.get("warm_ms_per_step")}
+    for k in ("density_1.0_same_kernels", "hipblaslt_dense_context"):
+        if k in head:
+            out[k] = head[k]
 
-    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": nsteps_graph,
-           "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations, N(0,0.02) blocks)",
-           "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.b, "density": w.density,
-                      "nnzb": nnzb, "pattern": w.pattern, "ops": "+".join(w.ops),
-                      "buffers": (f"cold ({nsets} rotated sets)" if nsets > 1 else
-                                  "cold (one set, each step touches more than the rotation size)"
-                                  if not args.warm else "warm (1 set)"),
-                      "pattern_sha256": synth.mask_digest(host["mask"]), "rows": synth.row_histogram(host["mask"])},
-           "pct_bf16_mfma_peak": 100 * value / PEAK_BF16_TFLOPS,
-           "ops": per_op, "roofline": roofline,
-           "timing": {"ms_per_step": "HIP-graph replay of the step over the rotated buffer sets, HIP events",
-                      "graph_wall_ms_per_step": wall_ms, "eager_gpu_ms_per_step": gpu_step_ms,
-                      "eager_host_enqueue_ms_per_step": enq * 1e3 / args.steps,
-                      "ops": "HIP events around each call, host queue pre-filled behind a spin kernel"}}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    del host
 
-    # the same step with one buffer set (cache-warm), for reference
-    warm_ms, _, _ = time_graph(make_runner(p, w, sets[:1], ws), 1, max(5, args.steps))
-    out["warm_ms_per_step"] = warm_ms
-
-    if not args.no_extras:
-        # the same kernels on the density-1.0 pattern of the same shape, same buffer rotation
-        full = np.ones_like(host["mask"])
-        host_d = dict(host)
-        host_d["mask"] = full
-        host_d["V"] = synth.block_values(int(full.sum()), w.b, args.seed)
-        pd = binding.Pattern.from_mask(full, w.N, w.K, w.b)
-        bytes_d = sum(op_bytes(w, int(full.sum()), op, w.bias) for op in w.ops)
-        nsets_d = 1 if args.warm else max(1, -(-ROTATE_BYTES // bytes_d))
-        del sets
-        sets_d = build_sets(w, host_d, nsets_d, dev)
-        wsd_b = binding.bwd_weight_workspace_bytes(pd, w.M) if "dw" in w.ops else 0
-        wsd = torch.empty((wsd_b,), dtype=torch.uint8, device=dev) if wsd_b else None
-        run_d = make_runner(pd, w, sets_d, wsd)
-        _, d_ops, _ = time_ops(run_d, max(10, args.steps // 2), 3, w.ops, hold_ms=60.0)
-        d_ms, _, _ = time_graph(run_d, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
-        out["density_1.0_same_kernels"] = {"ms_per_step": d_ms, "speedup_of_sparse": d_ms / step_ms,
-                                           "ops_us": {o: t * 1e3 for o, t in d_ops.items()},
-                                           "buffers": f"{nsets_d} rotated sets" if nsets_d > 1 else "warm"}
-
-        # hipBLASLt dense GEMMs of the same shapes (torch.matmul; context only)
-        dense_w = [s_["V"].new_empty((w.N, w.K)).normal_() for s_ in sets_d]
-
-        def dense_step(k, evs):
-            s_ = sets_d[k % len(sets_d)]
-            Wd = dense_w[k % len(sets_d)]
-            torch.matmul(s_["X"], Wd.t(), out=s_["Y"])
-            if "dx" in w.ops:
-                torch.matmul(s_["dY"], Wd, out=s_["dX"])
-            if "dw" in w.ops:
-                torch.matmul(s_["dY"].t(), s_["X"])
-        for k in range(3):
-            dense_step(k, None)
-        h_ms, _, _ = time_graph(dense_step, nsets_d, max(2, -(-max(10, args.steps // 2) // nsets_d)))
-        out["hipblaslt_dense_context"] = {"ms_per_step": h_ms, "speedup_of_sparse": h_ms / step_ms}
-        del sets_d, dense_w, pd
-
+    if extras:
+        out["other_workloads"] = {}
+        for k in OTHER_WORKLOADS:
+            if k == args.workload:
+                continue
+            wk = synth.WORKLOADS[k]
+            log(f"[bench] workload {wk.name}; generating inputs")
+            hk = synth.make_inputs(wk, args.seed)
+            r = measure(wk, hk, dev, args.steps, args.warmup, args.warm, True, f"workload {k}")
+            if "dx" not in wk.ops:
+                by = op_bytes(wk, r["nnzb"], "fwd", wk.bias)
+                r["gbs_per_step"] = by / (r["ms_per_step"] * 1e-3) / 1e9
+                r["pct_hbm_peak_per_step"] = 100 * r["gbs_per_step"] / PEAK_HBM_GBS
+            out["other_workloads"][wk.name] = r
+            del hk
         log("[bench] dense <-> BSR conversion kernels")
         out["next_rows"] = {"convert": convert_leg(dev, max(20, args.steps))}
         log("[bench] fp8 block values, decode forward")
@@ -773,10 +893,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on the host cores")
-        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -43,9 +43,10 @@
  *     several streams at once. The pattern's device metadata lives on the device that
  *     was current at creation; compute calls must run with that device current.
  *   - No C++ exception crosses this interface.
- *   - Size limits (32-bit buffer offsets in the kernels; BSR_ERR_INVALID_ARG beyond them):
- *     V below 4 GiB; 256 rows of X (forward) or dY (input gradient) below 4 GiB; for the
- *     weight gradient (M + 32) rows of dY and of X each below 4 GiB.
+ *   - Size limits (BSR_ERR_INVALID_ARG beyond them): at most 2^23 - 1 kept blocks per
+ *     pattern (checked at creation); 32-bit buffer offsets in the kernels: V below 4 GiB,
+ *     256 rows of X (forward) or dY (input gradient) below 4 GiB, and for the weight
+ *     gradient (M + 32) rows of dY and of X each below 4 GiB.
  */
 #ifndef BSR_LINEAR_H
 #define BSR_LINEAR_H
@@ -92,24 +93,33 @@ int32_t bsr_abi_version(void);
 int32_t bsr_pattern_create_from_mask(int32_t N, int32_t K, int32_t b, const uint8_t *mask,
                                      int32_t upload, bsr_pattern **out);
 
-/* Build a pattern from host CSR arrays (restore of a saved pattern). row_ptr[N/b+1] must
- * start at 0, be non-decreasing and end at nnzb; col_idx[nnzb] must lie in [0, K/b) and
- * be strictly increasing inside each row (BSR_ERR_INVALID_ARG otherwise). */
+/* Build a pattern from host CSR arrays: the index pointer and block indices of the BSR
+ * format (pytorch/ao sparsity README, Table 4.1), e.g. to restore a saved pattern, which
+ * stays fixed once chosen (pytorch_block_sparse summary page, "Future Development
+ * Roadmap"). row_ptr[N/b+1] must start at 0, be non-decreasing and end at nnzb;
+ * col_idx[nnzb] must lie in [0, K/b) and be strictly increasing inside each row
+ * (BSR_ERR_INVALID_ARG otherwise). */
 int32_t bsr_pattern_create_from_csr(int32_t N, int32_t K, int32_t b, int32_t nnzb,
                                     const int32_t *row_ptr, const int32_t *col_idx,
                                     int32_t upload, bsr_pattern **out);
 
-/* Shape of a pattern; any output pointer may be NULL. */
+/* Shape of a pattern (the weight's N x K, the block size b and the number of kept blocks
+ * of the BSR format, pytorch/ao sparsity README, Table 4.1); any output pointer may be
+ * NULL. Host only, no device access. */
 int32_t bsr_pattern_info(const bsr_pattern *p, int32_t *N, int32_t *K, int32_t *b,
                          int32_t *nnzb);
 
 /* Copy the metadata to caller-owned host arrays sized row_ptr[R+1], col_idx[nnzb],
- * col_ptr[C+1], row_idx[nnzb], perm[nnzb]. Any pointer may be NULL (skipped). */
+ * col_ptr[C+1], row_idx[nnzb], perm[nnzb]: the CSR index pointer and indices and their
+ * transposed (CSC) form (pytorch/ao sparsity README, Table 4.1), with perm mapping CSC
+ * order to CSR positions. Any pointer may be NULL (skipped). Host only. */
 int32_t bsr_pattern_export(const bsr_pattern *p, int32_t *row_ptr, int32_t *col_idx,
                            int32_t *col_ptr, int32_t *row_idx, int32_t *perm);
 
-/* Release a pattern and its device metadata. The caller guarantees that no enqueued
- * work still uses it (for example by synchronising the streams it was used on).
+/* Release a pattern (the fixed block pattern of one layer, pytorch_block_sparse summary
+ * page, "Future Development Roadmap") and its device metadata. The caller guarantees
+ * that no enqueued work still uses it (for example by synchronising the streams it was
+ * used on).
  * NULL is ignored. */
 void bsr_pattern_destroy(bsr_pattern *p);
 
@@ -150,7 +160,8 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
                               int64_t M, bsr_bf16 *dV, bsr_bf16 *dbias, void *workspace,
                               size_t ws_bytes, void *stream);
 
-/* Static name of a status code ("BSR_OK", ...). */
+/* Static name of a status code ("BSR_OK", ...) of the calls above; the codes are this
+ * library's own (the pages define no error interface). */
 const char *bsr_status_string(int32_t status);
 
 /* Detail of the last error on the calling thread ("" if none). Valid until the next call

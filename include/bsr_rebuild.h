@@ -48,15 +48,22 @@ int32_t bsr_meta_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row
  * values V[...] in that order (the contract of bsr_linear_fwd). The work-groups take the block rows
  * in natural order (the host-built pattern deals them heaviest first).
  *   N, K, b   as for a pattern (b = 32 or 64, N and K positive multiples of b).
- *   row_ptr   device int32 [N/b + 1], col_idx device int32 [row_ptr[N/b]]: canonical CSR (columns
- *             ascending and in range inside each row); not validated on the host, since they live
- *             on the device: malformed metadata is the caller's error.
- *   X [M][K], V [row_ptr[N/b]][b][b], bias [N] or NULL, Y [M][N]: bf16 device buffers, 16-byte
- *             aligned; 1 <= M <= 16 (M = 0 is a no-op); the values below 4 GiB.
+ *   row_ptr   device int32 [N/b + 1]: canonical CSR (non-decreasing, starting at 0).
+ *   col_idx   device int32 [cap]: block columns, ascending and in range inside each row.
+ *   cap       the number of blocks col_idx and V hold (>= 0). Block positions at or past cap are
+ *             dropped: a row keeps only its blocks below cap. This is the truncation
+ *             bsr_meta_rebuild applies when a mask holds more than its capacity (its row_ptr is
+ *             written in full, its col_idx only below cap), so a grown mask never makes this call
+ *             read past col_idx or V. Pass bsr_meta_rebuild's cap; compare its nnzb output with
+ *             cap to detect the truncation.
+ *   The metadata is not validated on the host, since it lives on the device: malformed
+ *   metadata is the caller's error, but loads stay inside X, V (cap blocks) and col_idx.
+ *   X [M][K], V [cap][b][b], bias [N] or NULL, Y [M][N]: bf16 device buffers, 16-byte aligned;
+ *             1 <= M <= 16 (M = 0 is a no-op); cap * b * b values below 4 GiB.
  * Every element of Y is written. */
 int32_t bsr_linear_fwd_small_m_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr,
-                                   const int32_t *col_idx, const bsr_bf16 *X, int64_t M, const bsr_bf16 *V,
-                                   const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
+                                   const int32_t *col_idx, int32_t cap, const bsr_bf16 *X, int64_t M,
+                                   const bsr_bf16 *V, const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,7 @@ def lib():
                   L.oracle_dequantize_fp8, L.oracle_compress_24, L.oracle_decompress_24):
             f.restype = None
         L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes, L.oracle_set_threads.restype = [ctypes.c_int], None
         _lib = L
     return _lib
 
@@ -204,6 +205,11 @@ def decompress_24(Vc, meta_) -> np.ndarray:
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the OpenMP loops (results are the same for any count)."""
+    lib().oracle_set_threads(int(n))
 
 
 def tolerance_check(g, ref: np.ndarray, S: np.ndarray, tol: float = TOL) -> dict:

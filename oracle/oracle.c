@@ -338,3 +338,15 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the number of threads of the loops above (no effect without OpenMP). Only
+ * independent outputs are split over threads, so results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

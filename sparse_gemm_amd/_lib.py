@@ -79,7 +79,7 @@ def load() -> ctypes.CDLL:
     L.bsr_linear_fwd_24_image.argtypes = [P, P, i64, P, P, P, P]
     L.bsr_meta_rebuild_workspace.argtypes, L.bsr_meta_rebuild_workspace.restype = [i32, i32], sz
     L.bsr_meta_rebuild.argtypes = [i32, i32, P, P, P, P, P, P, i32, P, P, sz, P]
-    L.bsr_linear_fwd_small_m_csr.argtypes = [i32, i32, i32, P, P, P, i64, P, P, P, P]
+    L.bsr_linear_fwd_small_m_csr.argtypes = [i32, i32, i32, P, P, i32, P, i64, P, P, P, P]
     for f in ("bsr_pattern_create_from_mask", "bsr_pattern_create_from_csr", "bsr_pattern_info",
               "bsr_pattern_export", "bsr_linear_fwd", "bsr_linear_bwd_input", "bsr_linear_bwd_weight",
               "bsr_block_norms", "bsr_mask_topk", "bsr_pattern_create_from_dense", "bsr_dense_to_values",

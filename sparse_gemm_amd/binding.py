@@ -445,18 +445,22 @@ def linear_fwd_small_m_csr(N: int, K: int, b: int, row_ptr: torch.Tensor, col_id
                            V: torch.Tensor, bias: Optional[torch.Tensor] = None,
                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = X . W~^T + bias for M <= 16 rows from device CSR metadata (e.g. meta_rebuild's), via
-    bsr_linear_fwd_small_m_csr; V holds row_ptr[-1] blocks (any larger leading size is allowed)."""
+    bsr_linear_fwd_small_m_csr. The capacity passed is min(len(col_idx), len(V)): blocks at CSR
+    positions at or past it are dropped (the truncation of a mask rebuilt past its capacity)."""
     M = X.shape[0]
     d = X.device.index
     _check_tensor(X, "X", (M, K), d)
     if V.dtype != torch.bfloat16 or not V.is_contiguous() or V.shape[1:] != (b, b):
         raise ValueError("V must be a contiguous bf16 [n, b, b] tensor")
+    if col_idx.dtype != torch.int32 or row_ptr.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    cap = min(int(col_idx.numel()), int(V.shape[0]))
     if bias is not None:
         _check_tensor(bias, "bias", (N,), d)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     _check_tensor(out, "out", (M, N), d)
-    _lib.check(lib().bsr_linear_fwd_small_m_csr(N, K, b, _ptr(row_ptr), _ptr(col_idx), _ptr(X), M, _ptr(V),
+    _lib.check(lib().bsr_linear_fwd_small_m_csr(N, K, b, _ptr(row_ptr), _ptr(col_idx), cap, _ptr(X), M, _ptr(V),
                                                 _ptr(bias), _ptr(out), torch.cuda.current_stream(d).cuda_stream),
                "bsr_linear_fwd_small_m_csr")
     return out

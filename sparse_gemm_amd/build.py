@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbsr_linear.so")
 ARCH = "gfx950"
 
-SOURCES = ["bsr_abi.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip", "bsr_rebuild.hip"]
+SOURCES = ["bsr_abi.cpp", "bsr_error.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip", "bsr_rebuild.hip"]
 
 # Packed-fp32 instructions are kept out of the generated code on purpose; the host pass
 # prints a harmless "not a recognized feature" warning for this flag.
@@ -35,10 +35,11 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; always rebuilds."""
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc()] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -50,7 +51,11 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"compile of {src} failed:\n" + "\n".join(noise))
         if noise and verbose:
             print("\n".join(noise), file=sys.stderr)
-        objs.append(obj)
+        return obj
+
+    jobs = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 8))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

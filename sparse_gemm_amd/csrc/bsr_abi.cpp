@@ -17,7 +17,6 @@
 namespace bsr {
 
 namespace {
-thread_local std::string g_last_error;
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -80,6 +79,10 @@ int32_t upload(bsr_pattern &p) {
 }
 
 int32_t finish_create(bsr_pattern *p, int32_t upload_flag, bsr_pattern **out) {
+    if (p->nnzb > kMaxNnzb) {
+        delete p;
+        return fail(BSR_ERR_INVALID_ARG, "more than " + std::to_string(kMaxNnzb) + " kept blocks");
+    }
     try {
         build_pattern(*p);
     } catch (const std::bad_alloc &) {
@@ -119,11 +122,6 @@ int32_t check_ptr(const void *ptr, const char *name, bool nullable = false) {
 
 }  // namespace
 
-int32_t fail(int32_t status, const std::string &msg) {
-    g_last_error = msg;
-    return status;
-}
-
 }  // namespace bsr
 
 using namespace bsr;
@@ -161,12 +159,7 @@ int32_t bsr_pattern_create_from_mask(int32_t N, int32_t K, int32_t b, const uint
     p->b = b;
     p->R = N / b;
     p->C = K / b;
-    p->row_ptr.assign(p->R + 1, 0);
-    for (int32_t r = 0; r < p->R; ++r) {
-        for (int32_t c = 0; c < p->C; ++c)
-            if (mask[(size_t)r * p->C + c]) p->col_idx.push_back(c);
-        p->row_ptr[r + 1] = (int32_t)p->col_idx.size();
-    }
+    csr_from_mask(p->R, p->C, mask, p->row_ptr, p->col_idx);
     p->nnzb = (int32_t)p->col_idx.size();
     return finish_create(p, upload_flag, out);
     BSR_TRY_END
@@ -179,20 +172,7 @@ int32_t bsr_pattern_create_from_csr(int32_t N, int32_t K, int32_t b, int32_t nnz
     *out = nullptr;
     BSR_CHECK(check_shape(N, K, b));
     const int32_t R = N / b, C = K / b;
-    if (nnzb < 0 || (int64_t)nnzb > (int64_t)R * C) return fail(BSR_ERR_INVALID_ARG, "nnzb out of range");
-    if (!row_ptr) return fail(BSR_ERR_INVALID_ARG, "row_ptr is NULL");
-    if (nnzb > 0 && !col_idx) return fail(BSR_ERR_INVALID_ARG, "col_idx is NULL");
-    if (row_ptr[0] != 0) return fail(BSR_ERR_INVALID_ARG, "row_ptr[0] must be 0");
-    if (row_ptr[R] != nnzb) return fail(BSR_ERR_INVALID_ARG, "row_ptr[R] must equal nnzb");
-    for (int32_t r = 0; r < R; ++r) {
-        if (row_ptr[r + 1] < row_ptr[r]) return fail(BSR_ERR_INVALID_ARG, "row_ptr must be non-decreasing");
-        if (row_ptr[r + 1] > nnzb) return fail(BSR_ERR_INVALID_ARG, "row_ptr exceeds nnzb");
-        for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
-            if (col_idx[i] < 0 || col_idx[i] >= C) return fail(BSR_ERR_INVALID_ARG, "col_idx out of range");
-            if (i > row_ptr[r] && col_idx[i] <= col_idx[i - 1])
-                return fail(BSR_ERR_INVALID_ARG, "col_idx must be strictly increasing inside a row");
-        }
-    }
+    if (const char *why = check_csr(R, C, nnzb, row_ptr, col_idx)) return fail(BSR_ERR_INVALID_ARG, why);
     auto *p = new bsr_pattern();
     p->N = N;
     p->K = K;
@@ -498,11 +478,13 @@ int32_t bsr_linear_fwd_24_image(const bsr_pattern *p, const bsr_bf16 *X, int64_t
 }
 
 int32_t bsr_linear_fwd_small_m_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
-                                   const bsr_bf16 *X, int64_t M, const bsr_bf16 *V, const bsr_bf16 *bias, bsr_bf16 *Y,
-                                   void *stream) {
+                                   int32_t cap, const bsr_bf16 *X, int64_t M, const bsr_bf16 *V, const bsr_bf16 *bias,
+                                   bsr_bf16 *Y, void *stream) {
     BSR_TRY_BEGIN
     BSR_CHECK(check_shape(N, K, b));
     if (M < 0 || M > kSmallM) return fail(BSR_ERR_INVALID_ARG, "M must lie in [0, 16]");
+    if (cap < 0) return fail(BSR_ERR_INVALID_ARG, "cap must be >= 0");
+    if ((size_t)cap * b * b * 2 > (size_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "cap * b * b values above 4 GiB");
     if (!row_ptr || !col_idx || ((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u))
         return fail(BSR_ERR_INVALID_ARG, "row_ptr and col_idx must be 4-byte aligned device pointers");
     BSR_CHECK(check_ptr(X, "X", M == 0));
@@ -512,7 +494,7 @@ int32_t bsr_linear_fwd_small_m_csr(int32_t N, int32_t K, int32_t b, const int32_
     if (M == 0) return BSR_OK;
     if (!V) return fail(BSR_ERR_INVALID_ARG, "V is NULL");
     FwdArgs a{X, M, K, V, bias, Y, N};
-    return launch_small_m_fwd_csr(N, K, b, row_ptr, col_idx, a, stream);
+    return launch_small_m_fwd_csr(N, K, b, row_ptr, col_idx, cap, a, stream);
     BSR_TRY_END
 }
 
@@ -557,6 +539,6 @@ const char *bsr_status_string(int32_t status) {
     }
 }
 
-const char *bsr_last_error(void) { return g_last_error.c_str(); }
+const char *bsr_last_error(void) { return last_error(); }
 
 }  // extern "C"

@@ -104,11 +104,26 @@ struct bsr_pattern {
 
 namespace bsr {
 
-// Builds CSR-derived metadata and schedules from validated CSR arrays.
+// Most kept blocks a pattern may hold: the weight-gradient work items pack a block's CSR
+// position into the upper 23 bits of an int32 (position << 8 | tile coordinates).
+constexpr int32_t kMaxNnzb = (1 << 23) - 1;
+
+// Builds CSR-derived metadata and schedules from validated CSR arrays (nnzb <= kMaxNnzb).
 void build_pattern(bsr_pattern &p);
 
-// Records an error message for the calling thread and returns `status`.
+// Canonical CSR of a row-major R x C block mask (nonzero = kept).
+void csr_from_mask(int32_t R, int32_t C, const uint8_t *mask, std::vector<int32_t> &row_ptr,
+                   std::vector<int32_t> &col_idx);
+
+// Checks host CSR arrays of an R x C block grid: nullptr when they are canonical (row_ptr starts
+// at 0, is non-decreasing and ends at nnzb; columns in range and strictly increasing in a row),
+// else a static description of the first defect.
+const char *check_csr(int32_t R, int32_t C, int32_t nnzb, const int32_t *row_ptr, const int32_t *col_idx);
+
+// Records an error message for the calling thread and returns `status` (bsr_error.cpp).
 int32_t fail(int32_t status, const std::string &msg);
+// The calling thread's last message ("" if none).
+const char *last_error();
 
 // ---- kernel launchers (bsr_kernels.hip). All return a bsr_status. ----
 struct FwdArgs {

@@ -500,14 +500,16 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
 //   slice s:  A[p][k] = V[i][s*16 + p][k]   B[k][m] = X[m][c*BS + k]   (m < 16; rows past M are 0)
 // ------------------------------------------------------------------------------------------
 // ROWPTR: `rows` is a CSR row pointer (block row r = work-group / PARTS, blocks row_ptr[r] ..
-// row_ptr[r+1]) instead of the host-built list; used with metadata rebuilt on the device.
+// row_ptr[r+1]) instead of the host-built list; used with metadata rebuilt on the device. Block
+// positions are clamped to `cap` (the blocks col_idx and V hold), so a row pointer whose total
+// exceeds them never reads past either array.
 // WORK: `rows` is the balanced work list, one entry per work-group {row, first, end, first slice |
 // slices << 8} with 1 or 2 slices (PSW = 2).
 template <int BS, int NW, int U, int PSW, bool PIPE = false, bool ROWPTR = false, bool WORK = false, int MT = 1>
 __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict__ X, int K, int M,
                                                      const uint16_t *__restrict__ V, const uint16_t *__restrict__ bias,
                                                      uint16_t *__restrict__ Y, int N, const int32_t *__restrict__ col_idx,
-                                                     const int32_t *__restrict__ rows) {
+                                                     const int32_t *__restrict__ rows, int cap = 0) {
     constexpr int PS = PSW;       // 16-row slices of each block handled by this work-group
     constexpr int KC = BS / 32;   // 32-deep k chunks per block
     constexpr int PARTS = BS / 16 / PSW;
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
     int4 e;
     if constexpr (ROWPTR) {
         const int rr = (int)(blockIdx.x / PARTS);
-        e = int4{rr, rows[rr], rows[rr + 1], 0};
+        e = int4{rr, min(rows[rr], cap), min(rows[rr + 1], cap), 0};
     } else if constexpr (WORK) {
         e = reinterpret_cast<const int4 *>(rows)[blockIdx.x];
     } else {
@@ -563,13 +565,14 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // blocks past the row's end read zeros for both operands (a zero block times a
-            // non-finite activation would not be zero)
+            // non-finite activation would not be zero). The block column rides in the
+            // range-checked voffset, so no column index makes the load leave the activations.
             const uint32_t xo = ib + u < i1 ? xoff : xend;
 #pragma unroll
             for (int t = 0; t < MT; ++t)
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc)
-                    b[u][t][kc] = buf_load16(rx, xo + (uint32_t)t * 16u * (uint32_t)K * 2u + kc * 64, (uint32_t)col[u] * BS * 2);
+                    b[u][t][kc] = buf_load16(rx, xo + (uint32_t)t * 16u * (uint32_t)K * 2u + kc * 64 + (uint32_t)col[u] * BS * 2, 0);
         }
     };
     auto compute_pass = [&](const bf16x8 (&a)[U][PS][KC], const bf16x8 (&b)[U][MT][KC]) __attribute__((always_inline)) {
@@ -1012,14 +1015,14 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
 }
 
 template <int BS>
-void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_ptr, const int32_t *col_idx,
+void launch_small_m_rowptr(int32_t R, int32_t N, int32_t K, const int32_t *row_ptr, const int32_t *col_idx, int32_t cap,
                            const FwdArgs &a, hipStream_t st) {
     // the configurations of the host-scheduled forward, in natural row order
     constexpr int NW = 8, U = BS == 32 ? 8 : 1, PSW = 2;
     constexpr bool PIPE = BS == 64;
     const dim3 grid((unsigned)(R * (BS / 16 / PSW)), (unsigned)((a.M + 15) / 16));
     hipLaunchKernelGGL((k_small_m<BS, NW, U, PSW, PIPE, true>), grid, dim3(NW * 64), 0, st, a.act, K, (int)a.M, a.V,
-                       a.bias, a.out, N, col_idx, row_ptr);
+                       a.bias, a.out, N, col_idx, row_ptr, cap);
 }
 
 template <int BS, int NW, int U, bool PIPE, int MT = 1>
@@ -1077,10 +1080,10 @@ int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream)
 }
 
 int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
-                               const FwdArgs &a, void *stream) {
+                               int32_t cap, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
-    if (b == 32) launch_small_m_rowptr<32>(N / b, N, K, row_ptr, col_idx, a, st);
-    else launch_small_m_rowptr<64>(N / b, N, K, row_ptr, col_idx, a, st);
+    if (b == 32) launch_small_m_rowptr<32>(N / b, N, K, row_ptr, col_idx, cap, a, st);
+    else launch_small_m_rowptr<64>(N / b, N, K, row_ptr, col_idx, cap, a, st);
     return launched("fwd small-M (device CSR) launch");
 }
 

@@ -205,6 +205,34 @@ static std::vector<int32_t> small_m_work_list(const bsr_pattern &p) {
     return out;
 }
 
+void csr_from_mask(int32_t R, int32_t C, const uint8_t *mask, std::vector<int32_t> &row_ptr,
+                   std::vector<int32_t> &col_idx) {
+    row_ptr.assign(R + 1, 0);
+    col_idx.clear();
+    for (int32_t r = 0; r < R; ++r) {
+        for (int32_t c = 0; c < C; ++c)
+            if (mask[(size_t)r * C + c]) col_idx.push_back(c);
+        row_ptr[r + 1] = (int32_t)col_idx.size();
+    }
+}
+
+const char *check_csr(int32_t R, int32_t C, int32_t nnzb, const int32_t *row_ptr, const int32_t *col_idx) {
+    if (nnzb < 0 || (int64_t)nnzb > (int64_t)R * C) return "nnzb out of range";
+    if (!row_ptr) return "row_ptr is NULL";
+    if (nnzb > 0 && !col_idx) return "col_idx is NULL";
+    if (row_ptr[0] != 0) return "row_ptr[0] must be 0";
+    if (row_ptr[R] != nnzb) return "row_ptr[R] must equal nnzb";
+    for (int32_t r = 0; r < R; ++r) {
+        if (row_ptr[r + 1] < row_ptr[r]) return "row_ptr must be non-decreasing";
+        if (row_ptr[r + 1] > nnzb) return "row_ptr exceeds nnzb";
+        for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
+            if (col_idx[i] < 0 || col_idx[i] >= C) return "col_idx out of range";
+            if (i > row_ptr[r] && col_idx[i] <= col_idx[i - 1]) return "col_idx must be strictly increasing inside a row";
+        }
+    }
+    return nullptr;
+}
+
 void build_pattern(bsr_pattern &p) {
     build_csc(p);
     for (int k = 0; k < kGemmVariants; ++k) {

@@ -16,6 +16,6 @@ int32_t launch_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row_p
 
 // bsr_kernels.hip: the small-M forward reading a device CSR row pointer in natural row order.
 int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *row_ptr, const int32_t *col_idx,
-                               const FwdArgs &a, void *stream);
+                               int32_t cap, const FwdArgs &a, void *stream);
 
 }  // namespace bsr

@@ -151,6 +151,11 @@ class BlockSparseLinear(nn.Module):
 
     def _load_from_state_dict(self, state_dict, prefix, local_metadata, strict, missing_keys, unexpected_keys,
                               error_msgs):
+        """Loads the pattern (row_ptr, col_idx) with the values. When the saved pattern differs from
+        the module's, the pattern is rebuilt and `values` is resized in place: the Parameter object
+        stays the same, so an optimizer built earlier still updates it, but any per-parameter
+        optimizer state of `values` (momentum, Adam moments) no longer matches its shape and must
+        be reset by the caller."""
         rp, ci = state_dict.get(prefix + "row_ptr"), state_dict.get(prefix + "col_idx")
         if rp is not None and ci is not None:
             rp_np = rp.cpu().numpy().astype(np.int32)
@@ -163,8 +168,9 @@ class BlockSparseLinear(nn.Module):
                                                     ci_np)
                 self.row_ptr = torch.from_numpy(rp_np.copy())
                 self.col_idx = torch.from_numpy(ci_np.copy())
-                self.values = nn.Parameter(torch.empty((self.pattern.nnzb, self.block_size, self.block_size),
-                                                       dtype=torch.bfloat16, device=dev))
+                self.values.data = torch.empty((self.pattern.nnzb, self.block_size, self.block_size),
+                                               dtype=torch.bfloat16, device=dev)
+                self.values.grad = None
         super()._load_from_state_dict(state_dict, prefix, local_metadata, strict, missing_keys, unexpected_keys,
                                       error_msgs)
 

@@ -4,10 +4,13 @@ This module only draws random inputs: block masks and the bf16 tensors X, V
 (block values), bias and dY. It holds none of the layer's arithmetic, so both
 the fp64 oracle (tests) and the HIP path consume exactly the same inputs.
 
-Workload shapes follow the five reference workloads of the block-sparse
-linear layer (pytorch_block_sparse summary page, "Block-Sparse Implementation
-and Usage": a drop-in nn.Linear with a density argument; patterns fixed at
-initialisation, "Future Development Roadmap").
+The five workload shapes (sizes, block sizes, densities, the Zipf row mix) are
+this project's benchmark configurations; the pages fix none of them. What the
+pages do fix is the layer they exercise: a drop-in nn.Linear with a density
+argument whose block pattern is chosen once at initialisation
+(pytorch_block_sparse summary page, "Block-Sparse Implementation and Usage",
+"Future Development Roadmap"), and the random choice of kept blocks (the
+"Random" criterion of the pytorch/ao sparsity README, Table 4.2).
 
 Random streams: one integer seed per workload; stream k of the seed is
 ``numpy.random.default_rng([seed, k])`` with k = 0 pattern, 1 X, 2 V, 3 bias,

@@ -173,3 +173,20 @@ def test_mask_topk_rejects_bad_input():
         binding.mask_topk(np.ones((2, 2)), -1)
     m = binding.mask_topk(np.array([[np.inf, 1.0, np.inf]]), 1)
     assert m.tolist() == [[1, 0, 0]]
+
+
+def test_pattern_size_limit():
+    """A pattern holds at most 2^23 - 1 kept blocks (the weight-gradient work items pack a block's
+    position into 23 bits); one more is refused with BSR_ERR_INVALID_ARG before anything is built."""
+    L = _lib.load()
+    b, C = 32, 128
+    R = (1 << 23) // C                        # R * C = 2^23 blocks
+    mask = np.ones((R, C), dtype=np.uint8)
+    h = ctypes.c_void_p()
+    st = L.bsr_pattern_create_from_mask(R * b, C * b, b, mask.ctypes.data_as(ctypes.c_void_p), 0, ctypes.byref(h))
+    assert st == 1 and not h.value
+    assert "kept blocks" in L.bsr_last_error().decode()
+    mask[0, 0] = 0                            # 2^23 - 1 blocks: accepted (host only)
+    p = Pattern.from_mask(mask, R * b, C * b, b, upload=False)
+    assert p.nnzb == (1 << 23) - 1
+    p.close()

@@ -72,3 +72,33 @@ def test_mfma_summary_arithmetic(tmp_path):
     assert cells[1] == "fwd" and cells[2] == "2"
     assert abs(float(cells[3]) - useful) <= 1e-6 * useful
     assert cells[4] == "1.000" and cells[5] == "25.0%"
+
+
+def test_rotation_counts_distinct_bytes():
+    """Each buffer set holds every tensor of the step once (X, V, dY, Y, dX, dV); the cold rotation
+    must hold at least 512 MiB of distinct buffers, with no set counted twice."""
+    for k, w in synth.WORKLOADS.items():
+        nnzb = int(synth.block_mask(w, 0).sum())
+        one = bench.set_bytes(w, nnzb)
+        b2 = 2 * nnzb * w.b * w.b
+        expect = 2 * w.M * w.K + b2 + 2 * w.M * w.N + (2 * w.N if w.bias else 0)
+        if "dx" in w.ops:
+            expect += 2 * w.M * w.N + 2 * w.M * w.K + b2
+        assert one == expect, k
+        n = bench.rotation_sets(w, nnzb, warm=False)
+        assert n * one >= bench.ROTATE_BYTES and (n - 1) * one < bench.ROTATE_BYTES
+        assert bench.rotation_sets(w, nnzb, warm=True) == 1
+    # BERT-base FFN-up: 65.3 MB per set -> 9 sets (8 would hold 522 MB < 512 MiB = 536.9 MB)
+    w2 = synth.WORKLOADS[2]
+    assert bench.rotation_sets(w2, int(synth.block_mask(w2, 0).sum()), False) == 9
+    # the Zipf layer's one set is already ~1 GB
+    w5 = synth.WORKLOADS[5]
+    assert bench.rotation_sets(w5, int(synth.block_mask(w5, 0).sum()), False) == 1
+
+
+def test_headline_is_the_largest_workload():
+    w = synth.WORKLOADS[bench.HEADLINE_WORKLOAD]
+    flops = {k: 2 * x.M * x.b * x.b * int(synth.block_mask(x, 0).sum()) * len(x.ops)
+             for k, x in synth.WORKLOADS.items()}
+    assert w.name == "zipf_16384x4096x11008_b32_d0.30"
+    assert flops[bench.HEADLINE_WORKLOAD] == max(flops.values())

@@ -71,6 +71,37 @@ def test_every_gemm_variant(monkeypatch, variant, M, N, K, b, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
+@pytest.mark.parametrize("b,M,bad_rows", [(64, 24, (20,)), (64, 57, (40, 56)), (32, 24, (17, 23))])
+def test_nonfinite_activation_small_m_tiles(b, M, bad_rows):
+    """The small-M forward with 2 or 4 activation tiles of 16 rows per work-group: an infinite
+    activation in a row of tile 1, 2 or 3 reaches only that row's outputs of block rows that keep
+    its input block. Rows of other tiles, and block rows whose passes run past their last kept
+    block (those blocks read zeros for both operands), stay finite and match the oracle."""
+    R, C = 6, 4
+    mask = np.ones((R, C), dtype=np.uint8)
+    mask[0::2, 1] = 0             # even block rows skip input block 1
+    mask[3, 2:] = 0               # block row 3 ends early
+    mask[5, :] = 0
+    mask[5, 1] = 1                # block row 5 keeps only block 1
+    host = case_inputs(M, R * b, C * b, b, 22, mask=mask, bias=True, dy=False)
+    say(f"case non-finite activation small-M b={b} M={M} rows={bad_rows}")
+    X = host["X"].clone()
+    for m in bad_rows:
+        X[m, b + 7] = float("inf")   # input block 1
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, R * b, C * b, b)
+    Y = binding.linear_fwd(p, X.to(dev()), host["V"].to(dev()), host["bias"].to(dev())).cpu()
+    torch.cuda.synchronize()
+    ref, S = oracle.fwd(host["X"], md["row_ptr"], md["col_idx"], host["V"], R * b, b, bias=host["bias"])
+    uses = np.repeat(mask[:, 1].astype(bool), b)
+    clean = np.ones((M, R * b), dtype=bool)
+    for m in bad_rows:
+        clean[m, uses] = False
+    assert torch.isfinite(Y[~torch.from_numpy(clean)].float()).sum() == 0
+    check("fwd small-M tiles (untouched)", Y[torch.from_numpy(clean)], ref[clean], S[clean])
+    p.close()
+
+
 @pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
 @pytest.mark.parametrize("M", [9, 300])
 def test_nonfinite_activation_stays_in_its_blocks(monkeypatch, variant, M):

@@ -152,6 +152,32 @@ def test_fwd_small_m_from_rebuilt_csr(M, N, K, b, d, seed):
     p.close()
 
 
+@pytest.mark.parametrize("M,N,K,b,seed", [(8, 512, 512, 64, 110), (16, 1024, 768, 32, 111), (3, 384, 256, 32, 112)])
+def test_fwd_small_m_from_csr_truncated_at_capacity(M, N, K, b, seed):
+    """A mask rebuilt past its capacity: row_ptr is written in full but col_idx only below cap, and V
+    holds cap blocks. The forward keeps each row's blocks below cap and drops the rest (never reading
+    past col_idx or V): it must equal the oracle on the CSR truncated at cap."""
+    say(f"case small-M from device CSR truncated at cap M={M} N={N} K={K} b={b}")
+    import oracle
+    from gpu_util import case_inputs
+    host = case_inputs(M, N, K, b, seed, density=0.6, bias=True, dy=False)
+    mask = host["mask"]
+    md = meta.scan(mask)
+    n = md["nnzb"]
+    cap = n // 2 + 1
+    out = binding.meta_rebuild(torch.from_numpy(mask).to(dev()), cap=cap)
+    assert int(out["nnzb"].item()) == n > cap
+    X, bias = host["X"].to(dev()), host["bias"].to(dev())
+    Vcap = host["V"][:cap].contiguous()
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_small_m_csr(N, K, b, out["row_ptr"], out["col_idx"], X, Vcap.to(dev()), bias, out=Y)
+    torch.cuda.synchronize()
+    rp = np.minimum(md["row_ptr"], cap).astype(np.int32)
+    ref, S = oracle.fwd(host["X"], rp, md["col_idx"][:cap], Vcap, N, b, bias=host["bias"])
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    assert res["violations"] == 0, res
+
+
 def test_changing_mask_to_forward_in_one_captured_graph():
     """A captured graph of [rebuild the metadata of the current mask, forward from it] replayed for
     several masks (mask and block values refreshed by eager copies between replays): every replay
