@@ -160,6 +160,26 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
                               int64_t M, bsr_bf16 *dV, bsr_bf16 *dbias, void *workspace,
                               size_t ws_bytes, void *stream);
 
+/* Bytes of the per-GPU scratch array behind bsr_linear_bwd_weight_noalloc (32 MiB). */
+#define BSR_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Weight gradient exactly as bsr_linear_bwd_weight (same kernels, same result bit for bit), for
+ * callers that cannot allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid allocation. The scratch space (fp32
+ * split-M partial sums of the kept blocks and of the bias) is a fixed array of
+ * BSR_NOALLOC_SCRATCH_BYTES in the library's code object, one per GPU, created when the
+ * library's kernels are loaded on that GPU and held until the process ends; the call makes no
+ * allocation. Limits and sharing:
+ *   - a call whose scratch need (bsr_linear_bwd_weight_workspace(p, M)) exceeds
+ *     BSR_NOALLOC_SCRATCH_BYTES returns BSR_ERR_WORKSPACE_TOO_SMALL and enqueues nothing;
+ *   - every call on one GPU uses that GPU's one array: calls whose work overlaps in time on one
+ *     GPU (several streams, several threads) race and give wrong results; order them on one
+ *     stream or synchronise between them. The array's contents between calls do not matter
+ *     (each call writes every partial it reads).
+ * Arguments and errors as for bsr_linear_bwd_weight. */
+int32_t bsr_linear_bwd_weight_noalloc(const bsr_pattern *p, const bsr_bf16 *dY, const bsr_bf16 *X,
+                                      int64_t M, bsr_bf16 *dV, bsr_bf16 *dbias, void *stream);
+
 /* Static name of a status code ("BSR_OK", ...) of the calls above; the codes are this
  * library's own (the pages define no error interface). */
 const char *bsr_status_string(int32_t status);

@@ -204,6 +204,21 @@ def linear_bwd_weight(p: Pattern, dY: torch.Tensor, X: torch.Tensor, want_dbias:
     return out, dbias
 
 
+def linear_bwd_weight_noalloc(p: Pattern, dY: torch.Tensor, X: torch.Tensor, out: torch.Tensor,
+                              dbias: Optional[torch.Tensor] = None):
+    """dV (and dbias) into caller-provided outputs via bsr_linear_bwd_weight_noalloc: the library's
+    per-GPU scratch array instead of a workspace; nothing is allocated."""
+    M = dY.shape[0]
+    _check_tensor(dY, "dY", (M, p.N), p.device)
+    _check_tensor(X, "X", (M, p.K), p.device)
+    _check_tensor(out, "out", (p.nnzb, p.b, p.b), p.device)
+    if dbias is not None:
+        _check_tensor(dbias, "dbias", (p.N,), p.device)
+    _lib.check(lib().bsr_linear_bwd_weight_noalloc(p.handle, _ptr(dY), _ptr(X), M, _ptr(out), _ptr(dbias),
+                                                   _stream(p.device)), "bsr_linear_bwd_weight_noalloc")
+    return out, dbias
+
+
 # ---- dense <-> BSR conversion and block magnitudes (include/bsr_convert.h) ----
 
 NORM_L1, NORM_L2_SQUARED = 1, 2

@@ -274,6 +274,27 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
     BSR_TRY_END
 }
 
+int32_t bsr_linear_bwd_weight_noalloc(const bsr_pattern *p, const bsr_bf16 *dY, const bsr_bf16 *X, int64_t M,
+                                      bsr_bf16 *dV, bsr_bf16 *dbias, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_ptr(dY, "dY", M == 0));
+    BSR_CHECK(check_ptr(X, "X", M == 0));
+    BSR_CHECK(check_ptr(dV, "dV", p->nnzb == 0));
+    BSR_CHECK(check_ptr(dbias, "dbias", true));
+    const size_t need = dw_workspace_bytes(*p, M);
+    if (need > (size_t)BSR_NOALLOC_SCRATCH_BYTES)
+        return fail(BSR_ERR_WORKSPACE_TOO_SMALL,
+                    "this pattern and M need " + std::to_string(need) + " bytes of scratch, above the " +
+                        std::to_string((size_t)BSR_NOALLOC_SCRATCH_BYTES) +
+                        " of the allocation-free call; use bsr_linear_bwd_weight with a workspace");
+    void *ws = nullptr;
+    if (need > 0) BSR_CHECK(noalloc_scratch(&ws));
+    DwArgs a{dY, X, M, dV, dbias, ws, need};
+    return launch_dw(*p, a, stream);
+    BSR_TRY_END
+}
+
 int32_t bsr_block_norms(int32_t N, int32_t K, int32_t b, const bsr_bf16 *W, int32_t kind, double *norms,
                         void *stream) {
     BSR_TRY_BEGIN

@@ -151,6 +151,9 @@ struct DwArgs {
 };
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M);
 int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream);
+// Device address of the current device's BSR_NOALLOC_SCRATCH_BYTES scratch array (looked up
+// once per device; no allocation).
+int32_t noalloc_scratch(void **out);
 
 // Compute units the balanced small-M work list is laid out for (one MI355X).
 constexpr int kSmallMUnits = 256;

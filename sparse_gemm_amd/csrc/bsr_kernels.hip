@@ -23,6 +23,8 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <string>
 
 #include "bsr_internal.hpp"
 
@@ -1088,6 +1090,34 @@ int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *r
 }
 
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan_dw(p, M).total : 0; }
+
+// ---- weight gradient without allocation: a scratch array in the code object ----
+// One array per GPU, created when the library's code object is loaded on that GPU and held until
+// the process ends. Its host-side name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+__device__ __align__(256) unsigned char scratch[BSR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int32_t noalloc_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BSR_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(BSR_ERR_UNSUPPORTED, "device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(BSR_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BSR_OK;
+}
 
 int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
