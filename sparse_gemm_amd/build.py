@@ -16,7 +16,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbsr_linear.so")
 ARCH = "gfx950"
 
-SOURCES = ["bsr_abi.cpp", "bsr_error.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip", "bsr_rebuild.hip"]
+SOURCES = ["bsr_abi.cpp", "bsr_error.cpp", "bsr_pattern.cpp", "bsr_select.cpp", "bsr_kernels.hip", "bsr_wide.hip",
+           "bsr_convert.hip", "bsr_fp8.hip", "bsr_sparse24.hip", "bsr_rebuild.hip"]
+# Kernels whose 4 x 4 grids of 32 x 32 accumulators (256 registers per lane) must live in the
+# accumulation registers: built without the flag that keeps accumulators in general registers.
+AGPR_SOURCES = {"bsr_wide.hip"}
 
 # Packed-fp32 instructions are kept out of the generated code on purpose; the host pass
 # prints a harmless "not a recognized feature" warning for this flag.
@@ -42,7 +46,8 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        flags = [f for f in HIP_FLAGS if src not in AGPR_SOURCES or f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+        cmd = [hipcc()] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)

@@ -49,6 +49,13 @@ int32_t upload(bsr_pattern &p) {
             parts.push_back({&sd.first->rec, &sd.second->rec});
         }
     }
+    for (auto sd : {std::make_pair(&p.wide_fwd, &d.wide_fwd), std::make_pair(&p.wide_bwd, &d.wide_bwd)}) {
+        parts.push_back({&sd.first->order, &sd.second->order});
+        parts.push_back({&sd.first->sub_ptr, &sd.second->sub_ptr});
+        parts.push_back({&sd.first->out, &sd.second->out});
+        parts.push_back({&sd.first->rec, &sd.second->rec});
+        parts.push_back({&sd.first->flags, &sd.second->flags});
+    }
     size_t total = 0;
     for (const Part &q : parts) total += (q.v->size() * sizeof(int32_t) + 255) & ~size_t(255);
     if (total == 0) total = 256;

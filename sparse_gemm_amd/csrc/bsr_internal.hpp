@@ -56,6 +56,27 @@ struct GroupSchedule {
     std::vector<int32_t> rec;        // [nsub * kRecInts]
 };
 
+// Wide-tile panel GEMM (b = 32; the matrix-core-bound regime of dense groups): a work-group owns
+// kWideG = 8 output blocks (256 output columns) and 256 activation rows, held by 4 waves as 4 x 4
+// grids of 32 x 32 accumulators. One sub-step per 64-column panel in which any member keeps a
+// block; the value block of unit u (member u / 2, block u % 2 of the panel) is staged at slot u.
+// Record, kWideRecInts ints: [0] panel, [1] presence mask (bit u = unit u has a block),
+// [2 + u] value block of unit u (-1 = none), [18], [19] unused (0).
+constexpr int kWideG = 8;
+constexpr int kWideU = 16;
+constexpr int kWideRecInts = 20;
+constexpr int kWideRows = 256;
+struct WideSchedule {
+    int ngroups = 0;
+    int64_t nunits = 0;              // kept blocks over all sub-steps (= nnzb)
+    std::vector<int32_t> order;      // processing order of the groups (most sub-steps first)
+    std::vector<int32_t> sub_ptr;    // [ngroups + 1]
+    std::vector<int32_t> out;        // [ngroups * kWideG] output block per member, -1 = unused
+    std::vector<int32_t> rec;        // [nsub * kWideRecInts]
+    std::vector<int32_t> flags;      // [ngroups]: 1 = dense group (every sub-step keeps all 16 units)
+    int64_t nsub() const { return sub_ptr.empty() ? 0 : sub_ptr.back(); }
+};
+
 // Weight-gradient work items. A tile is TR consecutive block rows by TC consecutive block columns
 // (TR * b = 256 and TC * b = 512 columns: per activation row, 512 bytes of dY and 1 KB of X, whole
 // cache lines); an item is up to kDwWaves * dw_slots(b) of a tile's kept blocks, each compute wave
@@ -74,6 +95,7 @@ struct DwSchedule {
 
 struct DevSchedule {
     const int32_t *order = nullptr, *sub_ptr = nullptr, *out = nullptr, *rec = nullptr;
+    const int32_t *flags = nullptr;   // wide schedules: per group, 1 = every sub-step keeps all units
 };
 
 // Device copies of the metadata (one allocation, carved into arrays).
@@ -84,6 +106,7 @@ struct DeviceMeta {
     const int32_t *row_ptr = nullptr, *col_idx = nullptr, *col_ptr = nullptr, *row_idx = nullptr,
                   *perm = nullptr;
     DevSchedule fwd[kGemmVariants], bwd[kGemmVariants];
+    DevSchedule wide_fwd, wide_bwd;
     const int32_t *dw_items = nullptr;
     const int32_t *small_m_rows = nullptr;  // small-M forward: [R][4] {block row, first block, end
                                             // block, 0}, most blocks first
@@ -97,6 +120,7 @@ struct bsr_pattern {
     int32_t N = 0, K = 0, b = 0, R = 0, C = 0, nnzb = 0;
     std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, small_m_rows, small_m_work;
     bsr::GroupSchedule fwd[bsr::kGemmVariants], bwd[bsr::kGemmVariants];
+    bsr::WideSchedule wide_fwd, wide_bwd;   // b = 32 only (empty otherwise)
     bsr::DwSchedule dw;
     bsr::DeviceMeta dev;
     bool uploaded = false;
@@ -135,6 +159,9 @@ struct FwdArgs {
     uint16_t *out;         // [M][out_ld]
     int out_ld;
 };
+// Whether the wide-tile kernel takes this call (dense groups, enough rows).
+bool use_wide(const bsr_pattern &p, bool transposed, int64_t M);
+int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream);
 // sparse24: forward only; a.V holds 2:4 block images (bsr_values_pack_24) instead of bf16 blocks.
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream,
                           bool sparse24 = false);

@@ -121,6 +121,68 @@ GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int
     return s;
 }
 
+// Wide-tile schedule (b = 32): output blocks grouped kWideG at a time in order of decreasing
+// kept-block count (so that rows with the same dense column set, e.g. full rows, share groups);
+// each group walks the panels in which any member keeps a block, ascending, one sub-step each.
+template <class ValFn>
+WideSchedule make_wide(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val) {
+    constexpr int PB = kPanelCols / 32;
+    const int32_t nout = (int32_t)ptr.size() - 1;
+    const std::vector<int32_t> ids = by_count_desc(ptr);
+    WideSchedule s;
+    s.ngroups = (nout + kWideG - 1) / kWideG;
+    s.out.assign((size_t)s.ngroups * kWideG, -1);
+    s.sub_ptr.assign(s.ngroups + 1, 0);
+    std::vector<int32_t> cursor(kWideG);
+    for (int32_t g = 0; g < s.ngroups; ++g) {
+        int members = 0;
+        for (int t = 0; t < kWideG && g * kWideG + t < nout; ++t, ++members) {
+            s.out[(size_t)g * kWideG + t] = ids[g * kWideG + t];
+            cursor[t] = ptr[ids[g * kWideG + t]];
+        }
+        int32_t nsub = 0;
+        for (;;) {
+            int32_t panel = INT32_MAX;
+            for (int t = 0; t < members; ++t) {
+                const int32_t o = s.out[(size_t)g * kWideG + t];
+                if (cursor[t] < ptr[o + 1]) panel = std::min(panel, idx[cursor[t]] / PB);
+            }
+            if (panel == INT32_MAX) break;
+            std::vector<int32_t> r(kWideRecInts, 0);
+            r[0] = panel;
+            for (int u = 0; u < kWideU; ++u) r[2 + u] = -1;
+            uint32_t mask = 0;
+            for (int t = 0; t < members; ++t) {
+                const int32_t o = s.out[(size_t)g * kWideG + t];
+                while (cursor[t] < ptr[o + 1] && idx[cursor[t]] / PB == panel) {
+                    const int u = t * PB + idx[cursor[t]] % PB;
+                    r[2 + u] = val(cursor[t]);
+                    mask |= 1u << u;
+                    ++s.nunits;
+                    cursor[t]++;
+                }
+            }
+            r[1] = (int32_t)mask;
+            s.rec.insert(s.rec.end(), r.begin(), r.end());
+            ++nsub;
+        }
+        s.sub_ptr[g + 1] = s.sub_ptr[g] + nsub;
+    }
+    s.flags.assign(s.ngroups, 0);
+    for (int32_t g = 0; g < s.ngroups; ++g) {
+        bool dense = s.sub_ptr[g + 1] > s.sub_ptr[g];
+        for (int32_t k = s.sub_ptr[g]; k < s.sub_ptr[g + 1] && dense; ++k)
+            dense = (uint32_t)s.rec[(size_t)k * kWideRecInts + 1] == (1u << kWideU) - 1;
+        s.flags[g] = dense ? 1 : 0;
+    }
+    s.order.resize(s.ngroups);
+    std::iota(s.order.begin(), s.order.end(), 0);
+    std::stable_sort(s.order.begin(), s.order.end(), [&](int32_t a, int32_t b) {
+        return s.sub_ptr[a + 1] - s.sub_ptr[a] > s.sub_ptr[b + 1] - s.sub_ptr[b];
+    });
+    return s;
+}
+
 // Weight-gradient items: the kept blocks of every tile (dw_tile_rows x dw_tile_cols block
 // positions) in row-major order, at most kDwWaves * dw_slots blocks per item (a fuller tile makes
 // several items), spread over the compute waves in contiguous runs as even as possible (blocks of
@@ -239,6 +301,13 @@ void build_pattern(bsr_pattern &p) {
         const GemmVariant v = gemm_variant(p.b, k);
         p.fwd[k] = make_panels(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, v.G, v.S);
         p.bwd[k] = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, v.G, v.S);
+    }
+    if (p.b == 32) {
+        p.wide_fwd = make_wide(p.row_ptr, p.col_idx, [](int32_t e) { return e; });
+        p.wide_bwd = make_wide(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; });
+    } else {
+        p.wide_fwd = WideSchedule();
+        p.wide_bwd = WideSchedule();
     }
     p.dw = make_dw_items(p);
     // small-M forward row list (the fp8 and 2:4 forwards for few rows): one entry per block row,

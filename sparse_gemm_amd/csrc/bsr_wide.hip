@@ -1,0 +1,349 @@
+// bsr_wide.hip -- the wide-tile panel GEMM (b = 32): forward and input gradient for groups whose
+// members keep blocks in most panels, the matrix-core-bound regime (e.g. block rows kept in full).
+//
+// Every kept block is a dense contraction on the matrix cores, zero blocks are skipped
+// (pytorch_block_sparse summary page, "Technical Foundation"). What changes against the panel GEMM
+// of bsr_kernels.hip is the register tile. A work-group is 4 waves, one per SIMD, and owns 256
+// activation rows x kWideG = 8 output blocks (256 output columns). Wave w owns rows
+// [128 (w & 1), +128) (4 row tiles of 32) and members [4 (w >> 1), +4): a 4 x 4 grid of 32 x 32 fp32
+// accumulators (256 accumulation registers). Per 16-deep chunk of a panel the wave reads 4
+// activation fragments and up to 4 value fragments (1 KB each) from LDS for up to 16 products,
+// 0.5 KB of LDS reads per product instead of 1 KB with the panel GEMM's 2 x 2 grids, whose
+// compute phase the LDS read rate bounds.
+//
+// Sub-step = one panel of 64 input columns: the activation panel (256 rows x 128 bytes, whole cache
+// lines) and the kept value blocks of its 16 units (unit u = member u / 2, block u % 2 of the panel;
+// 2 KB each, staged at slot u) go to LDS by direct-to-LDS loads that every wave issues for its
+// share. The 160 KB of LDS hold 3 activation stages and 2 value stages: during sub-step s the
+// value blocks of s + 1 are loaded (issued during the first 16-deep chunk of s) and the activation
+// panel of s + 2 (during the second chunk), so activation loads have two sub-steps to land. At
+// the end of s every wave waits for its loads of s + 1 and a barrier publishes them.
+// Groups whose every sub-step keeps all 16 units (e.g. block rows kept in full) run a body
+// without presence tests; the others test each member's block before its products.
+//   out tile^T [n][m] += A[n][k] . B[k][m],   B[k][m] = act[m][panel*64 + k]
+//   forward:    A[n][k] = V[i][n][k]   (natural layout, 16-byte LDS reads)
+//   input grad: A[n][k] = V[i][k][n]   (transposing LDS reads of the natural layout)
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <string>
+
+#include "bsr_device.hpp"
+#include "bsr_internal.hpp"
+
+namespace bsr {
+namespace {
+
+using namespace dev;
+
+constexpr int kXB = kWideRows * 128;                  // staged activation panel: 32 KB
+constexpr int kWBB = 32 * 64;                          // one value block: 2 KB
+constexpr int kVB = kWideU * kWBB;                     // staged value blocks of a panel: 32 KB
+constexpr int kXStages = 3, kVStages = 2;
+constexpr int kStagesBytes = kXStages * kXB + kVStages * kVB;   // 160 KB
+constexpr int kOutPitch = kWideG * 32 * 2 + 16;        // staged output row (bytes)
+constexpr int kSmem = kWideRows * kOutPitch > kStagesBytes ? kWideRows * kOutPitch : kStagesBytes;
+static_assert(kSmem <= 160 * 1024, "LDS of one work-group");
+
+struct WideRec {
+    int panel, mask, blk[4];   // blk: this wave's units wave + 4 j
+};
+
+struct WideArgs {
+    const uint16_t *act;
+    int in_ld, M;
+    const uint16_t *V;
+    uint32_t v_bytes;
+    const uint16_t *bias;
+    uint16_t *out;
+    int out_ld;
+};
+
+// One work-group's tile: group g, activation tile mt0. DENSE: every sub-step keeps all 16 units.
+template <bool TRANS, bool DENSE>
+__device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__restrict__ sub_ptr,
+                                          const int32_t *__restrict__ gout, const int32_t *__restrict__ rec, int g,
+                                          int mt0, unsigned char *smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    const int rows = min(kWideRows, a.M - mt0 * kWideRows);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (int64_t)mt0 * kWideRows * a.in_ld, (uint32_t)rows * a.in_ld * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.V, a.v_bytes);
+    const uint32_t sbase = lds_addr(smem);
+
+    // Sub-step records come through scalar loads whose index is clamped into the group (no
+    // select on the loaded values): a record is loaded three sub-steps ahead and first read at the
+    // end of the sub-step that loaded it, when the wait for it costs nothing.
+    auto load_rec = [&](int s) __attribute__((always_inline)) {
+        const int32_t *e = rec + (size_t)s * kWideRecInts;
+        WideRec x;
+        x.panel = __builtin_amdgcn_readfirstlane(e[0]);
+        x.mask = DENSE ? (1 << kWideU) - 1 : __builtin_amdgcn_readfirstlane(e[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + wave + 4 * j]);
+        return x;
+    };
+    // activation load i = wave + 4 j (j < 8) of panel x.panel into activation stage xs: rows
+    // 8 i .. 8 i + 7 (lane -> row 8 i + lane / 8, LDS chunk lane % 8 holding source chunk (lane % 8)
+    // ^ swz8(row)). Rows past M and columns past the matrix (a last half panel) read as zeros
+    // through the range-checked voffset.
+    auto issue_x = [&](int xs, const WideRec &x, int j) __attribute__((always_inline)) {
+        const int i = wave + 4 * j;
+        const int r = i * 8 + (lane >> 3);
+        dma16(ra, sbase + (uint32_t)xs * kXB + (uint32_t)i * 1024u,
+              (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)x.panel * 128u + (uint32_t)(((lane & 7) ^ swz8(r)) << 4), 0);
+    };
+    // value block of unit u = wave + 4 t (if kept) into value stage vs: two 1 KB halves (lane ->
+    // block row 16 q + lane / 4, chunk (lane % 4) ^ swz4(row))
+    auto issue_v = [&](int vs, const WideRec &x, int t) __attribute__((always_inline)) {
+        const int u = wave + 4 * t;
+        if (DENSE || ((x.mask >> u) & 1)) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int n = 16 * q + (lane >> 2);
+                dma16(rv, sbase + kXStages * kXB + (uint32_t)vs * kVB + (uint32_t)u * kWBB + (uint32_t)q * 1024u,
+                      (uint32_t)(n * 64 + (((lane & 3) ^ swz4(n)) << 4)), (uint32_t)x.blk[t] * kWBB);
+            }
+        }
+    };
+
+    f32x16 acc[4][4];   // [row tile][member of the wave]
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.f;
+
+    // value fragment of the block staged at wb for 16-deep chunk kc: natural layout for the
+    // forward; for the input gradient lane l holds V[kc*16 + 8 (l / 32) .. + 7][l % 32], from two
+    // transposing reads of 4 rows each
+    auto wfrag = [&](const unsigned char *wb, int kc) __attribute__((always_inline)) {
+        if constexpr (!TRANS) {
+            return *reinterpret_cast<const bf16x8 *>(wb + l32 * 64 + (((2 * kc + lh) ^ swz4(l32)) << 4));
+        } else {
+            const int gq = lane >> 4, s16 = lane & 15;
+            const int R = kc * 16 + (gq >> 1) * 8 + (s16 >> 2);
+            const int C = (gq & 1) * 16 + 4 * (s16 & 3);
+            auto at = [&](int row) {
+                return (lds_i16x4 *)(wb + row * 64 + ((((C >> 3) ^ swz4(row)) << 4) | ((C & 7) << 1)));
+            };
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        }
+    };
+    auto xfrag = [&](const unsigned char *xt, int rt, int c) __attribute__((always_inline)) {
+        const int r = wr * 128 + rt * 32 + l32;
+        return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
+    };
+
+    // Products of one staged sub-step, chunk by chunk (c = 16-deep chunk of the panel, block c / 2),
+    // member by member: fragment set c & 1 holds chunk c. m8 = presence of this wave's 8 units (bit
+    // 2 t + h: member 4 wm + t, block h of the panel). Absent units' products are skipped, never run
+    // on zero blocks (zero times a non-finite activation is not zero). Fragments are read one chunk
+    // ahead into the other register set (for every unit, present or not: a read of an unused slot
+    // is harmless), so the LDS latency hides behind the matrix cores.
+    bf16x8 xf[2][4], wf[2][4];
+    auto read_frags = [&](int set, int xs, int vs, int c) __attribute__((always_inline)) {
+        const unsigned char *xt = smem + xs * kXB;
+        const unsigned char *wt = smem + kXStages * kXB + vs * kVB + wm * 8 * kWBB;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xf[set][rt] = xfrag(xt, rt, c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wf[set][t] = wfrag(wt + (2 * t + (c >> 1)) * kWBB, c & 1);
+    };
+    // the products of chunk c; after(t) runs after those of member t (scheduling barriers keep it
+    // there, so load issues go out between products)
+    auto products = [&](int c, int m8, auto &&after) __attribute__((always_inline)) {
+        const int cur = c & 1, h = c >> 1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (DENSE || ((m8 >> (2 * t + h)) & 1)) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) acc[rt][t] = mfma32(wf[cur][t], xf[cur][rt], acc[rt][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            after(t);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto none = [](int) __attribute__((always_inline)) {};
+
+    // Sub-step pipeline. Before sub-step s: activation stages hold s, s + 1, s + 2 (landed or in
+    // flight), value stages s, s + 1; fragment set 0 holds chunk 0 of s. Sub-step s: chunks 0 .. 2
+    // (each reading the next chunk's fragments), then every wave waits for its LDS reads of s (all
+    // in registers now) and for its loads of s + 1, and a barrier publishes s + 1 and frees the
+    // stages of s; then the value blocks of s + 2 and the activation panel of s + 3 are issued into
+    // those stages between the products of chunk 3, after the reads of chunk 0 of s + 1. So the
+    // barrier never waits on an LDS read, the next sub-step starts with its first fragments in
+    // registers, and loads have more than one sub-step (values) and two (activations) to land.
+    const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
+    if (s0 < s1) {
+        WideRec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
+        WideRec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_x(0, r0, j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) issue_v(0, r0, t);
+        if (s0 + 1 < s1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) issue_x(1, r1, j);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) issue_v(1, r1, t);
+        }
+        if (s0 + 2 < s1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) issue_x(2, r2, j);
+        }
+        wait_vm<0, 0>(0);
+        __syncthreads();
+        read_frags(0, 0, 0, 0);
+        int xs = 0, vs = 0;
+        for (int s = s0; s < s1; ++s) {
+            const int m8 = (r0.mask >> (8 * wm)) & 0xFF;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                read_frags((c + 1) & 1, xs, vs, c + 1);
+                products(c, m8, none);
+            }
+            // every LDS read of sub-step s has landed in registers (chunk 3's included)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // the record of s + 4 is loaded now, with no LDS read outstanding: scalar loads share
+            // the LDS wait counter and return out of order, so one in flight would turn the partial
+            // LDS waits into full ones
+            const WideRec r4 = load_rec(min(s + 4, s1 - 1));
+            // this wave's loads of s + 1 have landed; the activation loads of s + 2, issued after
+            // them during sub-step s - 1, may still be in flight
+            if (s > s0 && s + 2 < s1) wait_vm<8, 8>(8);
+            else wait_vm<0, 0>(0);
+            __syncthreads();   // everyone's have; nobody reads the stages of s any more
+            const int xn = xs == 2 ? 0 : xs + 1, vn = vs ^ 1;
+            read_frags(0, xn, vn, 0);   // chunk 0 of s + 1 (harmless past the last sub-step)
+            const bool more2 = s + 2 < s1, more3 = s + 3 < s1;
+            // value loads first, activation loads last: the wait above counts on the last 8 loads
+            // of a sub-step being its activation loads (loads complete in issue order)
+            products(3, m8, [&](int t) __attribute__((always_inline)) {
+                if (t < 2) {
+                    if (more2) {
+                        issue_v(vs, r2, 2 * t);
+                        issue_v(vs, r2, 2 * t + 1);
+                    }
+                } else if (more3) {
+#pragma unroll
+                    for (int j = 4 * (t - 2); j < 4 * (t - 2) + 4; ++j) issue_x(xs, r3, j);
+                }
+            });
+            r0 = r1;
+            r1 = r2;
+            r2 = r3;
+            r3 = r4;
+            xs = xn;
+            vs = vn;
+        }
+    }
+    __syncthreads();   // the stages are free for the output tile
+
+    // Epilogue through LDS: item v of lane l of acc[rt][t] is output column 8 (v / 4) + 4 (l / 32) +
+    // v % 4 of member 4 wm + t, activation row 128 wr + 32 rt + l % 32. Bias in fp32, one bf16
+    // rounding; then every wave stores 64 staged rows as 16-byte pieces of whole 64-byte block rows.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tg = wm * 4 + t;
+        const int o = gout[g * kWideG + tg];
+        if (o < 0) continue;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tg * 32 + q * 8 + lh * 4;
+                const int row = wr * 128 + rt * 32 + l32;
+                f32x4 v = quad(acc[rt][t], q);
+                if (a.bias) v = add_bias4(v, a.bias + o * 32 + q * 8 + lh * 4);
+                store4_bf16(reinterpret_cast<uint16_t *>(smem + row * kOutPitch + c * 2), v[0], v[1], v[2], v[3]);
+            }
+            // one accumulator tile at a time: keeps the reads of the accumulation registers from
+            // being hoisted all at once (which spills)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    const int m0 = mt0 * kWideRows + wave * 64;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+        const int seg = i * 64 + lane, row = seg >> 5, cs = seg & 31;   // 32 pieces per row
+        const int t = cs >> 2, within = (cs & 3) * 8;
+        const int o = gout[g * kWideG + t];
+        if (o < 0 || m0 + row >= a.M) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 64 + row) * kOutPitch + cs * 16);
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(a.out + (int64_t)(m0 + row) * a.out_ld + o * 32 + within));
+    }
+}
+
+template <bool TRANS>
+__global__ __launch_bounds__(256, 1) void k_wide_gemm(WideArgs a, const int32_t *__restrict__ order,
+                                                      const int32_t *__restrict__ flags,
+                                                      const int32_t *__restrict__ sub_ptr,
+                                                      const int32_t *__restrict__ gout,
+                                                      const int32_t *__restrict__ rec, int ngroups, int nmtiles,
+                                                      int tpc) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
+    // Work-group -> (group, activation tile), as in the panel GEMM: each XCD takes a contiguous run
+    // of chunks of tpc activation tiles x all groups (heaviest groups first), so the work-groups
+    // running together on an XCD share activation panels and value blocks through its L2.
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = L / (tpc * ngroups), r4 = L % (tpc * ngroups);
+    const int mc = min(tpc, nmtiles - tpc * chunk);
+    const int g = order[r4 / mc];
+    const int mt0 = tpc * chunk + r4 % mc;
+    if (flags[g]) wide_tile<TRANS, true>(a, sub_ptr, gout, rec, g, mt0, smem);
+    else wide_tile<TRANS, false>(a, sub_ptr, gout, rec, g, mt0, smem);
+}
+
+int wide_tiles_per_chunk(int nmtiles) {
+    int t = 4;
+    if (const char *f = std::getenv("BSR_WIDE_TPC")) t = std::atoi(f);   // tuning knob
+    return std::max(1, std::min(t, nmtiles));
+}
+
+}  // namespace
+
+bool use_wide(const bsr_pattern &p, bool transposed, int64_t M) {
+    if (p.b != 32) return false;
+    const WideSchedule &s = transposed ? p.wide_bwd : p.wide_fwd;
+    if (const char *f = std::getenv("BSR_GEMM_VARIANT")) return std::atoi(f) == kGemmVariants;   // tuning knob
+    const int64_t nsub = s.nsub();
+    if (nsub == 0 || M < kWideRows) return false;
+    // dense groups: on average at least half of a sub-step's 16 units keep a block
+    return (double)s.nunits >= 8.0 * (double)nsub;
+}
+
+int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {
+    const hipStream_t st = (hipStream_t)stream;
+    const WideSchedule &s = transposed ? p.wide_bwd : p.wide_fwd;
+    const DevSchedule &d = transposed ? p.dev.wide_bwd : p.dev.wide_fwd;
+    const int nmtiles = (int)((a.M + kWideRows - 1) / kWideRows);
+    const int64_t nwg = (int64_t)s.ngroups * nmtiles;
+    if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
+    if ((size_t)p.nnzb * 32 * 32 * 2 > (size_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
+    if ((int64_t)kWideRows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
+        return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
+    if (nwg == 0) return BSR_OK;
+    const int tpc = wide_tiles_per_chunk(nmtiles);
+    const WideArgs wa{a.act, a.in_ld, (int)a.M, a.V, (uint32_t)((size_t)p.nnzb * 32 * 32 * 2), a.bias, a.out, a.out_ld};
+    if (transposed)
+        hipLaunchKernelGGL(k_wide_gemm<true>, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr,
+                           d.out, d.rec, s.ngroups, nmtiles, tpc);
+    else
+        hipLaunchKernelGGL(k_wide_gemm<false>, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr,
+                           d.out, d.rec, s.ngroups, nmtiles, tpc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide gemm launch: ") + hipGetErrorString(e));
+    return BSR_OK;
+}
+
+}  // namespace bsr

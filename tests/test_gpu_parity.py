@@ -55,7 +55,7 @@ def test_bias_gradient_ragged(M, N, K, b, d, seed):
     full_parity(M, N, K, b, host, dbias=True)
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "4"])
 @pytest.mark.parametrize("M,N,K,b,seed", [
     (300, 512, 480, 32, 11),   # 15 block columns: the last 64-column panel is half a panel
     (300, 512, 448, 64, 12),
@@ -102,7 +102,7 @@ def test_nonfinite_activation_small_m_tiles(b, M, bad_rows):
     p.close()
 
 
-@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3", "4"])
 @pytest.mark.parametrize("M", [9, 300])
 def test_nonfinite_activation_stays_in_its_blocks(monkeypatch, variant, M):
     """The layer sums over kept blocks only: an infinite activation in input block 1 reaches the
