@@ -40,6 +40,7 @@ int32_t upload(bsr_pattern &p) {
         {&p.row_ptr, &d.row_ptr}, {&p.col_idx, &d.col_idx}, {&p.col_ptr, &d.col_ptr},
         {&p.row_idx, &d.row_idx}, {&p.perm, &d.perm},       {&p.small_m_rows, &d.small_m_rows},
         {&p.dw.items, &d.dw_items},         {&p.small_m_work, &d.small_m_work},
+        {&p.wdw.items, &d.wdw_items},       {&p.wdw.compact, &d.wdw_compact},
     };
     for (int k = 0; k < kGemmVariants; ++k) {
         for (auto sd : {std::make_pair(&p.fwd[k], &d.fwd[k]), std::make_pair(&p.bwd[k], &d.bwd[k])}) {

@@ -93,6 +93,37 @@ struct DwSchedule {
     std::vector<int32_t> items;   // [n * kDwItemInts], by super-tiles of 8 x 4 tiles
 };
 
+// Wide weight-gradient items (b = 32): a tile of kWdwRows block rows (any rows) by kWdwCols block
+// columns (any columns), run by 4 waves that each hold 4 x 4 block accumulators; the products of
+// absent blocks are computed and dropped. Two kinds, in this order: dense items (4 rows whose 16
+// consecutive columns are all kept, rows taken in order of decreasing kept-block count, so that
+// full rows share tiles), then gathered items that take every remaining block, a seed row (most
+// remaining blocks) with the 3 rows that share most of its columns, and the 16 columns most of the
+// 4 rows keep (see make_wide_dw). Item layout, kWdwItemInts ints: [t] block row t (t < 4; -1 =
+// unused), [4 + j] block column j (j < 16; -1 = unused), [kWdwBlockAt + 16 t + j] CSR index of block
+// (t, j) or -1, [kWdwCompactAt + 16 t + j] its compact index (blocks numbered in item order, row-
+// major inside an item) or -1.
+constexpr int kWdwRows = 4;
+constexpr int kWdwCols = 16;
+constexpr int kWdwBlockAt = 24;
+constexpr int kWdwCompactAt = 88;
+constexpr int kWdwItemInts = 152;
+constexpr int kWdwWindow = 32;   // candidate rows per gathered item (next by remaining count)
+struct WideDwSchedule {
+    int n = 0;        // items
+    int ndense = 0;   // the first ndense items are dense
+    std::vector<int32_t> items;     // [n * kWdwItemInts], dense items in XCD-friendly order
+    std::vector<int32_t> compact;   // [nnzb]: CSR index of compact index c
+    std::vector<int32_t> first;     // [n + 1]: compact index of each item's first block; nnzb
+};
+
+// How one weight-gradient call runs the wide items: the first n1 whole (one work-group each over
+// every activation row), the other n2 split into c2 chunks of mchunk rows whose fp32 partials (P2
+// blocks per chunk, compact indices cbase ..) a reduction sums.
+struct WideDwPlan {
+    int n1 = 0, n2 = 0, c2 = 1, mchunk = 0, cbase = 0, P2 = 0;
+};
+
 struct DevSchedule {
     const int32_t *order = nullptr, *sub_ptr = nullptr, *out = nullptr, *rec = nullptr;
     const int32_t *flags = nullptr;   // wide schedules: per group, 1 = every sub-step keeps all units
@@ -108,6 +139,7 @@ struct DeviceMeta {
     DevSchedule fwd[kGemmVariants], bwd[kGemmVariants];
     DevSchedule wide_fwd, wide_bwd;
     const int32_t *dw_items = nullptr;
+    const int32_t *wdw_items = nullptr, *wdw_compact = nullptr;
     const int32_t *small_m_rows = nullptr;  // small-M forward: [R][4] {block row, first block, end
                                             // block, 0}, most blocks first
     const int32_t *small_m_work = nullptr;  // balanced small-M work list: [n][4] {block row, first
@@ -121,7 +153,8 @@ struct bsr_pattern {
     std::vector<int32_t> row_ptr, col_idx, col_ptr, row_idx, perm, small_m_rows, small_m_work;
     bsr::GroupSchedule fwd[bsr::kGemmVariants], bwd[bsr::kGemmVariants];
     bsr::WideSchedule wide_fwd, wide_bwd;   // b = 32 only (empty otherwise)
-    bsr::DwSchedule dw;
+    bsr::DwSchedule dw;        // items of the blocks the wide items leave
+    bsr::WideDwSchedule wdw;   // b = 32 only
     bsr::DeviceMeta dev;
     bool uploaded = false;
 };
@@ -178,6 +211,10 @@ struct DwArgs {
 };
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M);
 int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream);
+// The wide weight-gradient items (bsr_wide.hip): fp32 partials [chunk][nnzb][b*b] when partial
+// is not null, else bf16 into a.dV.
+WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M);
+int32_t launch_wide_dw(const bsr_pattern &p, const DwArgs &a, const WideDwPlan &w, float *partial, void *stream);
 // Device address of the current device's BSR_NOALLOC_SCRATCH_BYTES scratch array (looked up
 // once per device; no allocation).
 int32_t noalloc_scratch(void **out);

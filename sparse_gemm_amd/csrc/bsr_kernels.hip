@@ -796,9 +796,11 @@ int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
 // Weight-gradient plan: chunks of M (a multiple of the kernel's 32-row stage, at least 256 rows)
 // and the workspace layout.
 struct DwPlan {
-    int nchunks = 1, mchunk = 0;
-    size_t partial_bytes = 0;   // [nchunks][nnzb][b*b] fp32, only when nchunks > 1
-    int bchunks = 1;            // row chunks of the bias column sums
+    int nchunks = 1, mchunk = 0;   // tile items
+    WideDwPlan wide;               // wide items (b = 32; then there are no tile items)
+    size_t partial_bytes = 0;      // tile items: [nchunks][nnzb][b*b] fp32 when nchunks > 1;
+                                   // wide items: [c2][P2][1024] fp32 when c2 > 1
+    int bchunks = 1;               // row chunks of the bias column sums
     int64_t brows = 0;
     size_t bias_off = 0, bias_bytes = 0, total = 0;
 };
@@ -806,16 +808,21 @@ struct DwPlan {
 DwPlan plan_dw(const bsr_pattern &p, int64_t M) {
     DwPlan d;
     if (M <= 0) return d;
-    const int64_t n = std::max(p.dw.n, 1);
-    // The most chunks whose work-groups (one per compute unit at a time) still run in a single
-    // round; one chunk when the items alone fill the chip. Measured on BERT-base FFN-up (24 items):
-    // 8 chunks 24.5 us, 10 chunks (240 work-groups) 23.3 us, 11 chunks (264: a second round)
-    // 31.9 us; more chunks also cost an fp32 partial of every block each.
-    const int64_t c = std::max<int64_t>(1, std::min<int64_t>(kCUs / n, M / 256));
-    d.mchunk = (int)(((M + c - 1) / c + 31) / 32 * 32);
-    d.nchunks = (int)((M + d.mchunk - 1) / d.mchunk);
+    if (p.wdw.n > 0) {
+        d.wide = plan_wide_dw(p, M);
+        d.partial_bytes = d.wide.c2 > 1 ? (size_t)d.wide.c2 * d.wide.P2 * 1024 * sizeof(float) : 0;
+    } else {
+        const int64_t n = std::max(p.dw.n, 1);
+        // The most chunks whose work-groups (one per compute unit at a time) still run in a single
+        // round; one chunk when the items alone fill the chip. Measured on BERT-base FFN-up (24
+        // items): 8 chunks 24.5 us, 10 chunks (240 work-groups) 23.3 us, 11 chunks (264: a second
+        // round) 31.9 us; more chunks also cost an fp32 partial of every block each.
+        const int64_t c = std::max<int64_t>(1, std::min<int64_t>(kCUs / n, M / 256));
+        d.mchunk = (int)(((M + c - 1) / c + 31) / 32 * 32);
+        d.nchunks = (int)((M + d.mchunk - 1) / d.mchunk);
+        d.partial_bytes = d.nchunks > 1 ? (size_t)d.nchunks * p.nnzb * p.b * p.b * sizeof(float) : 0;
+    }
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    d.partial_bytes = d.nchunks > 1 ? (size_t)d.nchunks * p.nnzb * p.b * p.b * sizeof(float) : 0;
     d.bchunks = (int)std::min<int64_t>(64, std::max<int64_t>(1, M / 256));
     d.brows = (M + d.bchunks - 1) / d.bchunks;
     d.bchunks = (int)((M + d.brows - 1) / d.brows);
@@ -1012,9 +1019,15 @@ int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream) {
     }
     const DwPlan pl = plan_dw(p, a.M);
     char *ws = static_cast<char *>(a.ws);
-    if ((size_t)(a.M + 32) * p.N * 2 > (size_t)UINT32_MAX || (size_t)(a.M + 32) * p.K * 2 > (size_t)UINT32_MAX)
+    // 32-bit buffer offsets: activation rows up to 256 past the rows of one call (the wide kernel's
+    // surplus loads past a chunk)
+    if ((size_t)(a.M + 256) * p.N * 2 > (size_t)UINT32_MAX || (size_t)(a.M + 256) * p.K * 2 > (size_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activations above 4 GiB for 32-bit buffer offsets");
-    if (p.nnzb > 0) {
+    if (p.wdw.n > 0) {
+        // every block on the wide kernel
+        const int32_t rc = launch_wide_dw(p, a, pl.wide, reinterpret_cast<float *>(ws), stream);
+        if (rc != BSR_OK) return rc;
+    } else if (p.nnzb > 0) {
         float *partial = pl.nchunks > 1 ? reinterpret_cast<float *>(ws) : nullptr;
         const dim3 grid((unsigned)((int64_t)p.dw.n * pl.nchunks));
         constexpr int NL = kLoaderWaves, NT = (kDwWaves + NL) * 64;

@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <string>
 #include <numeric>
+#include <set>
 #include <tuple>
 #include <utility>
 
@@ -187,7 +188,7 @@ WideSchedule make_wide(const std::vector<int32_t> &ptr, const std::vector<int32_
 // positions) in row-major order, at most kDwWaves * dw_slots blocks per item (a fuller tile makes
 // several items), spread over the compute waves in contiguous runs as even as possible (blocks of
 // one run mostly share a row). Items are ordered by super-tiles of 8 x 4 tiles.
-DwSchedule make_dw_items(const bsr_pattern &p) {
+DwSchedule make_dw_items(const bsr_pattern &p, const std::vector<char> &taken) {
     const int TR = dw_tile_rows(p.b), TC = dw_tile_cols(p.b), SL = dw_slots(p.b), cap = kDwWaves * SL;
     std::vector<std::pair<int32_t, std::vector<int32_t>>> items;
     std::vector<int32_t> blk;   // (CSR index << 8) | (i << 4) | j, row-major inside the tile
@@ -196,7 +197,7 @@ DwSchedule make_dw_items(const bsr_pattern &p) {
             blk.clear();
             for (int32_t r = r0; r < std::min(p.R, r0 + TR); ++r)
                 for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e)
-                    if (p.col_idx[e] >= c0 && p.col_idx[e] < c0 + TC)
+                    if (p.col_idx[e] >= c0 && p.col_idx[e] < c0 + TC && !taken[e])
                         blk.push_back((e << 8) | ((r - r0) << 4) | (p.col_idx[e] - c0));
             for (size_t f = 0; f < blk.size(); f += cap) {
                 const int n = (int)std::min<size_t>(cap, blk.size() - f);
@@ -221,6 +222,142 @@ DwSchedule make_dw_items(const bsr_pattern &p) {
     DwSchedule s;
     s.n = (int)items.size();
     for (auto &x : items) s.items.insert(s.items.end(), x.second.begin(), x.second.end());
+    return s;
+}
+
+// Wide weight-gradient items (b = 32). Dense items first: block rows in order of decreasing kept-
+// block count, 4 at a time, against every tile of 16 consecutive block columns that all 4 rows keep
+// whole; they are ordered in runs of 8 row groups x 3 column tiles, so that the work-groups that run
+// together on one XCD (a contiguous run of items) share activation column segments and gradient row
+// segments in its L2. Then gathered items until every block is taken: the seed is the row with the
+// most remaining blocks; with it go the 3 rows, among the next kWdwWindow by remaining count, that
+// share most of its remaining columns (ties: more remaining blocks, then the order of the count
+// list); the item takes the 16 columns that most of its rows keep (ties: lower column), in
+// ascending column order. Returns an empty schedule (every block left to the tile items) for b = 64
+// and for patterns without a dense tile (measured: on BERT-base FFN-up and the square 10% layer the
+// tile items take 25 and 83 us, the gathered wide items 31 and 94 us).
+WideDwSchedule make_wide_dw(const bsr_pattern &p, std::vector<char> &taken) {
+    WideDwSchedule s;
+    taken.assign(p.nnzb, 0);
+    if (p.b != 32 || p.nnzb == 0) return s;
+    if (const char *f = std::getenv("BSR_DW_TILE"))   // tuning knob: 1 = tile items only
+        if (std::atoi(f) == 1) return s;
+    const int32_t R = p.R, C = p.C, W = (C + 63) / 64;
+    std::vector<uint64_t> rem((size_t)R * W, 0);   // remaining (untaken) kept columns per row
+    for (int32_t r = 0; r < R; ++r)
+        for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e)
+            rem[(size_t)r * W + p.col_idx[e] / 64] |= uint64_t(1) << (p.col_idx[e] % 64);
+    auto has = [&](int32_t r, int32_t c) { return (rem[(size_t)r * W + c / 64] >> (c % 64)) & 1; };
+    auto csr = [&](int32_t r, int32_t c) {
+        const auto b0 = p.col_idx.begin() + p.row_ptr[r], b1 = p.col_idx.begin() + p.row_ptr[r + 1];
+        return (int32_t)(std::lower_bound(b0, b1, c) - p.col_idx.begin());
+    };
+    std::vector<std::vector<int32_t>> dense, gathered;
+    auto make_item = [&](const std::vector<int32_t> &rows, const std::vector<int32_t> &cols) {
+        std::vector<int32_t> it(kWdwItemInts, -1);
+        for (size_t t = 0; t < rows.size(); ++t) it[t] = rows[t];
+        for (size_t j = 0; j < cols.size(); ++j) it[4 + j] = cols[j];
+        for (size_t t = 0; t < rows.size(); ++t)
+            for (size_t j = 0; j < cols.size(); ++j)
+                if (has(rows[t], cols[j])) {
+                    const int32_t e = csr(rows[t], cols[j]);
+                    it[kWdwBlockAt + 16 * t + j] = e;
+                    taken[e] = 1;
+                }
+        for (size_t t = 0; t < rows.size(); ++t)
+            for (size_t j = 0; j < cols.size(); ++j)
+                if (it[kWdwBlockAt + 16 * t + j] >= 0)
+                    rem[(size_t)rows[t] * W + cols[j] / 64] &= ~(uint64_t(1) << (cols[j] % 64));
+        return it;
+    };
+
+    // dense items
+    const std::vector<int32_t> order = by_count_desc(p.row_ptr);
+    const int32_t ngr = R / kWdwRows, nct = C / kWdwCols;
+    std::vector<std::vector<int32_t>> grid((size_t)ngr * nct);
+    for (int32_t gr = 0; gr < ngr; ++gr) {
+        const std::vector<int32_t> rows(order.begin() + gr * kWdwRows, order.begin() + (gr + 1) * kWdwRows);
+        if (p.row_ptr[rows.back() + 1] - p.row_ptr[rows.back()] < kWdwCols) break;   // sorted: no more
+        for (int32_t ct = 0; ct < nct; ++ct) {
+            std::vector<int32_t> cols(kWdwCols);
+            std::iota(cols.begin(), cols.end(), ct * kWdwCols);
+            bool full = true;
+            for (int32_t r : rows)
+                for (int32_t c : cols) full = full && has(r, c);
+            if (full) grid[(size_t)gr * nct + ct] = make_item(rows, cols);
+        }
+    }
+    for (int32_t g0 = 0; g0 < ngr; g0 += 8)
+        for (int32_t c0 = 0; c0 < nct; c0 += 3)
+            for (int32_t ct = c0; ct < std::min(nct, c0 + 3); ++ct)
+                for (int32_t gr = g0; gr < std::min(ngr, g0 + 8); ++gr)
+                    if (!grid[(size_t)gr * nct + ct].empty()) dense.push_back(std::move(grid[(size_t)gr * nct + ct]));
+
+    // gathered items over the remaining blocks; rows keyed by (remaining count desc, row asc)
+    std::vector<int32_t> cnt(R, 0);
+    std::set<std::pair<int32_t, int32_t>> live;
+    for (int32_t r = 0; r < R; ++r) {
+        for (int32_t w = 0; w < W; ++w) cnt[r] += __builtin_popcountll(rem[(size_t)r * W + w]);
+        if (cnt[r]) live.insert({-cnt[r], r});
+    }
+    std::vector<int32_t> mult(C, 0);
+    while (!live.empty()) {
+        auto at = live.begin();
+        const int32_t seed = at->second;
+        struct Cand {
+            int32_t shared, count, rank, row;
+        };
+        std::vector<Cand> cand;
+        int32_t rank = 0;
+        for (++at; at != live.end() && rank < kWdwWindow; ++at, ++rank) {
+            int32_t sh = 0;
+            for (int32_t w = 0; w < W; ++w)
+                sh += __builtin_popcountll(rem[(size_t)seed * W + w] & rem[(size_t)at->second * W + w]);
+            cand.push_back({sh, -at->first, rank, at->second});
+        }
+        std::sort(cand.begin(), cand.end(), [](const Cand &x, const Cand &y) {
+            return std::make_tuple(-x.shared, -x.count, x.rank) < std::make_tuple(-y.shared, -y.count, y.rank);
+        });
+        std::vector<int32_t> rows = {seed};
+        for (size_t k = 0; k < cand.size() && rows.size() < (size_t)kWdwRows; ++k) rows.push_back(cand[k].row);
+        std::vector<int32_t> cols;
+        for (int32_t r : rows)
+            for (int32_t w = 0; w < W; ++w)
+                for (uint64_t m = rem[(size_t)r * W + w]; m; m &= m - 1) {
+                    const int32_t c = w * 64 + __builtin_ctzll(m);
+                    if (mult[c]++ == 0) cols.push_back(c);
+                }
+        std::stable_sort(cols.begin(), cols.end(), [&](int32_t x, int32_t y) { return mult[x] != mult[y] ? mult[x] > mult[y] : x < y; });
+        for (int32_t c : cols) mult[c] = 0;
+        if (cols.size() > (size_t)kWdwCols) cols.resize(kWdwCols);
+        std::sort(cols.begin(), cols.end());
+        for (int32_t r : rows) live.erase({-cnt[r], r});
+        gathered.push_back(make_item(rows, cols));
+        for (int32_t r : rows) {
+            cnt[r] = 0;
+            for (int32_t w = 0; w < W; ++w) cnt[r] += __builtin_popcountll(rem[(size_t)r * W + w]);
+            if (cnt[r]) live.insert({-cnt[r], r});
+        }
+    }
+    if (dense.empty()) {   // no dense tile: the tile items do better (BERT-base FFN-up, the square layer)
+        taken.assign(p.nnzb, 0);
+        return s;
+    }
+    s.ndense = (int)dense.size();
+    s.n = (int)(dense.size() + gathered.size());
+    s.compact.assign(p.nnzb, -1);
+    int32_t next = 0;
+    for (auto *list : {&dense, &gathered})
+        for (auto &it : *list) {
+            s.first.push_back(next);
+            for (int k = 0; k < kWdwRows * kWdwCols; ++k)
+                if (it[kWdwBlockAt + k] >= 0) {
+                    it[kWdwCompactAt + k] = next;
+                    s.compact[next++] = it[kWdwBlockAt + k];
+                }
+            s.items.insert(s.items.end(), it.begin(), it.end());
+        }
+    s.first.push_back(next);
     return s;
 }
 
@@ -309,7 +446,9 @@ void build_pattern(bsr_pattern &p) {
         p.wide_fwd = WideSchedule();
         p.wide_bwd = WideSchedule();
     }
-    p.dw = make_dw_items(p);
+    std::vector<char> taken;
+    p.wdw = make_wide_dw(p, taken);
+    p.dw = make_dw_items(p, taken);
     // small-M forward row list (the fp8 and 2:4 forwards for few rows): one entry per block row,
     // {row, first block, end block, 0}. The rows of the first round of work-groups (one per compute
     // unit) come heaviest first and the rest lightest first, so that a unit's second work-group tends

@@ -25,8 +25,12 @@
 //   input grad: A[n][k] = V[i][k][n]   (transposing LDS reads of the natural layout)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "bsr_device.hpp"
 #include "bsr_internal.hpp"
@@ -304,6 +308,251 @@ __global__ __launch_bounds__(256, 1) void k_wide_gemm(WideArgs a, const int32_t 
     else wide_tile<TRANS, false>(a, sub_ptr, gout, rec, g, mt0, smem);
 }
 
+// ------------------------------------------------------------------------------------------
+// Wide weight gradient (b = 32): for the kept blocks of a tile of 4 block rows x 16 block columns
+// (any rows, any columns),
+//   dV[i][p][q] = sum_m dY[m][r*32 + p] * X[m][c*32 + q]     (the block-masked SDDMM)
+// over one chunk of activation rows. 4 waves, one per SIMD; wave w owns tile columns [4 w, 4 w + 4)
+// of all 4 rows: 4 x 4 accumulators of 32 x 32 (products D[q][p] += X^T . dY with A = X fragments
+// and B = dY fragments, so each lane ends with 4 consecutive q of one p). Every one of the 64
+// products is computed, absent blocks included, and only kept blocks are written: one code path,
+// no per-block branches around the matrix-core chain. Per 32-row step, the 4 rows' dY segments
+// (32 rows x 4 x 64 bytes, 8 KB) and the 16 columns' X segments (32 rows x 16 x 64 bytes, 16 KB
+// ... 32 KB) are staged by direct-to-LDS loads, 4 stages deep (the 160 KB of LDS): the loads of
+// step s + 4 are issued during step s, after every wave has read step s. A lane's source offset
+// within a row is the same for every step, so it is computed once; the row part is a wave-uniform
+// add. Loads past the chunk's rows read zeros (the buffer resources cover exactly the chunk's
+// rows), which is also how the last steps' surplus loads stay harmless. Unused rows and columns
+// of a tile read row or column 0: they only feed products that are dropped. Fragments come from
+// transposing LDS reads; the 16-byte chunks of each staged row are XOR swizzled by 4 (row % 4),
+// which keeps the reads of 4 consecutive rows per 16 lanes on distinct banks. Per 16-deep chunk a
+// wave reads 4 + 4 fragments for 16 products.
+// With one chunk of rows the sums are rounded to bf16 directly (staged through LDS, stored as
+// 16-byte pieces of whole block rows); otherwise fp32 partials go to the workspace at the blocks'
+// compact indices.
+// ------------------------------------------------------------------------------------------
+constexpr int kDwStep = 32;                        // activation rows per staged step
+constexpr int kDwDYB = kDwStep * kWdwRows * 64;    // staged dY: 8 KB
+constexpr int kDwXB = kDwStep * kWdwCols * 64;     // staged X: 32 KB
+constexpr int kDwStage = kDwDYB + kDwXB;           // 40 KB
+constexpr int kDwStages = 4;
+static_assert(kDwStages * kDwStage <= 160 * 1024, "LDS of one work-group");
+constexpr int kDwLoads = (kDwDYB + kDwXB) / 1024 / 4;   // direct-to-LDS loads per wave and step (10)
+
+struct WdwOut {
+    uint16_t *dV;       // bf16 blocks (one chunk of rows)
+    float *partial;     // or fp32 partials [chunk][P2][1024] at compact index - cbase
+    int ch, P2, cbase;
+};
+
+__device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X,
+                                             int K, const int32_t *__restrict__ it, int m_begin, int rows,
+                                             const WdwOut &o, unsigned char *smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dY + (size_t)m_begin * N, (uint32_t)((size_t)rows * N * 2));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)m_begin * K, (uint32_t)((size_t)rows * K * 2));
+    const uint32_t sbase = lds_addr(smem);
+    const int nsteps = (rows + kDwStep - 1) / kDwStep;
+
+    // Loads of step `step` into stage st, 10 per wave. dY loads d = wave, wave + 4 (1 KB each: 4
+    // activation rows x 4 block rows x 64 bytes): lane -> activation row 4 d + lane / 16, staged
+    // chunk lane % 16 of that row, which holds source chunk (lane % 16) ^ 4 (lane / 16) (block row
+    // of the tile = source chunk / 4, 16-byte piece = source chunk % 4). X loads x = wave + 4 k,
+    // k < 8 (one activation row of 1 KB each): staged chunk lane holds source chunk lane ^ 4 wave
+    // (x % 4 = wave; tile column = source chunk / 4).
+    const int dsrc = (lane & 15) ^ ((lane >> 4) << 2);
+    const uint32_t dlane = (uint32_t)(lane >> 4) * (uint32_t)N * 2u + (uint32_t)max(it[dsrc >> 2], 0) * 64u +
+                           (uint32_t)(dsrc & 3) * 16u;
+    const int xsrc = lane ^ (wave << 2);
+    const uint32_t xlane = (uint32_t)max(it[4 + (xsrc >> 2)], 0) * 64u + (uint32_t)(xsrc & 3) * 16u;
+    auto issue = [&](int st, int step, int k) __attribute__((always_inline)) {
+        const uint32_t base = sbase + (uint32_t)st * kDwStage;
+        if (k < 2) {
+            const int d = wave + 4 * k;
+            dma16(rd, base + (uint32_t)d * 1024u, dlane + (uint32_t)(step * kDwStep + 4 * d) * (uint32_t)N * 2u, 0);
+        } else {
+            const int x = wave + 4 * (k - 2);
+            dma16(rx, base + kDwDYB + (uint32_t)x * 1024u, xlane + (uint32_t)(step * kDwStep + x) * (uint32_t)K * 2u, 0);
+        }
+    };
+
+    // T[k0 + 8 (l / 32) .. + 7][n0 + l % 32] of a staged tile (rows of `pitch` bytes) for lane l:
+    // two transposing reads of 4 rows (lane s of a 16-lane group points at row R + s / 4, columns
+    // C .. C + 3: 8 bytes inside one 16-byte chunk)
+    auto frag = [&](const unsigned char *tile, int pitch, int k0, int n0) __attribute__((always_inline)) {
+        const int gq = lane >> 4, s16 = lane & 15;
+        const int R = k0 + (gq >> 1) * 8 + (s16 >> 2);
+        const int C = n0 + (gq & 1) * 16 + 4 * (s16 & 3);
+        auto at = [&](int row) {
+            return (lds_i16x4 *)(tile + row * pitch + ((((C >> 3) ^ ((row & 3) << 2)) << 4) | ((C & 7) << 1)));
+        };
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(R + 4));
+        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    f32x16 acc[kWdwRows][4];   // [block row t][column jj of the wave]
+#pragma unroll
+    for (int t = 0; t < kWdwRows; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[t][jj][v] = 0.f;
+
+    bf16x8 fa[2][4], fb[2][4];   // [set][jj]: X fragments (A); [set][t]: dY fragments (B)
+    auto read_frags = [&](int set, int st, int kc) __attribute__((always_inline)) {
+        const unsigned char *dt = smem + st * kDwStage, *xt = dt + kDwDYB;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) fa[set][jj] = frag(xt, kWdwCols * 64, kc * 16, (4 * wave + jj) * 32);
+#pragma unroll
+        for (int t = 0; t < kWdwRows; ++t) fb[set][t] = frag(dt, kWdwRows * 64, kc * 16, t * 32);
+    };
+    auto products = [&](int set, auto &&after) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < kWdwRows; ++t) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = mfma32(fa[set][jj], fb[set][t], acc[t][jj]);
+            __builtin_amdgcn_sched_barrier(0);
+            after(t);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Step pipeline: before step s the stages hold steps s .. s + 3 (landed or in flight) and
+    // fragment set 0 holds chunk 0 of s. Step s: read chunk 1, products of chunk 0 with the second
+    // half of the loads of s + 3 issued in between (into the stage of s - 1, free since the last
+    // barrier); wait for every LDS read of s and for this wave's loads of s + 1 (loads complete in
+    // issue order, so those of s + 2 and s + 3 may stay in flight); barrier (s + 1 published, stage
+    // of s free); read chunk 0 of s + 1; products of chunk 1 with the first half of the loads of
+    // s + 4 issued in between into the stage of s. The issue of a direct-to-LDS load holds the wave
+    // while the compute unit's load path is busy (about 64 bytes a clock), so the loads go out one or
+    // two at a time between groups of 4 products. Steps past the chunk load zeros, so the loop has
+    // no tail cases.
+    constexpr int kHalf = kDwLoads / 2;
+    static_assert(kDwLoads == 10 && kHalf == 5, "the product groups below issue 5 loads per half step");
+    auto spread = [&](int stage, int step, int k0) __attribute__((always_inline)) {
+        // 5 loads over the 4 product groups: 2, 1, 1, 1
+        return [=, &issue](int t) __attribute__((always_inline)) {
+            const int a = t == 0 ? 0 : t + 1, b = t + 2;
+#pragma unroll
+            for (int k = a; k < b; ++k) issue(stage, step, k0 + k);
+        };
+    };
+#pragma unroll
+    for (int q = 0; q < kDwStages; ++q)
+#pragma unroll
+        for (int k = 0; k < (q < kDwStages - 1 ? kDwLoads : kHalf); ++k) issue(q, q, k);
+    // step 0 landed: the loads of steps 1 .. kDwStages - 2 and the first half of kDwStages - 1 may
+    // stay in flight
+    constexpr int kPrologueFlight = (kDwStages - 2) * kDwLoads + kHalf;
+    wait_vm<kPrologueFlight, kPrologueFlight>(0);
+    __syncthreads();
+    read_frags(0, 0, 0);
+    for (int s = 0; s < nsteps; ++s) {
+        const int st = s % kDwStages;
+        read_frags(1, st, 1);
+        products(0, spread((s + kDwStages - 1) % kDwStages, s + kDwStages - 1, kHalf));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vm<(kDwStages - 2) * kDwLoads, (kDwStages - 2) * kDwLoads>(0);
+        __syncthreads();
+        read_frags(0, (s + 1) % kDwStages, 0);
+        products(1, spread(st, s + kDwStages, 0));
+    }
+    wait_vm<0, 0>(0);
+    __syncthreads();   // the stages are free for the output staging
+
+    // Item v of lane l of acc[t][jj]: D[q][p] with q = 8 (v / 4) + 4 (l / 32) + v % 4 (block column
+    // of dV), p = l % 32 (block row): 4 consecutive q of one p.
+    if (o.partial) {
+#pragma unroll
+        for (int t = 0; t < kWdwRows; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int c = it[kWdwCompactAt + 16 * t + 4 * wave + jj];
+                if (c < 0) continue;
+                float *dst = o.partial + ((size_t)o.ch * o.P2 + (c - o.cbase)) * 1024 + l32 * 32 + 4 * lh;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4 *>(dst + 8 * q4) = quad(acc[t][jj], q4);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        return;
+    }
+    // bf16: wave's 16 blocks staged as [slot][32 rows][64 + 16 bytes], then 16-byte stores
+    constexpr int BP = 80;                          // staged block row pitch (bytes)
+    unsigned char *wst = smem + wave * 16 * 32 * BP;
+#pragma unroll
+    for (int t = 0; t < kWdwRows; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 v = quad(acc[t][jj], q4);
+                store4_bf16(reinterpret_cast<uint16_t *>(wst + (4 * t + jj) * 32 * BP + l32 * BP + (8 * q4 + 4 * lh) * 2),
+                            v[0], v[1], v[2], v[3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    // (each wave reads back only what it wrote: no barrier needed beyond the wave's own LDS ordering)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+        const int seg = i * 64 + lane, slot = seg >> 7, rowp = (seg >> 2) & 31, piece = seg & 3;
+        const int e = it[kWdwBlockAt + 16 * (slot >> 2) + 4 * wave + (slot & 3)];
+        if (e < 0) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(wst + slot * 32 * BP + rowp * BP + piece * 16);
+        *reinterpret_cast<u32x4 *>(o.dV + (size_t)e * 1024 + rowp * 32 + piece * 8) = val;
+    }
+}
+
+// Work-groups go to the XCDs round robin (XCD = blockIdx % 8), so that each XCD gets an equal
+// share of both kinds of work in its first round: XCD x runs, in order, its contiguous run of the
+// first n1 items (whole rows range each), then its contiguous run of the n2 x c2 (chunk, item) pairs
+// of the other items (items fastest). Work-groups past an XCD's share exit at once.
+__global__ __launch_bounds__(256, 1) void k_wide_dw(const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X,
+                                                    int K, int M, const int32_t *__restrict__ items, int n1, int n2,
+                                                    int c2, int mchunk, int cbase, int P2,
+                                                    float *__restrict__ partial, uint16_t *__restrict__ dV) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kDwStages * kDwStage];
+    const int x = blockIdx.x % kXCDs, i = blockIdx.x / kXCDs;
+    const int a0 = (int)((int64_t)n1 * x / kXCDs), a = (int)((int64_t)n1 * (x + 1) / kXCDs) - a0;
+    int item, m_begin = 0, rows = M;
+    WdwOut o{dV, nullptr, 0, P2, cbase};
+    if (i < a) {
+        item = a0 + i;
+    } else {
+        const int64_t n2c = (int64_t)n2 * c2;
+        const int64_t b0 = n2c * x / kXCDs, b = n2c * (x + 1) / kXCDs - b0;
+        const int64_t j = i - a;
+        if (j >= b) return;
+        const int64_t g = b0 + j;
+        o.ch = (int)(g / n2);
+        item = n1 + (int)(g % n2);
+        m_begin = o.ch * mchunk;
+        rows = min(M - m_begin, mchunk);
+        if (c2 > 1) o.partial = partial;
+    }
+    wide_dw_tile(dY, N, X, K, items + (size_t)item * kWdwItemInts, m_begin, rows, o, smem);
+}
+
+// dV of the blocks of the split items: the fixed-order sum of their fp32 partials over the chunks.
+// Thread = 4 values of one block (compact index cbase + c).
+__global__ __launch_bounds__(256) void k_wide_dw_reduce(const float *__restrict__ partial, int nchunks, int P2,
+                                                        int cbase, const int32_t *__restrict__ compact,
+                                                        uint16_t *__restrict__ dV) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)P2 * 256) return;
+    const int64_t c = idx >> 8, v = (idx & 255) * 4;
+    const size_t stride = (size_t)P2 * 1024;
+    const float *src = partial + c * 1024 + v;
+    f32x4 s = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+    for (int ch = 1; ch < nchunks; ++ch)
+        s += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + (size_t)ch * stride));
+    store4_bf16(dV + (size_t)compact[cbase + c] * 1024 + v, s[0], s[1], s[2], s[3]);
+}
+
 int wide_tiles_per_chunk(int nmtiles) {
     int t = 4;
     if (const char *f = std::getenv("BSR_WIDE_TPC")) t = std::atoi(f);   // tuning knob
@@ -320,6 +569,115 @@ bool use_wide(const bsr_pattern &p, bool transposed, int64_t M) {
     if (nsub == 0 || M < kWideRows) return false;
     // dense groups: on average at least half of a sub-step's 16 units keep a block
     return (double)s.nunits >= 8.0 * (double)nsub;
+}
+
+// Splits of the wide weight-gradient items for M activation rows. A model of one XCD (32 compute
+// units, one work-group each, work-groups placed in order on the unit that frees first) gives the
+// finishing time, in 32-row steps, of its share of the first n1 items (whole: ceil(M / 32) steps
+// each) and of the (chunk, item) pairs of the rest (mchunk / 32 steps each), plus a few steps per
+// work-group for its prologue and epilogue; the partials of split items cost their bytes (written
+// once, read once) at about 2 MB per step, plus a reduction launch. The candidates keep the dense
+// items whole, or split every item, into 1 .. 16 chunks of at least 256 rows; the cheapest wins
+// (ties: fewer chunks).
+WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M) {
+    const WideDwSchedule &s = p.wdw;
+    WideDwPlan best;
+    if (s.n == 0 || M <= 0) return best;
+    constexpr int64_t kExtra = 6;   // prologue and epilogue of a work-group, in steps
+    constexpr int kUnits = kCUs / kXCDs;
+    const int64_t steps = (M + 31) / 32;
+    auto xcd_time = [&](int64_t a, int64_t la, int64_t b, int64_t lb) {
+        std::vector<std::pair<int64_t, int64_t>> free_at = {{0, kUnits}};   // (time, units)
+        auto place = [&](int64_t jobs, int64_t len) {
+            while (jobs > 0) {
+                size_t k = 0;
+                for (size_t q = 1; q < free_at.size(); ++q)
+                    if (free_at[q].first < free_at[k].first) k = q;
+                const int64_t t = free_at[k].first, c = free_at[k].second, use = std::min(jobs, c);
+                if (use == c) free_at.erase(free_at.begin() + (long)k);
+                else free_at[k].second -= use;
+                bool merged = false;
+                for (auto &f : free_at)
+                    if (f.first == t + len) f.second += use, merged = true;
+                if (!merged) free_at.push_back({t + len, use});
+                jobs -= use;
+            }
+        };
+        place(a, la);
+        place(b, lb);
+        int64_t last = 0;
+        for (auto &f : free_at) last = std::max(last, f.first);
+        return last;
+    };
+    double best_cost = 0;
+    bool have = false;
+    for (int n1 : {s.ndense, 0}) {
+        if (have && n1 == 0 && s.ndense == 0) break;
+        for (int c2 = 1; c2 <= 16; ++c2) {
+            const int64_t mchunk = ((M + c2 - 1) / c2 + 31) / 32 * 32;
+            if (c2 > 1 && mchunk < 256) break;
+            const int c2e = (int)((M + mchunk - 1) / mchunk);
+            if (c2 > 1 && c2e != c2) continue;
+            const int n2 = s.n - n1;
+            int64_t t = 0;
+            for (int x = 0; x < kXCDs; ++x) {
+                const int64_t a = (int64_t)n1 * (x + 1) / kXCDs - (int64_t)n1 * x / kXCDs;
+                const int64_t n2c = (int64_t)n2 * c2e;
+                const int64_t b = n2c * (x + 1) / kXCDs - n2c * x / kXCDs;
+                t = std::max(t, xcd_time(a, steps + kExtra, b, mchunk / 32 + kExtra));
+            }
+            const int64_t P2 = s.first[s.n] - s.first[n1];
+            const double cost = (double)t + (c2e > 1 ? (double)P2 * c2e * 8192.0 / 2.0e6 + 8.0 : 0.0);
+            if (!have || cost < best_cost) {
+                have = true;
+                best_cost = cost;
+                best.n1 = n1;
+                best.n2 = n2;
+                best.c2 = c2e;
+                best.mchunk = (int)(c2e > 1 ? mchunk : M);
+                best.cbase = s.first[n1];
+                best.P2 = (int)P2;
+            }
+            if (n2 == 0) break;
+        }
+    }
+    if (const char *f = std::getenv("BSR_WDW_SPLIT")) {   // tuning knob: "n1,c2"
+        int n1 = 0, c2 = 1;
+        if (std::sscanf(f, "%d,%d", &n1, &c2) == 2 && n1 >= 0 && n1 <= s.n && c2 >= 1) {
+            const int64_t mchunk = ((M + c2 - 1) / c2 + 31) / 32 * 32;
+            best.n1 = n1;
+            best.n2 = s.n - n1;
+            best.c2 = (int)((M + mchunk - 1) / mchunk);
+            best.mchunk = (int)(best.c2 > 1 ? mchunk : M);
+            best.cbase = s.first[n1];
+            best.P2 = s.first[s.n] - s.first[n1];
+        }
+    }
+    return best;
+}
+
+int32_t launch_wide_dw(const bsr_pattern &p, const DwArgs &a, const WideDwPlan &w, float *partial, void *stream) {
+    if (p.wdw.n == 0) return BSR_OK;
+    const hipStream_t st = (hipStream_t)stream;
+    int most = 0;
+    for (int x = 0; x < kXCDs; ++x) {
+        const int64_t n2c = (int64_t)w.n2 * w.c2;
+        const int64_t share = (int64_t)w.n1 * (x + 1) / kXCDs - (int64_t)w.n1 * x / kXCDs + n2c * (x + 1) / kXCDs -
+                              n2c * x / kXCDs;
+        most = (int)std::max<int64_t>(most, share);
+    }
+    if (most == 0) return BSR_OK;
+    hipLaunchKernelGGL(k_wide_dw, dim3((unsigned)(most * kXCDs)), dim3(256), 0, st, a.dY, p.N, a.X, p.K, (int)a.M,
+                       p.dev.wdw_items, w.n1, w.n2, w.c2, w.mchunk, w.cbase, w.P2, partial, a.dV);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide weight-gradient launch: ") + hipGetErrorString(e));
+    if (w.c2 > 1 && w.P2 > 0) {
+        hipLaunchKernelGGL(k_wide_dw_reduce, dim3((unsigned)(((int64_t)w.P2 * 256 + 255) / 256)), dim3(256), 0, st,
+                           partial, w.c2, w.P2, w.cbase, p.dev.wdw_compact, a.dV);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide weight-gradient reduce: ") + hipGetErrorString(e));
+    }
+    return BSR_OK;
 }
 
 int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream) {

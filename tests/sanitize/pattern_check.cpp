@@ -112,10 +112,98 @@ static void check_pattern(const bsr_pattern &p) {
         check_groups(p.fwd[k], p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.b, n);
         check_groups(p.bwd[k], p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, n);
     }
-    // weight-gradient items: every kept block once, inside its item's tile
+    // wide panel-GEMM schedules (b = 32): one sub-step per panel any member keeps a block in;
+    // every kept block once, at slot 2 t + (block % 2) of its member t; dense flags exact
+    if (p.b == 32) {
+        for (int dir = 0; dir < 2; ++dir) {
+            const WideSchedule &s = dir ? p.wide_bwd : p.wide_fwd;
+            const std::vector<int32_t> &ptr = dir ? p.col_ptr : p.row_ptr, &idx = dir ? p.row_idx : p.col_idx;
+            const int32_t nout = (int32_t)ptr.size() - 1;
+            REQUIRE(s.ngroups == (nout + kWideG - 1) / kWideG);
+            REQUIRE((size_t)s.nsub() * kWideRecInts == s.rec.size() && (int)s.flags.size() == s.ngroups);
+            std::vector<int> seen(n, 0), oseen(nout, 0);
+            int64_t units = 0;
+            for (int g = 0; g < s.ngroups; ++g) {
+                bool dense = s.sub_ptr[g + 1] > s.sub_ptr[g];
+                for (int32_t k = s.sub_ptr[g]; k < s.sub_ptr[g + 1]; ++k) {
+                    const int32_t *r = &s.rec[(size_t)k * kWideRecInts];
+                    if (k > s.sub_ptr[g]) REQUIRE(r[0] > r[-kWideRecInts]);
+                    dense = dense && (uint32_t)r[1] == 0xFFFFu;
+                    REQUIRE(r[1] != 0);
+                    for (int u = 0; u < kWideU; ++u) {
+                        const bool present = (r[1] >> u) & 1;
+                        REQUIRE(present == (r[2 + u] >= 0));
+                        if (!present) continue;
+                        const int32_t o = s.out[(size_t)g * kWideG + u / 2];
+                        REQUIRE(o >= 0 && o < nout);
+                        if (o < 0 || o >= nout) continue;
+                        const int32_t want = r[0] * 2 + u % 2;
+                        int32_t e = -1;
+                        for (int32_t q = ptr[o]; q < ptr[o + 1]; ++q)
+                            if (idx[q] == want) e = dir ? p.perm[q] : q;
+                        REQUIRE(e >= 0 && r[2 + u] == e);
+                        if (e >= 0) seen[e]++;
+                        ++units;
+                    }
+                }
+                REQUIRE(s.flags[g] == (dense ? 1 : 0));
+                for (int t = 0; t < kWideG; ++t) {
+                    const int32_t o = s.out[(size_t)g * kWideG + t];
+                    if (o >= 0 && o < nout) oseen[o]++;
+                }
+            }
+            REQUIRE(units == s.nunits && units == n);
+            for (int32_t i = 0; i < n; ++i) REQUIRE(seen[i] == 1);
+            for (int32_t o = 0; o < nout; ++o) REQUIRE(oseen[o] == 1);
+        }
+    } else {
+        REQUIRE(p.wide_fwd.ngroups == 0 && p.wide_bwd.ngroups == 0 && p.wdw.n == 0);
+    }
+    // weight-gradient items: every kept block exactly once over the wide items and the tile items
+    // (no tile items once there are wide ones); a wide item's blocks are exactly the kept blocks of
+    // its rows x columns that it claims, rows and columns distinct, dense items whole 4 x 16 tiles
+    // of consecutive columns; compact indices number the blocks in item order
     const int TR = dw_tile_rows(p.b), TC = dw_tile_cols(p.b), SL = dw_slots(p.b);
     REQUIRE((size_t)p.dw.n * kDwItemInts == p.dw.items.size());
+    REQUIRE((size_t)p.wdw.n * kWdwItemInts == p.wdw.items.size());
+    if (p.wdw.n > 0) {
+        REQUIRE(p.b == 32 && p.dw.n == 0);
+        REQUIRE((int)p.wdw.compact.size() == n && (int)p.wdw.first.size() == p.wdw.n + 1);
+        REQUIRE(p.wdw.ndense > 0 && p.wdw.ndense <= p.wdw.n);
+    }
     std::fill(hit.begin(), hit.end(), 0);
+    int32_t next = 0;
+    for (int it = 0; it < p.wdw.n; ++it) {
+        const int32_t *x = &p.wdw.items[(size_t)it * kWdwItemInts];
+        REQUIRE(p.wdw.first[it] == next);
+        for (int t = 0; t < kWdwRows; ++t) {
+            REQUIRE(x[t] >= -1 && x[t] < R);
+            for (int u = 0; u < t; ++u) REQUIRE(x[t] < 0 || x[t] != x[u]);
+        }
+        for (int j = 0; j < kWdwCols; ++j) {
+            REQUIRE(x[4 + j] >= -1 && x[4 + j] < C);
+            for (int u = 0; u < j; ++u) REQUIRE(x[4 + j] < 0 || x[4 + j] != x[4 + u]);
+        }
+        const bool dense = it < p.wdw.ndense;
+        int cnt = 0;
+        for (int t = 0; t < kWdwRows; ++t)
+            for (int j = 0; j < kWdwCols; ++j) {
+                const int32_t e = x[kWdwBlockAt + 16 * t + j], c = x[kWdwCompactAt + 16 * t + j];
+                REQUIRE((e >= 0) == (c >= 0));
+                if (dense) REQUIRE(e >= 0 && x[4 + j] == x[4] + j && x[4] % kWdwCols == 0);
+                if (e < 0) continue;
+                ++cnt;
+                const int32_t r = x[t], col = x[4 + j];
+                REQUIRE(r >= 0 && col >= 0 && e < n);
+                if (r < 0 || col < 0 || e >= n) continue;
+                hit[e]++;
+                REQUIRE(p.col_idx[e] == col && e >= p.row_ptr[r] && e < p.row_ptr[r + 1]);
+                REQUIRE(c == next && p.wdw.compact[c] == e);
+                ++next;
+            }
+        REQUIRE(cnt > 0);
+    }
+    if (p.wdw.n > 0) REQUIRE(p.wdw.first[p.wdw.n] == next && next == n);
     for (int it = 0; it < p.dw.n; ++it) {
         const int32_t *x = &p.dw.items[(size_t)it * kDwItemInts];
         const int32_t r0 = x[0], c0 = x[1];

@@ -104,3 +104,52 @@ def test_wide_is_deterministic(monkeypatch):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
     p.close()
+
+
+# ---- the wide weight gradient (dense tiles of 4 full block rows x 16 consecutive block columns,
+# then gathered tiles of any 4 rows x any 16 columns taking every other block) ----
+
+@pytest.mark.parametrize("M,R,C,nfull,seed", [
+    (300, 21, 40, 9, 7),      # 21 rows: 2 dense row groups, 8 leftover columns, gathered rows
+    (1000, 12, 32, 8, 8),     # gathered items split over row chunks (fp32 partials + reduce); M ragged
+    (4133, 16, 16, 16, 9),    # every block kept: every tile dense
+    (97, 9, 24, 5, 10),       # M below one 32-row step past 64, ragged steps
+    (1, 8, 16, 8, 11),        # one activation row: 31 rows of each step read as zeros
+    (45, 10, 20, 6, 12),      # 45 rows, 20 columns (a partial 16-column gather)
+])
+def test_wide_dw_matches_oracle(M, R, C, nfull, seed):
+    b = 32
+    mask = mixed_mask(R, C, nfull, seed, empty_rows=(R - 1,) if nfull < R else ())
+    say(f"case wide dW M={M} R={R} C={C} full={nfull} nnzb={int(mask.sum())}")
+    host = case_inputs(M, R * b, C * b, b, seed, mask=mask, bias=True)
+    full_parity(M, R * b, C * b, b, host, ops=("dw",), dbias=True)
+
+
+def test_wide_dw_integer_inputs_bit_exact():
+    """Small-integer activations and gradients: every fp32 sum over the rows is exact, so dV equals
+    the oracle bit for bit, through both the dense and the gathered wide tiles."""
+    M, R, C, b = 700, 10, 32, 32
+    mask = mixed_mask(R, C, 6, 11)
+    g = np.random.default_rng(11)
+    X = torch.from_numpy(g.integers(-2, 3, size=(M, C * b)).astype(np.float32)).to(torch.bfloat16)
+    dY = torch.from_numpy(g.integers(-1, 2, size=(M, R * b)).astype(np.float32)).to(torch.bfloat16)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, R * b, C * b, b)
+    dV, _ = binding.linear_bwd_weight(p, dY.to(dev()), X.to(dev()))
+    torch.cuda.synchronize()
+    ref, _ = oracle.dw(dY, X, md["row_ptr"], md["col_idx"], b)
+    assert np.array_equal(dV.cpu().double().numpy(), ref)
+    p.close()
+
+
+def test_wide_dw_is_deterministic():
+    M, R, C, b = 2048, 16, 32, 32
+    mask = mixed_mask(R, C, 10, 12)
+    host = case_inputs(M, R * b, C * b, b, 12, mask=mask)
+    p = Pattern.from_mask(mask, R * b, C * b, b)
+    X, dY = host["X"].to(dev()), host["dY"].to(dev())
+    a1, _ = binding.linear_bwd_weight(p, dY, X)
+    a2, _ = binding.linear_bwd_weight(p, dY, X)
+    torch.cuda.synchronize()
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
+    p.close()

@@ -70,8 +70,8 @@ def test_noalloc_refuses_sizes_above_the_scratch_array():
     """A pattern and M whose split-M partials need more than the scratch array: refused with
     BSR_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the outputs keep their contents)."""
     N = K = 2048
-    b, M = 32, 4096
-    host = case_inputs(M, N, K, b, 42, density=0.5)
+    b, M = 64, 4096   # 64 x 64 blocks at density 0.6: 5 row chunks of fp32 partials, 38.5 MiB
+    host = case_inputs(M, N, K, b, 42, density=0.6)
     p = Pattern.from_mask(host["mask"], N, K, b)
     need = binding.bwd_weight_workspace_bytes(p, M)
     assert need > _scratch_bytes(), need
