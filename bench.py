@@ -60,9 +60,9 @@ def op_bytes(w, nnzb: int, op: str, bias: bool) -> int:
     raise ValueError(op)
 
 
-KERNEL_SOURCES = ("sparse_gemm_amd/csrc/bsr_kernels.hip", "sparse_gemm_amd/csrc/bsr_pattern.cpp",
+KERNEL_SOURCES = ("sparse_gemm_amd/csrc/bsr_kernels.hip", "sparse_gemm_amd/csrc/bsr_wide.hip",
+                  "sparse_gemm_amd/csrc/bsr_device.hpp", "sparse_gemm_amd/csrc/bsr_pattern.cpp",
                   "sparse_gemm_amd/csrc/bsr_internal.hpp")
-OP_KERNELS = {"fwd": ("k_panel_gemm", "k_small_m"), "dx": ("k_panel_gemm",), "dw": ("k_dw_panel", "k_dw_reduce")}
 
 
 def op_of_kernel(name: str):
@@ -78,9 +78,12 @@ def op_of_kernel(name: str):
         if len(args) >= 9 and args[8] == "true":
             return None
         return "dx" if len(args) >= 8 and args[7] == "true" else "fwd"
+    if "k_wide_gemm" in name:
+        # template argument <TRANS>: the input gradient when true
+        return "dx" if "k_wide_gemm<true>" in name else "fwd"
     if "k_small_m" in name:
         return "fwd"
-    if "k_dw_panel" in name or "k_dw_reduce" in name or "k_colsum" in name:
+    if any(k in name for k in ("k_dw_panel", "k_dw_reduce", "k_wide_dw", "k_colsum")):
         return "dw"
     return None
 COPY_BYTES = 256 << 20   # plain copy used to calibrate the HBM byte counters
@@ -416,14 +419,10 @@ def time_launches(fn, nsets: int, reps: int) -> float:
     return a.elapsed_time(b) / reps
 
 
-def op_kernels(w, op: str):
-    """Library kernels one launch of the op runs at this workload (the dispatch of bsr_abi.cpp)."""
-    if op == "fwd":
-        small = (w.M <= 64) if w.b == 64 else (w.M <= 32)
-        return ["k_small_m"] if small else ["k_panel_gemm"]
-    if op == "dx":
-        return ["k_panel_gemm"]
-    return list(OP_KERNELS["dw"])
+def op_kernels(p, w, op: str):
+    """Library kernels one launch of the op runs at this workload, as the library dispatches them."""
+    from sparse_gemm_amd import binding
+    return binding.op_kernels(p, op, w.M)
 
 
 def roofline_of(w, nnzb: int, op: str, t_s: float, traffic) -> dict:
@@ -473,7 +472,7 @@ def measure(w, host, dev, nsteps: int, warmup: int, warm: bool, extras: bool, la
         per_op[op] = {"us": op_alone[op] * 1e3, "us_in_step": op_in_step[op] * 1e3,
                       "tflops": F / t / 1e12, "pct_mfma_peak": 100 * F / t / 1e12 / PEAK_BF16_TFLOPS,
                       "gbs": by / t / 1e9, "pct_hbm_peak": 100 * by / t / 1e9 / PEAK_HBM_GBS, "bytes": by,
-                      "pct_roofline": 100 * t_roof / t, "kernels": op_kernels(w, op)}
+                      "pct_roofline": 100 * t_roof / t, "kernels": op_kernels(p, w, op)}
         if op in pct:
             per_op[op].update({"p10_us_in_step": pct[op][0] * 1e3, "median_us_in_step": pct[op][1] * 1e3,
                                "p90_us_in_step": pct[op][2] * 1e3})
@@ -481,7 +480,7 @@ def measure(w, host, dev, nsteps: int, warmup: int, warm: bool, extras: bool, la
     roof = roofline_of(w, nnzb, dom, op_alone[dom] * 1e-3, tr.get(dom) if tr else None)
     roof["kernel"] = {"fwd": "bsr_linear_fwd", "dx": "bsr_linear_bwd_input", "dw": "bsr_linear_bwd_weight"}[dom]
     roof["per_launch"] = {"flops": F, "algorithmic_bytes": op_bytes(w, nnzb, dom, w.bias),
-                          "avg_us": op_alone[dom] * 1e3, "kernels": op_kernels(w, dom),
+                          "avg_us": op_alone[dom] * 1e3, "kernels": op_kernels(p, w, dom),
                           "timing": "back-to-back launches over the rotated buffer sets, HIP events on the "
                                     "launch stream, queue pre-filled behind a spin kernel"}
     res = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.b, "density": w.density, "nnzb": nnzb,

@@ -19,7 +19,7 @@ STATUS = {0: "BSR_OK", 1: "BSR_ERR_INVALID_ARG", 2: "BSR_ERR_UNSUPPORTED", 3: "B
 EXPORTS = ("bsr_abi_version", "bsr_pattern_create_from_mask", "bsr_pattern_create_from_csr",
            "bsr_pattern_info", "bsr_pattern_export", "bsr_pattern_destroy", "bsr_linear_fwd",
            "bsr_linear_bwd_input", "bsr_linear_bwd_weight_workspace", "bsr_linear_bwd_weight",
-           "bsr_linear_bwd_weight_noalloc",
+           "bsr_linear_bwd_weight_noalloc", "bsr_op_kernels",
            "bsr_status_string", "bsr_last_error",
            # include/bsr_convert.h
            "bsr_block_norms", "bsr_mask_topk", "bsr_pattern_create_from_dense", "bsr_dense_to_values",
@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
     L.bsr_linear_fwd.argtypes = [P, P, i64, P, P, P, P]
     L.bsr_linear_bwd_input.argtypes = [P, P, i64, P, P, P]
     L.bsr_linear_bwd_weight_workspace.argtypes, L.bsr_linear_bwd_weight_workspace.restype = [P, i64], sz
+    L.bsr_op_kernels.argtypes, L.bsr_op_kernels.restype = [P, i32, i64, ctypes.c_char_p, i32], i32
     L.bsr_linear_bwd_weight.argtypes = [P, P, P, i64, P, P, P, sz, P]
     L.bsr_linear_bwd_weight_noalloc.argtypes = [P, P, P, i64, P, P, P]
     L.bsr_block_norms.argtypes = [i32, i32, i32, P, i32, P, P]

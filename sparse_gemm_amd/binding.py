@@ -181,6 +181,16 @@ def bwd_weight_workspace_bytes(p: Pattern, M: int) -> int:
     return int(lib().bsr_linear_bwd_weight_workspace(p.handle, int(M)))
 
 
+def op_kernels(p: Pattern, op: str, M: int) -> list:
+    """Names of the main kernels one call of op ("fwd", "dx" or "dw") launches for M rows (the
+    bias gradient's excluded), as the library dispatches them."""
+    code = {"fwd": 0, "dx": 1, "dw": 2}[op]
+    buf = ctypes.create_string_buffer(256)
+    _lib.check(lib().bsr_op_kernels(p.handle, code, int(M), buf, len(buf)), "bsr_op_kernels")
+    names = buf.value.decode()
+    return names.split(",") if names else []
+
+
 def linear_bwd_weight(p: Pattern, dY: torch.Tensor, X: torch.Tensor, want_dbias: bool = False,
                       out: Optional[torch.Tensor] = None, dbias: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None):

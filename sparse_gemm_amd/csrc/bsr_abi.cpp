@@ -128,6 +128,16 @@ int32_t check_ptr(const void *ptr, const char *name, bool nullable = false) {
     return BSR_OK;
 }
 
+// The streaming small-M kernel (up to four 16-row tiles per work-group) beats the panel GEMM up to
+// 64 rows for b = 64 (decode weight 8 x 4096 -> 14336: 17 rows 36.8 -> 16.1 us, 32 rows 37.1 -> 19.2,
+// 64 rows 37.4 -> 29.5; 96 rows 46.8 against 37.5) and up to 32 rows for b = 32 (BERT-base FFN-up
+// weight: 6.2 -> 4.1-4.4 us; even at 48 rows, behind from 64).
+int64_t small_m_max(const bsr_pattern &p) {
+    int64_t small_max = p.b == 64 ? 4 * kSmallM : 2 * kSmallM;
+    if (const char *f = std::getenv("BSR_SMALLM_MAX")) small_max = std::atoll(f);   // tuning knob
+    return small_max;
+}
+
 }  // namespace
 
 }  // namespace bsr
@@ -233,13 +243,7 @@ int32_t bsr_linear_fwd(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const
     BSR_CHECK(check_ptr(Y, "Y", M == 0));
     if (M == 0) return BSR_OK;
     FwdArgs a{X, M, p->K, V, bias, Y, p->N};
-    // The streaming small-M kernel (up to four 16-row tiles per work-group) beats the panel GEMM up to
-    // 64 rows for b = 64 (decode weight 8 x 4096 -> 14336: 17 rows 36.8 -> 16.1 us, 32 rows 37.1 ->
-    // 19.2, 64 rows 37.4 -> 29.5; 96 rows 46.8 against 37.5) and up to 32 rows for b = 32 (BERT-base
-    // FFN-up weight: 6.2 -> 4.1-4.4 us; even at 48 rows, behind from 64).
-    int64_t small_max = p->b == 64 ? 4 * kSmallM : 2 * kSmallM;
-    if (const char *f = std::getenv("BSR_SMALLM_MAX")) small_max = std::atoll(f);   // tuning knob
-    if (M <= small_max) return launch_small_m_fwd(*p, a, stream);
+    if (M <= small_m_max(*p)) return launch_small_m_fwd(*p, a, stream);
     return launch_group_gemm(*p, false, a, stream);
     BSR_TRY_END
 }
@@ -254,6 +258,19 @@ int32_t bsr_linear_bwd_input(const bsr_pattern *p, const bsr_bf16 *dY, int64_t M
     if (M == 0) return BSR_OK;
     FwdArgs a{dY, M, p->N, V, nullptr, dX, p->K};
     return launch_group_gemm(*p, true, a, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_op_kernels(const bsr_pattern *p, int32_t op, int64_t M, char *buf, int32_t len) {
+    BSR_TRY_BEGIN
+    if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    if (op < 0 || op > 2) return fail(BSR_ERR_INVALID_ARG, "op must be 0 (forward), 1 (input gradient) or 2 (weight gradient)");
+    if (M < 0) return fail(BSR_ERR_INVALID_ARG, "M must be >= 0");
+    if (!buf || len <= 0) return fail(BSR_ERR_INVALID_ARG, "buf must hold at least one byte");
+    const std::string names = kernels_of(*p, op, M, small_m_max(*p));
+    if ((int64_t)names.size() + 1 > len) return fail(BSR_ERR_INVALID_ARG, "buf too small for the kernel names");
+    std::memcpy(buf, names.c_str(), names.size() + 1);
+    return BSR_OK;
     BSR_TRY_END
 }
 

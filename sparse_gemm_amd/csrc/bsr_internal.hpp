@@ -210,6 +210,9 @@ struct DwArgs {
     size_t ws_bytes;
 };
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M);
+// Comma-separated names of the main kernels one call of op (0 forward, 1 input gradient, 2 weight
+// gradient, bias gradient excluded) launches for M rows; small_max: the forward's small-M limit.
+std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max);
 int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream);
 // The wide weight-gradient items (bsr_wide.hip): fp32 partials [chunk][nnzb][b*b] when partial
 // is not null, else bf16 into a.dV.

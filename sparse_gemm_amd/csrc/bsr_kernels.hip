@@ -978,6 +978,16 @@ int32_t launch_small_m_fwd_csr(int32_t N, int32_t K, int32_t b, const int32_t *r
 
 size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan_dw(p, M).total : 0; }
 
+std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max) {
+    if (M <= 0) return op == 2 ? "k_fill_zero" : "";
+    if (op == 0 && M <= small_max) return "k_small_m";
+    if (op == 0 || op == 1) return use_wide(p, op == 1, M) ? "k_wide_gemm" : "k_panel_gemm";
+    if (p.nnzb == 0) return "";
+    const DwPlan pl = plan_dw(p, M);
+    if (p.wdw.n > 0) return pl.wide.c2 > 1 && pl.wide.P2 > 0 ? "k_wide_dw,k_wide_dw_reduce" : "k_wide_dw";
+    return pl.nchunks > 1 ? "k_dw_panel,k_dw_reduce" : "k_dw_panel";
+}
+
 // ---- weight gradient without allocation: a scratch array in the code object ----
 // One array per GPU, created when the library's code object is loaded on that GPU and held until
 // the process ends. Its host-side name is only a stand-in: kernels get the device address that

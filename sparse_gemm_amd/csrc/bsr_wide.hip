@@ -15,9 +15,9 @@
 // lines) and the kept value blocks of its 16 units (unit u = member u / 2, block u % 2 of the panel;
 // 2 KB each, staged at slot u) go to LDS by direct-to-LDS loads that every wave issues for its
 // share. The 160 KB of LDS hold 3 activation stages and 2 value stages: during sub-step s the
-// value blocks of s + 1 are loaded (issued during the first 16-deep chunk of s) and the activation
-// panel of s + 2 (during the second chunk), so activation loads have two sub-steps to land. At
-// the end of s every wave waits for its loads of s + 1 and a barrier publishes them.
+// activation panel of s + 2 is loaded (issued during the first three 16-deep chunks of s) and the
+// value blocks of s + 2 (during the last chunk, once the barrier has freed their stage). At the
+// end of s every wave waits for its loads of s + 1 and a barrier publishes them.
 // Groups whose every sub-step keeps all 16 units (e.g. block rows kept in full) run a body
 // without presence tests; the others test each member's block before its products.
 //   out tile^T [n][m] += A[n][k] . B[k][m],   B[k][m] = act[m][panel*64 + k]
@@ -176,16 +176,18 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto none = [](int) __attribute__((always_inline)) {};
 
-    // Sub-step pipeline. Before sub-step s: activation stages hold s, s + 1, s + 2 (landed or in
-    // flight), value stages s, s + 1; fragment set 0 holds chunk 0 of s. Sub-step s: chunks 0 .. 2
-    // (each reading the next chunk's fragments), then every wave waits for its LDS reads of s (all
-    // in registers now) and for its loads of s + 1, and a barrier publishes s + 1 and frees the
-    // stages of s; then the value blocks of s + 2 and the activation panel of s + 3 are issued into
-    // those stages between the products of chunk 3, after the reads of chunk 0 of s + 1. So the
-    // barrier never waits on an LDS read, the next sub-step starts with its first fragments in
-    // registers, and loads have more than one sub-step (values) and two (activations) to land.
+    // Sub-step pipeline. Before sub-step s: activation stages hold s, s + 1 (landed or in flight),
+    // value stages s, s + 1; fragment set 0 holds chunk 0 of s. Sub-step s: chunks 0 .. 2 (each
+    // reading the next chunk's fragments), with the activation panel of s + 2 issued between their
+    // products into the third activation stage (free since the last barrier); then every wave waits
+    // for its LDS reads of s (all in registers now) and for its loads of s + 1, and a barrier
+    // publishes s + 1 and frees the stages of s; then the value blocks of s + 2 are issued into
+    // their stage between the products of chunk 3, after the reads of chunk 0 of s + 1. The issue
+    // of a direct-to-LDS load holds the wave while the compute unit's load path is busy, so the
+    // loads go out one or two at a time between groups of 4 products. The barrier never waits on an
+    // LDS read, the next sub-step starts with its first fragments in registers, and loads have about
+    // one sub-step to land.
     const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
     if (s0 < s1) {
         WideRec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
@@ -200,20 +202,21 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
 #pragma unroll
             for (int t = 0; t < 4; ++t) issue_v(1, r1, t);
         }
-        if (s0 + 2 < s1) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) issue_x(2, r2, j);
-        }
         wait_vm<0, 0>(0);
         __syncthreads();
         read_frags(0, 0, 0, 0);
         int xs = 0, vs = 0;
         for (int s = s0; s < s1; ++s) {
             const int m8 = (r0.mask >> (8 * wm)) & 0xFF;
+            const bool more2 = s + 2 < s1;
+            const int x2 = xs == 0 ? 2 : xs - 1;   // activation stage of s + 2 (that of s - 1)
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
                 read_frags((c + 1) & 1, xs, vs, c + 1);
-                products(c, m8, none);
+                // the 8 activation loads of s + 2 over the first 3 product groups of chunks 0 .. 2
+                products(c, m8, [&](int t) __attribute__((always_inline)) {
+                    if (more2 && t < 3 && 3 * c + t < 8) issue_x(x2, r2, 3 * c + t);
+                });
             }
             // every LDS read of sub-step s has landed in registers (chunk 3's included)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -222,25 +225,15 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
             // LDS waits into full ones
             const WideRec r4 = load_rec(min(s + 4, s1 - 1));
             // this wave's loads of s + 1 have landed; the activation loads of s + 2, issued after
-            // them during sub-step s - 1, may still be in flight
-            if (s > s0 && s + 2 < s1) wait_vm<8, 8>(8);
+            // them during chunks 0 .. 2, may still be in flight
+            if (more2) wait_vm<8, 8>(8);
             else wait_vm<0, 0>(0);
             __syncthreads();   // everyone's have; nobody reads the stages of s any more
             const int xn = xs == 2 ? 0 : xs + 1, vn = vs ^ 1;
             read_frags(0, xn, vn, 0);   // chunk 0 of s + 1 (harmless past the last sub-step)
-            const bool more2 = s + 2 < s1, more3 = s + 3 < s1;
-            // value loads first, activation loads last: the wait above counts on the last 8 loads
-            // of a sub-step being its activation loads (loads complete in issue order)
+            // value loads of s + 2: 2 per product group
             products(3, m8, [&](int t) __attribute__((always_inline)) {
-                if (t < 2) {
-                    if (more2) {
-                        issue_v(vs, r2, 2 * t);
-                        issue_v(vs, r2, 2 * t + 1);
-                    }
-                } else if (more3) {
-#pragma unroll
-                    for (int j = 4 * (t - 2); j < 4 * (t - 2) + 4; ++j) issue_x(xs, r3, j);
-                }
+                if (more2) issue_v(vs, r2, t);
             });
             r0 = r1;
             r1 = r2;

@@ -190,3 +190,28 @@ def test_pattern_size_limit():
     p = Pattern.from_mask(mask, R * b, C * b, b, upload=False)
     assert p.nnzb == (1 << 23) - 1
     p.close()
+
+
+def test_op_kernels_names_the_dispatch():
+    """bsr_op_kernels (host only) names the kernels each call launches: the wide kernels for a
+    pattern with full block rows at large M, the streaming small-M forward for few rows, the tile
+    weight gradient (split over row chunks) for a uniform pattern; bad arguments are rejected."""
+    from sparse_gemm_amd import binding
+    w = synth.WORKLOADS[5]
+    p = Pattern.from_mask(synth.block_mask(w, 0), w.N, w.K, w.b, upload=False)
+    assert binding.op_kernels(p, "fwd", w.M) == ["k_wide_gemm"]
+    assert binding.op_kernels(p, "dx", w.M) == ["k_wide_gemm"]
+    assert binding.op_kernels(p, "dw", w.M) == ["k_wide_dw", "k_wide_dw_reduce"]
+    assert binding.op_kernels(p, "fwd", 8) == ["k_small_m"]
+    assert binding.op_kernels(p, "fwd", 0) == []
+    assert binding.op_kernels(p, "dw", 0) == ["k_fill_zero"]
+    w2 = synth.WORKLOADS[2]
+    p2 = Pattern.from_mask(synth.block_mask(w2, 0), w2.N, w2.K, w2.b, upload=False)
+    assert binding.op_kernels(p2, "fwd", w2.M)[0] in ("k_panel_gemm", "k_wide_gemm")
+    assert binding.op_kernels(p2, "dw", w2.M) == ["k_dw_panel", "k_dw_reduce"]
+    L = _lib.load()
+    buf = ctypes.create_string_buffer(4)
+    assert L.bsr_op_kernels(p.handle, 0, w.M, buf, 4) == 1   # too small
+    assert L.bsr_op_kernels(p.handle, 3, w.M, buf, 4) == 1
+    assert L.bsr_op_kernels(p.handle, 0, -1, buf, 4) == 1
+    assert L.bsr_op_kernels(None, 0, 1, buf, 4) == 1
