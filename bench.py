@@ -248,6 +248,44 @@ def summarize_mfma(pmc_dir: str, workload_name: str, seed: int = 0, out_path=Non
     return path
 
 
+def trace_path(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"kernel_trace_{workload_name}.md")
+
+
+def summarize_trace(trace_dir: str, workload: int, workload_name: str, out_path=None) -> str:
+    """Per-kernel durations from one rocprofv3 --kernel-trace --stats run of the benchmark
+    (its *kernel_stats.csv). Writes the summary under profiles/ and returns its path."""
+    import csv
+    import glob
+    src = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
+    if not src:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(src[0])))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    lines = [f"# Kernel trace: bench.py, workload {workload_name}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py "
+             f"--workload {workload} --steps 20 --warmup 5 --no-cpu-baseline --no-extras",
+             f"python3 bench.py --workload {workload} --trace-summary <dir>", "```", "",
+             "| Kernel | Calls | Avg (us) | Min (us) | Max (us) | % of GPU time |", "|---|---|---|---|---|---|"]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows:
+        short = re.sub(r"\(.*$", "", r["Name"].replace("void ", "").replace("bsr::(anonymous namespace)::", "")
+                       .replace("(anonymous namespace)::", ""))
+        if len(short) > 100:
+            short = short[:97] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.2f} |")
+    lines.append("")
+    lines.append(f"kernel_source_sha256: {kernel_source_hash()}")
+    path = out_path or trace_path(workload_name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -796,7 +834,14 @@ def main():
                     help="summarize two rocprofv3 --pmc runs into profiles/ and exit (no GPU needed)")
     ap.add_argument("--mfma-summary", metavar="PMC_DIR",
                     help="summarize one rocprofv3 --pmc run of the MFMA counters into profiles/ and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarize one rocprofv3 --kernel-trace --stats run into profiles/ and exit")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        from sparse_gemm_amd import synth
+        print(summarize_trace(args.trace_summary, args.workload, synth.WORKLOADS[args.workload].name))
+        return
 
     if args.mfma_summary:
         from sparse_gemm_amd import synth
