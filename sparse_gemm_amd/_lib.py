@@ -30,7 +30,8 @@ EXPORTS = ("bsr_abi_version", "bsr_pattern_create_from_mask", "bsr_pattern_creat
            "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24", "bsr_values_pack_24",
            "bsr_linear_fwd_24_image", "bsr_values_quantize_fp8_24", "bsr_linear_fwd_fp8_24",
            # include/bsr_rebuild.h
-           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild", "bsr_linear_fwd_small_m_csr")
+           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild", "bsr_linear_fwd_small_m_csr",
+           "bsr_pattern_create_device", "bsr_pattern_rebuild", "bsr_pattern_device_arrays")
 
 
 class BsrError(RuntimeError):
@@ -83,6 +84,9 @@ def load() -> ctypes.CDLL:
     L.bsr_meta_rebuild_workspace.argtypes, L.bsr_meta_rebuild_workspace.restype = [i32, i32], sz
     L.bsr_meta_rebuild.argtypes = [i32, i32, P, P, P, P, P, P, i32, P, P, sz, P]
     L.bsr_linear_fwd_small_m_csr.argtypes = [i32, i32, i32, P, P, i32, P, i64, P, P, P, P]
+    L.bsr_pattern_create_device.argtypes = [i32, i32, i32, i32, PP]
+    L.bsr_pattern_rebuild.argtypes = [P, P, P]
+    L.bsr_pattern_device_arrays.argtypes = [P, PP, PP, PP, PP, PP, PP]
     for f in ("bsr_pattern_create_from_mask", "bsr_pattern_create_from_csr", "bsr_pattern_info",
               "bsr_pattern_export", "bsr_linear_fwd", "bsr_linear_bwd_input", "bsr_linear_bwd_weight",
               "bsr_linear_bwd_weight_noalloc",
@@ -94,7 +98,8 @@ def load() -> ctypes.CDLL:
            "bsr_values_compress_24", "bsr_values_decompress_24", "bsr_linear_fwd_24", "bsr_values_pack_24",
            "bsr_linear_fwd_24_image", "bsr_values_quantize_fp8_24", "bsr_linear_fwd_fp8_24",
            # include/bsr_rebuild.h
-           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild", "bsr_linear_fwd_small_m_csr"):
+           "bsr_meta_rebuild_workspace", "bsr_meta_rebuild", "bsr_linear_fwd_small_m_csr",
+           "bsr_pattern_create_device", "bsr_pattern_rebuild", "bsr_pattern_device_arrays"):
         getattr(L, f).restype = i32
     L.bsr_status_string.argtypes, L.bsr_status_string.restype = [i32], ctypes.c_char_p
     L.bsr_last_error.argtypes, L.bsr_last_error.restype = [], ctypes.c_char_p

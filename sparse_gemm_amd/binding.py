@@ -28,6 +28,31 @@ def _single_hip_runtime() -> None:
 
 
 _checked = None
+_hip_rt = None
+
+
+def _hip() -> ctypes.CDLL:
+    """The HIP runtime this process already maps (the one torch and the library share)."""
+    global _hip_rt
+    if _hip_rt is None:
+        lib()
+        with open("/proc/self/maps") as f:
+            paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+        if not paths:
+            raise RuntimeError("no HIP runtime mapped")
+        _hip_rt = ctypes.CDLL(paths[0])
+    return _hip_rt
+
+
+def device_int(addr: int) -> int:
+    """The int32 at a device address (for example a device-built pattern's live nnzb), copied to
+    the host after the device has finished its queued work."""
+    torch.cuda.synchronize()
+    v = ctypes.c_int32()
+    rc = _hip().hipMemcpy(ctypes.byref(v), ctypes.c_void_p(addr), ctypes.c_size_t(4), 2)   # device to host
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
+    return v.value
 
 
 def lib() -> ctypes.CDLL:
@@ -101,6 +126,34 @@ class Pattern:
                                                      ci.ctypes.data_as(ctypes.c_void_p) if ci.size else None,
                                                      int(upload), ctypes.byref(h)), "bsr_pattern_create_from_csr")
         return cls(h, upload, dev)
+
+    @classmethod
+    def device_built(cls, N: int, K: int, b: int, cap: int) -> "Pattern":
+        """An empty pattern whose metadata and work lists live on the device, rebuilt there from a
+        device mask by rebuild() (bsr_pattern_create_device); nnzb reports the capacity cap."""
+        dev = cls._device(True)
+        h = ctypes.c_void_p()
+        _lib.check(lib().bsr_pattern_create_device(N, K, b, int(cap), ctypes.byref(h)), "bsr_pattern_create_device")
+        pat = cls(h, True, dev)
+        pat.cap = int(cap)
+        return pat
+
+    def rebuild(self, mask: torch.Tensor) -> None:
+        """Rebuild a device-built pattern from the device uint8 mask [N/b, K/b] on the current stream
+        (bsr_pattern_rebuild; no host synchronisation)."""
+        if mask.dtype != torch.uint8 or not mask.is_cuda or mask.device.index != self.device:
+            raise ValueError(f"mask must be a uint8 tensor on cuda:{self.device}")
+        if tuple(mask.shape) != (self.R, self.C) or not mask.is_contiguous():
+            raise ValueError(f"mask must be a contiguous [{self.R}, {self.C}] tensor")
+        _lib.check(lib().bsr_pattern_rebuild(self._h, _ptr(mask), _stream(self.device)), "bsr_pattern_rebuild")
+
+    def device_arrays(self) -> dict:
+        """Device addresses of a device-built pattern's row_ptr, col_idx, col_ptr, row_idx, perm and
+        live nnzb (bsr_pattern_device_arrays)."""
+        ptrs = [ctypes.c_void_p() for _ in range(6)]
+        _lib.check(lib().bsr_pattern_device_arrays(self._h, *(ctypes.byref(q) for q in ptrs)),
+                   "bsr_pattern_device_arrays")
+        return dict(zip(("row_ptr", "col_idx", "col_ptr", "row_idx", "perm", "nnzb"), (q.value for q in ptrs)))
 
     def export(self) -> dict:
         out = dict(row_ptr=np.empty(self.R + 1, np.int32), col_idx=np.empty(self.nnzb, np.int32),

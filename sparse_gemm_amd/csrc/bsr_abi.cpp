@@ -108,10 +108,13 @@ int32_t finish_create(bsr_pattern *p, int32_t upload_flag, bsr_pattern **out) {
     return BSR_OK;
 }
 
-// Common checks of a compute call.
-int32_t check_call(const bsr_pattern *p, int64_t M) {
+// Common checks of a compute call; device_ok: the call also takes device-built patterns.
+int32_t check_call(const bsr_pattern *p, int64_t M, bool device_ok = false) {
     if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
     if (!p->uploaded) return fail(BSR_ERR_NO_DEVICE_DATA, "pattern was created without upload");
+    if (p->device_built && !device_ok)
+        return fail(BSR_ERR_UNSUPPORTED, "a device-built pattern serves bsr_linear_fwd, bsr_linear_bwd_input and "
+                                         "bsr_linear_bwd_weight(_noalloc) only");
     if (M < 0) return fail(BSR_ERR_INVALID_ARG, "M must be >= 0");
     if (M > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "M must fit in int32");
     int dev = -1;
@@ -216,6 +219,8 @@ int32_t bsr_pattern_info(const bsr_pattern *p, int32_t *N, int32_t *K, int32_t *
 int32_t bsr_pattern_export(const bsr_pattern *p, int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
                            int32_t *row_idx, int32_t *perm) {
     if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    if (p->device_built)
+        return fail(BSR_ERR_UNSUPPORTED, "a device-built pattern has no host metadata (bsr_pattern_device_arrays)");
     auto put = [](int32_t *dst, const std::vector<int32_t> &v) {
         if (dst && !v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(int32_t));
     };
@@ -236,14 +241,19 @@ void bsr_pattern_destroy(bsr_pattern *p) {
 int32_t bsr_linear_fwd(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *V, const bsr_bf16 *bias,
                        bsr_bf16 *Y, void *stream) {
     BSR_TRY_BEGIN
-    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_call(p, M, true));
     BSR_CHECK(check_ptr(X, "X", M == 0));
     BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
     BSR_CHECK(check_ptr(bias, "bias", true));
     BSR_CHECK(check_ptr(Y, "Y", M == 0));
     if (M == 0) return BSR_OK;
     FwdArgs a{X, M, p->K, V, bias, Y, p->N};
-    if (M <= small_m_max(*p)) return launch_small_m_fwd(*p, a, stream);
+    if (p->device_built) {
+        // device-built: the streaming forward straight from the device CSR (natural row order)
+        if (M <= kSmallM) return launch_small_m_fwd_csr(p->N, p->K, p->b, p->dev.row_ptr, p->dev.col_idx, p->nnzb, a, stream);
+    } else if (M <= small_m_max(*p)) {
+        return launch_small_m_fwd(*p, a, stream);
+    }
     return launch_group_gemm(*p, false, a, stream);
     BSR_TRY_END
 }
@@ -251,7 +261,7 @@ int32_t bsr_linear_fwd(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const
 int32_t bsr_linear_bwd_input(const bsr_pattern *p, const bsr_bf16 *dY, int64_t M, const bsr_bf16 *V, bsr_bf16 *dX,
                              void *stream) {
     BSR_TRY_BEGIN
-    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_call(p, M, true));
     BSR_CHECK(check_ptr(dY, "dY", M == 0));
     BSR_CHECK(check_ptr(V, "V", p->nnzb == 0));
     BSR_CHECK(check_ptr(dX, "dX", M == 0));
@@ -282,7 +292,7 @@ size_t bsr_linear_bwd_weight_workspace(const bsr_pattern *p, int64_t M) {
 int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bsr_bf16 *X, int64_t M, bsr_bf16 *dV,
                               bsr_bf16 *dbias, void *workspace, size_t ws_bytes, void *stream) {
     BSR_TRY_BEGIN
-    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_call(p, M, true));
     BSR_CHECK(check_ptr(dY, "dY", M == 0));
     BSR_CHECK(check_ptr(X, "X", M == 0));
     BSR_CHECK(check_ptr(dV, "dV", p->nnzb == 0));
@@ -302,7 +312,7 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
 int32_t bsr_linear_bwd_weight_noalloc(const bsr_pattern *p, const bsr_bf16 *dY, const bsr_bf16 *X, int64_t M,
                                       bsr_bf16 *dV, bsr_bf16 *dbias, void *stream) {
     BSR_TRY_BEGIN
-    BSR_CHECK(check_call(p, M));
+    BSR_CHECK(check_call(p, M, true));
     BSR_CHECK(check_ptr(dY, "dY", M == 0));
     BSR_CHECK(check_ptr(X, "X", M == 0));
     BSR_CHECK(check_ptr(dV, "dV", p->nnzb == 0));
@@ -569,6 +579,109 @@ int32_t bsr_meta_rebuild(int32_t R, int32_t C, const uint8_t *mask, int32_t *row
                     "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(need));
     return launch_rebuild(R, C, mask, row_ptr, col_idx, col_ptr, row_idx, perm, cap, nnzb, workspace, stream);
     BSR_TRY_END
+}
+
+int32_t bsr_pattern_create_device(int32_t N, int32_t K, int32_t b, int32_t cap, bsr_pattern **out) {
+    BSR_TRY_BEGIN
+    if (!out) return fail(BSR_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    BSR_CHECK(check_shape(N, K, b));
+    const int32_t R = N / b, C = K / b;
+    if ((int64_t)R * C >= (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "R*C must be below 2^31");
+    if (cap < 1 || cap > kMaxNnzb || (int64_t)cap > (int64_t)R * C)
+        return fail(BSR_ERR_INVALID_ARG, "cap must lie in [1, min(2^23 - 1, (N/b)*(K/b))]");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BSR_ERR_HIP, "hipGetDevice failed (no usable GPU?)");
+    auto *p = new bsr_pattern();
+    p->N = N;
+    p->K = K;
+    p->b = b;
+    p->R = R;
+    p->C = C;
+    p->nnzb = cap;
+    p->device_built = true;
+    const GemmVariant v = gemm_variant(b, kDeviceVariant);
+    const int32_t gf = (R + v.G - 1) / v.G, gb = (C + v.G - 1) / v.G;
+    for (auto [s, n] : {std::make_pair(&p->fwd[kDeviceVariant], gf), std::make_pair(&p->bwd[kDeviceVariant], gb)}) {
+        s->G = v.G;
+        s->S = v.S;
+        s->ngroups = n;
+    }
+    const int64_t TR = dw_tile_rows(b), TC = dw_tile_cols(b), capi = (int64_t)kDwWaves * dw_slots(b);
+    const int64_t ntiles = ((R + TR - 1) / TR) * ((C + TC - 1) / TC);
+    p->dw.n = (int)std::min<int64_t>(cap, ntiles * ((TR * TC + capi - 1) / capi));
+    // one allocation, zeroed: before the first rebuild the pattern is empty (every row pointer,
+    // sub-step pointer and live count 0)
+    struct Part {
+        size_t ints;
+        const int32_t **dst;
+    };
+    DeviceMeta &d = p->dev;
+    const Part parts[] = {
+        {(size_t)R + 1, &d.row_ptr}, {(size_t)cap, &d.col_idx}, {(size_t)C + 1, &d.col_ptr}, {(size_t)cap, &d.row_idx},
+        {(size_t)cap, &d.perm}, {1, &d.live_nnzb}, {1, &d.live_items},
+        {(size_t)gf, &d.fwd[kDeviceVariant].order}, {(size_t)gf + 1, &d.fwd[kDeviceVariant].sub_ptr},
+        {(size_t)gf * v.G, &d.fwd[kDeviceVariant].out}, {(size_t)cap * kRecInts, &d.fwd[kDeviceVariant].rec},
+        {(size_t)gb, &d.bwd[kDeviceVariant].order}, {(size_t)gb + 1, &d.bwd[kDeviceVariant].sub_ptr},
+        {(size_t)gb * v.G, &d.bwd[kDeviceVariant].out}, {(size_t)cap * kRecInts, &d.bwd[kDeviceVariant].rec},
+        {(size_t)p->dw.n * kDwItemInts, &d.dw_items},
+    };
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    size_t total = 0;
+    for (const Part &q : parts) total += al(q.ints * sizeof(int32_t));
+    const size_t sched_bytes = sched_scratch_bytes(R, C, b), rebuild_bytes = rebuild_workspace_bytes(R, C);
+    total += al(sched_bytes) + al(rebuild_bytes);
+    void *base = nullptr;
+    hipError_t e = hipMalloc(&base, total);
+    if (e != hipSuccess) {
+        delete p;
+        return fail(e == hipErrorOutOfMemory ? BSR_ERR_OUT_OF_MEMORY : BSR_ERR_HIP,
+                    std::string("hipMalloc of a device-built pattern: ") + hipGetErrorString(e));
+    }
+    e = hipMemset(base, 0, total);
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        delete p;
+        return fail(BSR_ERR_HIP, std::string("hipMemset: ") + hipGetErrorString(e));
+    }
+    char *c = static_cast<char *>(base);
+    for (const Part &q : parts) {
+        *q.dst = reinterpret_cast<const int32_t *>(c);
+        c += al(q.ints * sizeof(int32_t));
+    }
+    d.sched_scratch = c;
+    c += al(sched_bytes);
+    d.rebuild_ws = c;
+    d.base = base;
+    d.bytes = total;
+    d.device = dev;
+    p->uploaded = true;
+    *out = p;
+    return BSR_OK;
+    BSR_TRY_END
+}
+
+int32_t bsr_pattern_rebuild(bsr_pattern *p, const uint8_t *mask, void *stream) {
+    BSR_TRY_BEGIN
+    BSR_CHECK(check_call(p, 0, true));
+    if (!p->device_built) return fail(BSR_ERR_UNSUPPORTED, "pattern is not device-built (bsr_pattern_create_device)");
+    if (!mask) return fail(BSR_ERR_INVALID_ARG, "mask is NULL");
+    return launch_pattern_rebuild(*p, mask, stream);
+    BSR_TRY_END
+}
+
+int32_t bsr_pattern_device_arrays(const bsr_pattern *p, const int32_t **row_ptr, const int32_t **col_idx,
+                                  const int32_t **col_ptr, const int32_t **row_idx, const int32_t **perm,
+                                  const int32_t **nnzb) {
+    if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
+    if (!p->device_built) return fail(BSR_ERR_UNSUPPORTED, "pattern is not device-built (bsr_pattern_create_device)");
+    if (row_ptr) *row_ptr = p->dev.row_ptr;
+    if (col_idx) *col_idx = p->dev.col_idx;
+    if (col_ptr) *col_ptr = p->dev.col_ptr;
+    if (row_idx) *row_idx = p->dev.row_idx;
+    if (perm) *perm = p->dev.perm;
+    if (nnzb) *nnzb = p->dev.live_nnzb;
+    return BSR_OK;
 }
 
 const char *bsr_status_string(int32_t status) {

@@ -36,6 +36,9 @@ constexpr int kLoaderWaves = 2;
 struct GemmVariant {
     int G, S, waves;
 };
+// The variant whose work lists a device-built pattern's rebuild produces (G = 4, S = 4, 4 waves
+// for b = 32; one block per panel, 4 waves for b = 64).
+constexpr int kDeviceVariant = 1;
 inline GemmVariant gemm_variant(int b, int k) {
     if (b == 64) return GemmVariant{1, 1, k == 0 ? 8 : 4};
     return k == 0 ? GemmVariant{4, 8, 8} : k == 1 ? GemmVariant{4, 4, 4} : k == 2 ? GemmVariant{2, 4, 4} : GemmVariant{1, 2, 4};
@@ -140,6 +143,10 @@ struct DeviceMeta {
     DevSchedule wide_fwd, wide_bwd;
     const int32_t *dw_items = nullptr;
     const int32_t *wdw_items = nullptr, *wdw_compact = nullptr;
+    // device-built patterns: the live block count and weight-gradient item count, the builders'
+    // scratch and the metadata rebuild's workspace
+    const int32_t *live_nnzb = nullptr, *live_items = nullptr;
+    void *sched_scratch = nullptr, *rebuild_ws = nullptr;
     const int32_t *small_m_rows = nullptr;  // small-M forward: [R][4] {block row, first block, end
                                             // block, 0}, most blocks first
     const int32_t *small_m_work = nullptr;  // balanced small-M work list: [n][4] {block row, first
@@ -157,6 +164,10 @@ struct bsr_pattern {
     bsr::WideDwSchedule wdw;   // b = 32 only
     bsr::DeviceMeta dev;
     bool uploaded = false;
+    // Device-built pattern (bsr_pattern_create_device): metadata and work lists live on the device
+    // only, rebuilt there from a device mask; nnzb is the capacity (the most kept blocks it holds),
+    // dw.n the capacity of weight-gradient items, and no host-side list is filled.
+    bool device_built = false;
 };
 
 namespace bsr {

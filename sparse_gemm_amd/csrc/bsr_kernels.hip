@@ -535,8 +535,8 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
 template <int BS, int NL>
 __global__ __launch_bounds__((kDwWaves + NL) * 64) void k_dw_panel(
     const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X, int K, int M,
-    const int32_t *__restrict__ items, int nitems, int mchunk, float *__restrict__ partial, int nnzb,
-    uint16_t *__restrict__ dV) {
+    const int32_t *__restrict__ items, int nitems, const int32_t *__restrict__ live, int mchunk,
+    float *__restrict__ partial, int nnzb, uint16_t *__restrict__ dV) {
     constexpr int NW = kDwWaves;
     constexpr int SL = BS == 64 ? 2 : 8;        // blocks per compute wave (dw_slots)
     constexpr int NT = BS / 32;                 // 32 x 32 sub-tiles per block side
@@ -554,6 +554,7 @@ __global__ __launch_bounds__((kDwWaves + NL) * 64) void k_dw_panel(
     // each XCD takes a contiguous run of (chunk, item) pairs, items fastest
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int item = L % nitems, ch = L / nitems;
+    if (live && item >= *live) return;   // a device-built list shorter than its capacity
     const int32_t *it = items + (size_t)item * kDwItemInts;
     const int r0 = it[0], c0 = it[1];
     const int m_begin = ch * mchunk, m_end = min(M, m_begin + mchunk);
@@ -764,6 +765,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint16_t *__restrict__ p, siz
 // Variant of a panel GEMM call (see gemm_variant); "fills" = at least two work-groups per compute
 // unit, so that one work-group's prologue and epilogue overlap another's main loop.
 int choose_variant(const bsr_pattern &p, bool transposed, int64_t M) {
+    if (p.device_built) return kDeviceVariant;   // the only work lists its rebuild produces
     if (const char *f = std::getenv("BSR_GEMM_VARIANT")) {   // tuning knob: 0 | 1 | 2 | 3
         const int k = std::atoi(f);
         if (k >= 0 && k < kGemmVariants) return k;
@@ -980,6 +982,7 @@ size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan
 
 std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max) {
     if (M <= 0) return op == 2 ? "k_fill_zero" : "";
+    if (p.device_built) small_max = std::min<int64_t>(small_max, kSmallM);
     if (op == 0 && M <= small_max) return "k_small_m";
     if (op == 0 || op == 1) return use_wide(p, op == 1, M) ? "k_wide_gemm" : "k_panel_gemm";
     if (p.nnzb == 0) return "";
@@ -1043,10 +1046,10 @@ int32_t launch_dw(const bsr_pattern &p, const DwArgs &a, void *stream) {
         constexpr int NL = kLoaderWaves, NT = (kDwWaves + NL) * 64;
         if (p.b == 32)
             hipLaunchKernelGGL((k_dw_panel<32, NL>), grid, dim3(NT), 0, st, a.dY, p.N, a.X, p.K, (int)a.M, d.dw_items,
-                               p.dw.n, pl.mchunk, partial, p.nnzb, a.dV);
+                               p.dw.n, d.live_items, pl.mchunk, partial, p.nnzb, a.dV);
         else
             hipLaunchKernelGGL((k_dw_panel<64, NL>), grid, dim3(NT), 0, st, a.dY, p.N, a.X, p.K, (int)a.M, d.dw_items,
-                               p.dw.n, pl.mchunk, partial, p.nnzb, a.dV);
+                               p.dw.n, d.live_items, pl.mchunk, partial, p.nnzb, a.dV);
         if (partial) {
             const size_t count = (size_t)p.nnzb * p.b * p.b;
             hipLaunchKernelGGL(k_dw_reduce, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, st, partial,

@@ -555,7 +555,7 @@ int wide_tiles_per_chunk(int nmtiles) {
 }  // namespace
 
 bool use_wide(const bsr_pattern &p, bool transposed, int64_t M) {
-    if (p.b != 32) return false;
+    if (p.b != 32 || p.device_built) return false;
     const WideSchedule &s = transposed ? p.wide_bwd : p.wide_fwd;
     if (const char *f = std::getenv("BSR_GEMM_VARIANT")) return std::atoi(f) == kGemmVariants;   // tuning knob
     const int64_t nsub = s.nsub();

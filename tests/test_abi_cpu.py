@@ -215,3 +215,19 @@ def test_op_kernels_names_the_dispatch():
     assert L.bsr_op_kernels(p.handle, 3, w.M, buf, 4) == 1
     assert L.bsr_op_kernels(p.handle, 0, -1, buf, 4) == 1
     assert L.bsr_op_kernels(None, 0, 1, buf, 4) == 1
+
+
+def test_device_pattern_argument_errors():
+    """bsr_pattern_create_device rejects bad shapes and capacities before touching a GPU."""
+    L = _lib.load()
+    h = ctypes.c_void_p()
+    assert L.bsr_pattern_create_device(256, 256, 48, 10, ctypes.byref(h)) == 2    # block size
+    assert L.bsr_pattern_create_device(256, 250, 32, 10, ctypes.byref(h)) == 1    # K not a multiple
+    assert L.bsr_pattern_create_device(256, 256, 32, 0, ctypes.byref(h)) == 1     # cap < 1
+    assert L.bsr_pattern_create_device(256, 256, 32, 65, ctypes.byref(h)) == 1    # cap > R*C
+    assert L.bsr_pattern_create_device(256, 256, 32, 10, None) == 1
+    assert L.bsr_pattern_rebuild(None, None, None) == 1
+    host = Pattern.from_mask(np.ones((8, 8), np.uint8), 256, 256, 32, upload=False)
+    ptr = ctypes.c_void_p()
+    assert L.bsr_pattern_device_arrays(host.handle, ctypes.byref(ptr), None, None, None, None, None) == 2
+    assert L.bsr_pattern_device_arrays(None, None, None, None, None, None, None) == 1
