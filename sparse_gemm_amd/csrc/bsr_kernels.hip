@@ -518,6 +518,153 @@ __global__ __launch_bounds__(NW * 64) void k_small_m(const uint16_t *__restrict_
 }
 
 // ------------------------------------------------------------------------------------------
+// Small-M forward over the balanced work list, with the value slices loaded as whole cache lines.
+// Same work split, products and reduction as k_small_m (WORK, one block per wave and pass, the
+// next pass's loads requested before the current pass's products), but each value load reads 1 KB
+// contiguous (8 rows x 128 bytes for b = 64, 16 rows x 64 bytes for b = 32) into registers, and
+// the wave re-lays it through its own 4 KB of LDS (16-byte chunks XOR-swizzled per row) into the
+// matrix-core fragments (row l % 16, chunk 4 kc + l / 16). Loading the fragments straight from
+// memory puts 16 rows x 64 bytes (16 half lines) in every load: a plain streaming probe on one
+// MI355X reads a 64 MB set in 13.4 us that way against 9.2 us with 1 KB contiguous per load. Every
+// load is an ordinary one, so the compiler's waits are exact; no barrier inside the loop (a wave
+// reads back only its own writes).
+// ------------------------------------------------------------------------------------------
+template <int BS>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (BS == 64) return swz8(r);
+    else return swz4(r);
+}
+
+template <int BS, int NW, int MT, int NB>
+__global__ __launch_bounds__(NW * 64) void k_small_m_lines(const uint16_t *__restrict__ X, int K, int M,
+                                                           const uint16_t *__restrict__ V,
+                                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ Y,
+                                                           int N, const int32_t *__restrict__ col_idx,
+                                                           const int32_t *__restrict__ work) {
+    constexpr int PS = 2, KC = BS / 32;
+    constexpr int RB = BS * 2;             // bytes of one block row
+    constexpr int SLB = 16 * RB;           // one 16-row slice of a block (2 KB for b = 64, 1 KB for 32)
+    constexpr int DPS = SLB / 1024;        // 1 KB loads per slice (= KC)
+    constexpr int LPR = RB / 16;           // lanes per block row in a load
+    constexpr int RPL = 64 / LPR;          // block rows per load
+    constexpr int WB = PS * SLB;           // a wave's LDS region (both slices of one block)
+    constexpr int RED = NW * MT * PS * 64 * 16;
+    static_assert(DPS == KC, "one 1 KB load per 32-deep chunk of a slice");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NW * WB > RED ? NW * WB : RED];
+
+    const int4 e = reinterpret_cast<const int4 *>(work)[blockIdx.x];
+    const int r = e.x, i1 = e.z;
+    const int s0 = e.w & 0xff, ns = e.w >> 8;   // first slice, slices (1 or 2; uniform)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int m0 = blockIdx.y * 16 * MT, Mc = min(16 * MT, M - m0);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)m0 * K, (uint32_t)Mc * K * 2);
+    const uint32_t xoff = (uint32_t)(l16 * K + lq * 8) * 2;
+    const uint32_t xend = (uint32_t)Mc * K * 2;   // past this chunk's activations: reads zeros
+    unsigned char *wreg = smem + wave * WB;
+
+    // load d of a slice: block row d * RPL + lane / LPR, 16-byte chunk lane % LPR (source offset),
+    // written to LDS at chunk (lane % LPR) ^ swizzle(row)
+    const int lrow = lane / LPR, lchunk = lane % LPR;
+    auto load_pass = [&](int ib, bf16x8 (&v)[PS][KC], bf16x8 (&b)[MT][KC]) __attribute__((always_inline)) {
+        // blocks past the row's end read zeros for both operands (a zero block times a non-finite
+        // activation would not be zero)
+        const bool in = ib < i1;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t)min(ib, i1 - 1) * BS * BS, in ? BS * BS * 2 : 0);
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl)
+            if (sl < ns) {
+#pragma unroll
+                for (int d = 0; d < DPS; ++d)
+                    v[sl][d] = buf_load16(rv, (uint32_t)((s0 + sl) * SLB + (d * RPL + lrow) * RB + lchunk * 16), 0);
+            }
+        const int col = col_idx[min(ib, i1 - 1)];
+        const uint32_t xo = in ? xoff : xend;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                b[t][kc] = buf_load16(rx, xo + (uint32_t)t * 16u * (uint32_t)K * 2u + kc * 64 + (uint32_t)col * BS * 2, 0);
+    };
+
+    f32x4 acc[MT][PS];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl) acc[t][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute_pass = [&](const bf16x8 (&v)[PS][KC], const bf16x8 (&b)[MT][KC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl)
+            if (sl < ns) {
+#pragma unroll
+                for (int d = 0; d < DPS; ++d) {
+                    const int row = d * RPL + lrow;
+                    *reinterpret_cast<bf16x8 *>(wreg + sl * SLB + row * RB + ((lchunk ^ vswz<BS>(row)) << 4)) = v[sl][d];
+                }
+            }
+        bf16x8 a[PS][KC];
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl)
+            if (sl < ns) {
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+                    a[sl][kc] = *reinterpret_cast<const bf16x8 *>(wreg + sl * SLB + l16 * RB +
+                                                                 (((kc * 4 + lq) ^ vswz<BS>(l16)) << 4));
+            }
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl)
+            if (sl < ns) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) acc[t][sl] = mfma(a[sl][kc], b[t][kc], acc[t][sl]);
+            }
+    };
+
+    // this wave's blocks: e.y + wave, + NW, ...; NB register sets in a ring, the loads of the pass
+    // NB - 1 ahead requested before the current pass's products
+    bf16x8 vs[NB][PS][KC], bs[NB][MT][KC];
+    const int ib0 = e.y + wave;
+#pragma unroll
+    for (int q = 0; q < NB - 1; ++q)
+        if (ib0 + q * NW < i1) load_pass(ib0 + q * NW, vs[q], bs[q]);
+    for (int ib = ib0; ib < i1;) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int ahead = ib + (NB - 1) * NW;
+            if (ahead < i1) load_pass(ahead, vs[(q + NB - 1) % NB], bs[(q + NB - 1) % NB]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pass(vs[q], bs[q]);
+            ib += NW;
+            if (ib >= i1) break;
+        }
+    }
+    __syncthreads();   // every wave's region is free for the reduction
+    f32x4 (*red)[MT * PS][64] = reinterpret_cast<f32x4 (*)[MT * PS][64]>(smem);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int sl = 0; sl < PS; ++sl) red[wave][t * PS + sl][lane] = acc[t][sl];
+    __syncthreads();
+    // wave w < ns sums slice w over the waves; lane l holds output rows n = 4 (l / 16) .. + 3 of the
+    // slice for activation row l % 16
+    if (wave < ns) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            f32x4 v = red[0][t * PS + wave][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += red[w][t * PS + wave][lane];
+            const int row = t * 16 + l16;
+            if (row < Mc) {
+                const int n = r * BS + (s0 + wave) * 16 + lq * 4;
+                if (bias) v = add_bias4(v, bias + n);
+                store4_bf16(Y + (int64_t)(m0 + row) * N + n, v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Weight gradient on the kept blocks (block-masked SDDMM): for block i of row r, column c,
 //   dV[i][p][q] = sum_m dY[m][r*BS + p] * X[m][c*BS + q].
 // Work-group = (item, chunk of M); an item is up to kDwWaves * SL kept blocks of one tile of TR
@@ -923,6 +1070,13 @@ void launch_small_m_work(const bsr_pattern &p, const FwdArgs &a, hipStream_t st)
                        (int)a.M, a.V, a.bias, a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
 }
 
+template <int BS, int MT = 1, int NB = 2>
+void launch_small_m_lines(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
+    const dim3 grid((unsigned)(p.small_m_work.size() / 4), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+    hipLaunchKernelGGL((k_small_m_lines<BS, 8, MT, NB>), grid, dim3(8 * 64), 0, st, a.act, p.K, (int)a.M, a.V, a.bias,
+                       a.out, p.N, p.dev.col_idx, p.dev.small_m_work);
+}
+
 template <int BS, int NW, int U, int PSW, bool PIPE>
 void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)(p.R * (BS / 16 / PSW)), (unsigned)((a.M + 15) / 16));
@@ -933,23 +1087,33 @@ void launch_small_m_cfg(const bsr_pattern &p, const FwdArgs &a, hipStream_t st) 
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream) {
     const hipStream_t st = (hipStream_t)stream;
     // Default: the balanced work list (items of one or two 16-row slices, a whole number of rounds
-    // of one work-group per compute unit, heavy and light items paired over the rounds). b = 32:
-    // 8 waves x 8 blocks in flight; b = 64: 8 waves x 1 block per pass with the next pass's loads
-    // requested before the current products. Measured on the decode shape 8 x 4096 -> 14336 (cold,
-    // HIP events): 13.5 us; on the row list (two slices per work-group, configurations 0-5): 14.45
-    // (8 x 1 overlapped), 14.95 (8 x 2, no overlap), 14.9 (8 x 2 overlapped), 15.2 (16 x 1
-    // overlapped), 15.9 (8 x 4), 16.2 (one slice per work-group) -- with heaviest-first rows.
+    // of one work-group per compute unit, heavy and light items paired over the rounds) on the
+    // whole-line kernel (k_small_m_lines): 8 waves x 1 block per pass, 3 passes in flight for b = 64
+    // and 2 for b = 32. The same list on k_small_m (configurations 3 and 8: b = 32 8 waves x 8
+    // blocks, b = 64 8 waves x 1 block with 2 passes in flight) took 13.2-13.5 us on the decode shape
+    // 8 x 4096 -> 14336 (cold, HIP events) against 13.1; the row list (two slices per work-group,
+    // configurations 0-5): 14.45 (8 x 1 overlapped), 14.95 (8 x 2, no overlap), 14.9 (8 x 2
+    // overlapped), 15.2 (16 x 1 overlapped), 15.9 (8 x 4), 16.2 (one slice per work-group).
     int cfg = -1;
-    if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 6
+    if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);   // tuning knob: 0 .. 8
     if (p.b == 32) {
         switch (cfg) {
             case 0: launch_small_m_cfg<32, 8, 8, 2, false>(p, a, st); break;
             case 1: launch_small_m_cfg<32, 8, 4, 2, true>(p, a, st); break;
             case 2: launch_small_m_cfg<32, 8, 8, 2, true>(p, a, st); break;
-            default:
+            case 6:
+                if (a.M > 16) launch_small_m_lines<32, 2>(p, a, st);
+                else launch_small_m_lines<32>(p, a, st);
+                break;
+            case 3:
                 // rows above 16: two 16-row tiles per work-group, each value fragment loaded once
                 if (a.M > 16) launch_small_m_work<32, 8, 8, false, 2>(p, a, st);
                 else launch_small_m_work<32, 8, 8, false>(p, a, st);
+                break;
+            default:   // 6: whole-line value loads (BERT-base FFN-up weight, 8 / 16 / 32 rows: 9.3 / 7.5 /
+                       // 9.4 -> 8.0 / 7.3 / 8.2 us against the 8-blocks-per-pass list kernel)
+                if (a.M > 16) launch_small_m_lines<32, 2>(p, a, st);
+                else launch_small_m_lines<32>(p, a, st);
                 break;
         }
     } else {
@@ -960,10 +1124,26 @@ int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream)
             case 3: launch_small_m_cfg<64, 8, 2, 1, true>(p, a, st); break;
             case 4: launch_small_m_cfg<64, 16, 1, 2, true>(p, a, st); break;
             case 5: launch_small_m_cfg<64, 8, 4, 2, false>(p, a, st); break;
-            default:
+            case 6:
+                if (a.M > 32) launch_small_m_lines<64, 4>(p, a, st);
+                else if (a.M > 16) launch_small_m_lines<64, 2>(p, a, st);
+                else launch_small_m_lines<64>(p, a, st);
+                break;
+            case 7:
+                if (a.M > 32) launch_small_m_lines<64, 4, 3>(p, a, st);
+                else if (a.M > 16) launch_small_m_lines<64, 2, 3>(p, a, st);
+                else launch_small_m_lines<64, 1, 3>(p, a, st);
+                break;
+            case 8:
                 if (a.M > 32) launch_small_m_work<64, 8, 1, true, 4>(p, a, st);
                 else if (a.M > 16) launch_small_m_work<64, 8, 1, true, 2>(p, a, st);
                 else launch_small_m_work<64, 8, 1, true>(p, a, st);
+                break;
+            default:   // 7: whole-line value loads, 3 passes in flight per wave (decode shape, cold
+                       // sets, three interleaved runs: 13.17-13.47 -> 13.10-13.14 us)
+                if (a.M > 32) launch_small_m_lines<64, 4, 3>(p, a, st);
+                else if (a.M > 16) launch_small_m_lines<64, 2, 3>(p, a, st);
+                else launch_small_m_lines<64, 1, 3>(p, a, st);
                 break;
         }
     }
@@ -983,7 +1163,15 @@ size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan
 std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max) {
     if (M <= 0) return op == 2 ? "k_fill_zero" : "";
     if (p.device_built) small_max = std::min<int64_t>(small_max, kSmallM);
-    if (op == 0 && M <= small_max) return "k_small_m";
+    if (op == 0 && M <= small_max) {
+        int cfg = -1;
+        if (const char *f = std::getenv("BSR_SMALLM_CONFIG")) cfg = std::atoi(f);
+        // the dispatch of launch_small_m_fwd: configurations 0 .. 3 (b = 32) and 0 .. 5, 8 (b = 64)
+        // run k_small_m, every other value (the default included) the whole-line kernel
+        const bool classic = p.b == 32 ? (cfg >= 0 && cfg <= 3) : ((cfg >= 0 && cfg <= 5) || cfg == 8);
+        const bool lines = !p.device_built && !classic;
+        return lines ? "k_small_m_lines" : "k_small_m";
+    }
     if (op == 0 || op == 1) return use_wide(p, op == 1, M) ? "k_wide_gemm" : "k_panel_gemm";
     if (p.nnzb == 0) return "";
     const DwPlan pl = plan_dw(p, M);

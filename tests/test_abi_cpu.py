@@ -202,7 +202,7 @@ def test_op_kernels_names_the_dispatch():
     assert binding.op_kernels(p, "fwd", w.M) == ["k_wide_gemm"]
     assert binding.op_kernels(p, "dx", w.M) == ["k_wide_gemm"]
     assert binding.op_kernels(p, "dw", w.M) == ["k_wide_dw", "k_wide_dw_reduce"]
-    assert binding.op_kernels(p, "fwd", 8) == ["k_small_m"]
+    assert binding.op_kernels(p, "fwd", 8) == ["k_small_m_lines"]
     assert binding.op_kernels(p, "fwd", 0) == []
     assert binding.op_kernels(p, "dw", 0) == ["k_fill_zero"]
     w2 = synth.WORKLOADS[2]

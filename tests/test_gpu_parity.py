@@ -349,7 +349,7 @@ def test_workload_sampled(k, nrows, nblocks):
     _sampled_parity(w, 0, nrows, nblocks)
 
 
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7"])
 @pytest.mark.parametrize("M,N,K,b,d,seed", [(8, 512, 512, 64, 0.5, 90), (16, 384, 640, 64, 0.45, 91),
                                             (3, 256, 512, 32, 0.4, 92), (13, 640, 320, 32, 0.6, 93),
                                             (29, 512, 512, 64, 0.5, 96), (32, 384, 256, 32, 0.5, 97)])
@@ -367,12 +367,15 @@ def test_every_small_m_config(monkeypatch, cfg, M, N, K, b, d, seed):
     ("", 57, 512, 512, 64, 0.5, 106), ("", 64, 896, 640, 64, 0.4, 107),
     ("80", 48, 384, 512, 64, 0.5, 103), ("80", 80, 640, 320, 32, 0.4, 104), ("80", 71, 256, 256, 32, 0.6, 105),
 ])
-def test_small_m_row_chunks(monkeypatch, limit, M, N, K, b, d, seed):
+@pytest.mark.parametrize("cfg", ["", "6"])
+def test_small_m_row_chunks(monkeypatch, cfg, limit, M, N, K, b, d, seed):
     """The small-M forward with 2 or 4 activation tiles of 16 rows per work-group and several grid rows,
     a ragged last tile and bias: by default up to 64 rows (b = 64) or 32 (b = 32), and up to 80 rows
     with the dispatch limit raised."""
     if limit:
         monkeypatch.setenv("BSR_SMALLM_MAX", limit)
-    say(f"case small-M row chunks limit={limit or 'default'} M={M} N={N} K={K} b={b} d={d}")
+    if cfg:
+        monkeypatch.setenv("BSR_SMALLM_CONFIG", cfg)
+    say(f"case small-M row chunks cfg={cfg or 'default'} limit={limit or 'default'} M={M} N={N} K={K} b={b} d={d}")
     host = case_inputs(M, N, K, b, seed, density=d, bias=True, dy=False)
     full_parity(M, N, K, b, host, ops=("fwd",))
