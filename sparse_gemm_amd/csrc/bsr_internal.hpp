@@ -64,7 +64,9 @@ struct GroupSchedule {
 // grids of 32 x 32 accumulators. One sub-step per 64-column panel in which any member keeps a
 // block; the value block of unit u (member u / 2, block u % 2 of the panel) is staged at slot u.
 // Record, kWideRecInts ints: [0] panel, [1] presence mask (bit u = unit u has a block),
-// [2 + u] value block of unit u (-1 = none), [18], [19] unused (0).
+// [2 + u] value block of unit u (-1 = none), [18], [19] the panel's two input blocks (the
+// activation columns 32 [18] .. + 31 and 32 [19] .. + 31 staged as its 64 columns; consecutive
+// blocks for the forward, blocks paired by kept-block count for the input gradient).
 constexpr int kWideG = 8;
 constexpr int kWideU = 16;
 constexpr int kWideRecInts = 20;

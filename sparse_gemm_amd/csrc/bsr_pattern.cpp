@@ -124,45 +124,60 @@ GroupSchedule make_panels(const std::vector<int32_t> &ptr, const std::vector<int
 
 // Wide-tile schedule (b = 32): output blocks grouped kWideG at a time in order of decreasing
 // kept-block count (so that rows with the same dense column set, e.g. full rows, share groups);
-// each group walks the panels in which any member keeps a block, ascending, one sub-step each.
+// each group walks the panels in which any member keeps a block, ascending, one sub-step each. A
+// panel is two input blocks: `pairs[2p]`, `pairs[2p + 1]` (-1 = none), by default the consecutive
+// blocks 2p, 2p + 1 (whole 128-byte lines of each activation row); the input gradient pairs the
+// input blocks (block rows of W) in order of decreasing kept-block count instead, so that full
+// rows share panels whose 16 units are all kept (Zipf 16384 x 4096 -> 11008: 1640 -> 1177
+// sub-steps over the 16 groups).
 template <class ValFn>
-WideSchedule make_wide(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val) {
+WideSchedule make_wide(const std::vector<int32_t> &ptr, const std::vector<int32_t> &idx, ValFn val, int32_t nin,
+                       const std::vector<int32_t> &pairs) {
     constexpr int PB = kPanelCols / 32;
     const int32_t nout = (int32_t)ptr.size() - 1;
     const std::vector<int32_t> ids = by_count_desc(ptr);
+    // slot of each input block: panel * PB + unit half
+    std::vector<int32_t> vin(nin, -1);
+    for (size_t k = 0; k < pairs.size(); ++k)
+        if (pairs[k] >= 0) vin[pairs[k]] = (int32_t)k;
     WideSchedule s;
     s.ngroups = (nout + kWideG - 1) / kWideG;
     s.out.assign((size_t)s.ngroups * kWideG, -1);
     s.sub_ptr.assign(s.ngroups + 1, 0);
-    std::vector<int32_t> cursor(kWideG);
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> ent(kWideG);   // (slot, value block), ascending
+    std::vector<size_t> cursor(kWideG);
     for (int32_t g = 0; g < s.ngroups; ++g) {
         int members = 0;
         for (int t = 0; t < kWideG && g * kWideG + t < nout; ++t, ++members) {
-            s.out[(size_t)g * kWideG + t] = ids[g * kWideG + t];
-            cursor[t] = ptr[ids[g * kWideG + t]];
+            const int32_t o = ids[g * kWideG + t];
+            s.out[(size_t)g * kWideG + t] = o;
+            ent[t].clear();
+            for (int32_t e = ptr[o]; e < ptr[o + 1]; ++e) ent[t].push_back({vin[idx[e]], val(e)});
+            std::sort(ent[t].begin(), ent[t].end());
+            cursor[t] = 0;
         }
         int32_t nsub = 0;
         for (;;) {
             int32_t panel = INT32_MAX;
-            for (int t = 0; t < members; ++t) {
-                const int32_t o = s.out[(size_t)g * kWideG + t];
-                if (cursor[t] < ptr[o + 1]) panel = std::min(panel, idx[cursor[t]] / PB);
-            }
+            for (int t = 0; t < members; ++t)
+                if (cursor[t] < ent[t].size()) panel = std::min(panel, ent[t][cursor[t]].first / PB);
             if (panel == INT32_MAX) break;
             std::vector<int32_t> r(kWideRecInts, 0);
             r[0] = panel;
             for (int u = 0; u < kWideU; ++u) r[2 + u] = -1;
+            // the panel's two input blocks (a missing second one repeats the first: its units are
+            // absent, so its staged bytes are never used)
+            r[18] = pairs[(size_t)panel * PB];
+            r[19] = pairs[(size_t)panel * PB + 1] >= 0 ? pairs[(size_t)panel * PB + 1] : r[18];
             uint32_t mask = 0;
-            for (int t = 0; t < members; ++t) {
-                const int32_t o = s.out[(size_t)g * kWideG + t];
-                while (cursor[t] < ptr[o + 1] && idx[cursor[t]] / PB == panel) {
-                    const int u = t * PB + idx[cursor[t]] % PB;
-                    r[2 + u] = val(cursor[t]);
+            for (int t = 0; t < members; ++t)
+                while (cursor[t] < ent[t].size() && ent[t][cursor[t]].first / PB == panel) {
+                    const int u = t * PB + ent[t][cursor[t]].first % PB;
+                    r[2 + u] = ent[t][cursor[t]].second;
                     mask |= 1u << u;
                     ++s.nunits;
                     cursor[t]++;
                 }
-            }
             r[1] = (int32_t)mask;
             s.rec.insert(s.rec.end(), r.begin(), r.end());
             ++nsub;
@@ -182,6 +197,13 @@ WideSchedule make_wide(const std::vector<int32_t> &ptr, const std::vector<int32_
         return s.sub_ptr[a + 1] - s.sub_ptr[a] > s.sub_ptr[b + 1] - s.sub_ptr[b];
     });
     return s;
+}
+
+// Consecutive input blocks in panels (2p, 2p + 1), padded with -1 to whole panels.
+std::vector<int32_t> consecutive_pairs(int32_t nin) {
+    std::vector<int32_t> v((size_t)(nin + 1) / 2 * 2, -1);
+    for (int32_t k = 0; k < nin; ++k) v[k] = k;
+    return v;
 }
 
 // Weight-gradient items: the kept blocks of every tile (dw_tile_rows x dw_tile_cols block
@@ -440,8 +462,14 @@ void build_pattern(bsr_pattern &p) {
         p.bwd[k] = make_panels(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.b, v.G, v.S);
     }
     if (p.b == 32) {
-        p.wide_fwd = make_wide(p.row_ptr, p.col_idx, [](int32_t e) { return e; });
-        p.wide_bwd = make_wide(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; });
+        p.wide_fwd = make_wide(p.row_ptr, p.col_idx, [](int32_t e) { return e; }, p.C, consecutive_pairs(p.C));
+        // input gradient: block rows of W paired by decreasing kept-block count (stable: equal
+        // counts keep their natural, consecutive order)
+        std::vector<int32_t> rows_pairs = by_count_desc(p.row_ptr);
+        if (const char *f = std::getenv("BSR_WIDE_PAIRS"))   // tuning knob: 0 = consecutive pairs
+            if (std::atoi(f) == 0) rows_pairs = consecutive_pairs(p.R);
+        rows_pairs.resize((size_t)(p.R + 1) / 2 * 2, -1);
+        p.wide_bwd = make_wide(p.col_ptr, p.row_idx, [&](int32_t e) { return p.perm[e]; }, p.R, rows_pairs);
     } else {
         p.wide_fwd = WideSchedule();
         p.wide_bwd = WideSchedule();

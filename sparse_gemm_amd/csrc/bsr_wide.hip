@@ -51,6 +51,7 @@ static_assert(kSmem <= 160 * 1024, "LDS of one work-group");
 
 struct WideRec {
     int panel, mask, blk[4];   // blk: this wave's units wave + 4 j
+    int segA, segB;            // byte offsets in an activation row of the panel's two input blocks
 };
 
 struct WideArgs {
@@ -88,17 +89,20 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
         x.mask = DENSE ? (1 << kWideU) - 1 : __builtin_amdgcn_readfirstlane(e[1]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + wave + 4 * j]);
+        x.segA = __builtin_amdgcn_readfirstlane(e[18]) * 64;
+        x.segB = __builtin_amdgcn_readfirstlane(e[19]) * 64;
         return x;
     };
-    // activation load i = wave + 4 j (j < 8) of panel x.panel into activation stage xs: rows
-    // 8 i .. 8 i + 7 (lane -> row 8 i + lane / 8, LDS chunk lane % 8 holding source chunk (lane % 8)
-    // ^ swz8(row)). Rows past M and columns past the matrix (a last half panel) read as zeros
-    // through the range-checked voffset.
+    // activation load i = wave + 4 j (j < 8) of the panel into activation stage xs: rows 8 i .. 8 i
+    // + 7 (lane -> row 8 i + lane / 8, LDS chunk lane % 8 holding source chunk q = (lane % 8) ^
+    // swz8(row): 16 bytes q % 4 of input block segA (q < 4) or segB). Rows past M read as zeros
+    // through the range-checked voffset; a last half panel's missing block is never used.
     auto issue_x = [&](int xs, const WideRec &x, int j) __attribute__((always_inline)) {
         const int i = wave + 4 * j;
         const int r = i * 8 + (lane >> 3);
+        const int q = (lane & 7) ^ swz8(r);
         dma16(ra, sbase + (uint32_t)xs * kXB + (uint32_t)i * 1024u,
-              (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)x.panel * 128u + (uint32_t)(((lane & 7) ^ swz8(r)) << 4), 0);
+              (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)(q < 4 ? x.segA : x.segB) + (uint32_t)((q & 3) << 4), 0);
     };
     // value block of unit u = wave + 4 t (if kept) into value stage vs: two 1 KB halves (lane ->
     // block row 16 q + lane / 4, chunk (lane % 4) ^ swz4(row))

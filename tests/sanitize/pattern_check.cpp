@@ -123,6 +123,7 @@ static void check_pattern(const bsr_pattern &p) {
             REQUIRE((size_t)s.nsub() * kWideRecInts == s.rec.size() && (int)s.flags.size() == s.ngroups);
             std::vector<int> seen(n, 0), oseen(nout, 0);
             int64_t units = 0;
+            std::vector<std::vector<std::pair<int32_t, int32_t>>> pair_of((size_t)(dir ? R : C) + 1);
             for (int g = 0; g < s.ngroups; ++g) {
                 bool dense = s.sub_ptr[g + 1] > s.sub_ptr[g];
                 for (int32_t k = s.sub_ptr[g]; k < s.sub_ptr[g + 1]; ++k) {
@@ -130,6 +131,14 @@ static void check_pattern(const bsr_pattern &p) {
                     if (k > s.sub_ptr[g]) REQUIRE(r[0] > r[-kWideRecInts]);
                     dense = dense && (uint32_t)r[1] == 0xFFFFu;
                     REQUIRE(r[1] != 0);
+                    // the panel's two input blocks: in range; the forward's are consecutive; a
+                    // repeated first block (no second one) carries no unit of the second half
+                    const int32_t nin = dir ? R : C;
+                    REQUIRE(r[18] >= 0 && r[18] < nin && r[19] >= 0 && r[19] < nin);
+                    if (!dir) REQUIRE(r[18] == 2 * r[0] && (r[19] == 2 * r[0] + 1 || (r[19] == r[18] && 2 * r[0] + 1 == C)));
+                    if (r[19] == r[18])
+                        for (int u = 1; u < kWideU; u += 2) REQUIRE(((r[1] >> u) & 1) == 0);
+                    pair_of[(size_t)r[0]].push_back({r[18], r[19]});
                     for (int u = 0; u < kWideU; ++u) {
                         const bool present = (r[1] >> u) & 1;
                         REQUIRE(present == (r[2 + u] >= 0));
@@ -137,7 +146,7 @@ static void check_pattern(const bsr_pattern &p) {
                         const int32_t o = s.out[(size_t)g * kWideG + u / 2];
                         REQUIRE(o >= 0 && o < nout);
                         if (o < 0 || o >= nout) continue;
-                        const int32_t want = r[0] * 2 + u % 2;
+                        const int32_t want = u % 2 ? r[19] : r[18];
                         int32_t e = -1;
                         for (int32_t q = ptr[o]; q < ptr[o + 1]; ++q)
                             if (idx[q] == want) e = dir ? p.perm[q] : q;
@@ -155,6 +164,15 @@ static void check_pattern(const bsr_pattern &p) {
             REQUIRE(units == s.nunits && units == n);
             for (int32_t i = 0; i < n; ++i) REQUIRE(seen[i] == 1);
             for (int32_t o = 0; o < nout; ++o) REQUIRE(oseen[o] == 1);
+            // one pair per panel, and every input block in at most one panel
+            std::vector<int> in_panel((size_t)(dir ? R : C), 0);
+            for (auto &v : pair_of) {
+                for (auto &q : v) REQUIRE(q == v[0]);
+                if (v.empty()) continue;
+                in_panel[v[0].first]++;
+                if (v[0].second != v[0].first) in_panel[v[0].second]++;
+            }
+            for (int x : in_panel) REQUIRE(x <= 1);
         }
     } else {
         REQUIRE(p.wide_fwd.ngroups == 0 && p.wide_bwd.ngroups == 0 && p.wdw.n == 0);
