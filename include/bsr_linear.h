@@ -163,7 +163,7 @@ int32_t bsr_linear_bwd_weight(const bsr_pattern *p, const bsr_bf16 *dY, const bs
 /* Names of the main kernels one call launches, for matching measurements (kernel traces, counters)
  * to calls: the per-op times the pages compare (pytorch_block_sparse summary page, "Performance and
  * Memory Efficiency") are sums of these kernels. op: 0 bsr_linear_fwd, 1 bsr_linear_bwd_input,
- * 2 bsr_linear_bwd_weight (the bias-gradient kernels excluded); M rows. Writes a NUL-terminated,
+ * 2 bsr_linear_bwd_weight (the bias-gradient kernels excluded), 3 bsr_linear_fwd_24; M rows. Writes a NUL-terminated,
  * comma-separated list (possibly empty) to buf[len]; BSR_ERR_INVALID_ARG for a NULL pattern or
  * buffer, an unknown op, M < 0 or a buffer too small. Host only, no device access. */
 int32_t bsr_op_kernels(const bsr_pattern *p, int32_t op, int64_t M, char *buf, int32_t len);

@@ -235,9 +235,9 @@ def bwd_weight_workspace_bytes(p: Pattern, M: int) -> int:
 
 
 def op_kernels(p: Pattern, op: str, M: int) -> list:
-    """Names of the main kernels one call of op ("fwd", "dx" or "dw") launches for M rows (the
-    bias gradient's excluded), as the library dispatches them."""
-    code = {"fwd": 0, "dx": 1, "dw": 2}[op]
+    """Names of the main kernels one call of op ("fwd", "dx", "dw" or "fwd_24") launches for M rows
+    (the bias gradient's excluded), as the library dispatches them."""
+    code = {"fwd": 0, "dx": 1, "dw": 2, "fwd_24": 3}[op]
     buf = ctypes.create_string_buffer(256)
     _lib.check(lib().bsr_op_kernels(p.handle, code, int(M), buf, len(buf)), "bsr_op_kernels")
     names = buf.value.decode()

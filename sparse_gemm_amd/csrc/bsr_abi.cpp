@@ -274,7 +274,9 @@ int32_t bsr_linear_bwd_input(const bsr_pattern *p, const bsr_bf16 *dY, int64_t M
 int32_t bsr_op_kernels(const bsr_pattern *p, int32_t op, int64_t M, char *buf, int32_t len) {
     BSR_TRY_BEGIN
     if (!p) return fail(BSR_ERR_INVALID_ARG, "pattern is NULL");
-    if (op < 0 || op > 2) return fail(BSR_ERR_INVALID_ARG, "op must be 0 (forward), 1 (input gradient) or 2 (weight gradient)");
+    if (op < 0 || op > 3)
+        return fail(BSR_ERR_INVALID_ARG,
+                    "op must be 0 (forward), 1 (input gradient), 2 (weight gradient) or 3 (2:4 forward)");
     if (M < 0) return fail(BSR_ERR_INVALID_ARG, "M must be >= 0");
     if (!buf || len <= 0) return fail(BSR_ERR_INVALID_ARG, "buf must hold at least one byte");
     const std::string names = kernels_of(*p, op, M, small_m_max(*p));
@@ -469,11 +471,16 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
     BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
     BSR_CHECK(check_ptr(bias, "bias", true));
     BSR_CHECK(check_ptr(Y, "Y", M == 0));
-    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
     if ((size_t)p->nnzb * p->b * p->b >= (size_t)0xFFFFFFF0u)
         return fail(BSR_ERR_INVALID_ARG, "compressed block values above 4 GiB");
-    if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     if (M == 0) return BSR_OK;
+    // many rows over block rows kept in most panels: the wide tile on the compressed blocks
+    if (use_wide(*p, false, M)) {
+        const FwdArgs a{X, M, p->K, nullptr, bias, Y, p->N};
+        return launch_wide_gemm_24(*p, a, Vc, meta, stream);
+    }
+    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
+    if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     return launch_fwd_24(*p, X, M, Vc, meta, bias, Y, stream);
     BSR_TRY_END
 }

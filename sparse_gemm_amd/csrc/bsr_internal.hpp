@@ -208,6 +208,9 @@ struct FwdArgs {
 // Whether the wide-tile kernel takes this call (dense groups, enough rows).
 bool use_wide(const bsr_pattern &p, bool transposed, int64_t M);
 int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream);
+// the wide forward with 2:4-compressed blocks (Vc [nnzb][32][16], meta [nnzb][32][2])
+int32_t launch_wide_gemm_24(const bsr_pattern &p, const FwdArgs &a, const uint16_t *Vc, const uint16_t *meta,
+                            void *stream);
 // sparse24: forward only; a.V holds 2:4 block images (bsr_values_pack_24) instead of bf16 blocks.
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream,
                           bool sparse24 = false);

@@ -1162,6 +1162,7 @@ size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan
 
 std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max) {
     if (M <= 0) return op == 2 ? "k_fill_zero" : "";
+    if (op == 3) return use_wide(p, false, M) ? "k_wide_gemm_24" : "k_fwd_24";
     if (p.device_built) small_max = std::min<int64_t>(small_max, kSmallM);
     if (op == 0 && M <= small_max) {
         int cfg = -1;

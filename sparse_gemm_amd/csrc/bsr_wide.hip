@@ -306,6 +306,242 @@ __global__ __launch_bounds__(256, 1) void k_wide_gemm(WideArgs a, const int32_t 
 }
 
 // ------------------------------------------------------------------------------------------
+// 2:4 wide-tile forward (b = 32): the wide GEMM's tile, schedule and pipeline with every kept block
+// in the compressed 2:4 form (torchao sparsity README, Table 4.1: half the values plus 2-bit
+// indices): Vc holds a block's 32 rows x 16 kept values (1 KB), meta its 32 rows x two 16-bit
+// index words (128 bytes). Both are staged as they are (1 KB of values per unit, identity lane map;
+// each wave's 4 units' index words by one load whose lanes 32 .. 63 read zeros), so a sub-step
+// stages 20 KB of values instead of 32. Per block and row tile one v_smfmac_f32_32x32x32_bf16: lane
+// (row n = l % 32, half h = l / 32) takes 8 kept values of columns 16 h .. 16 h + 15 of block row n
+// and their 16 index bits; the activation operand is the two 16-deep fragments of the block's 32
+// columns, concatenated. Sub-step s: the block-0 products (with 6 activation loads of s + 2 among
+// them), the wait and the barrier, then the block-1 products (with the other 2 and the value loads
+// of s + 2): 6 and 7 loads per half, as the compute unit's load path takes them.
+// ------------------------------------------------------------------------------------------
+constexpr int kVB24 = kWideU * 1024 + 4 * 1024;                   // staged values + index words
+constexpr uint32_t kPastEnd24 = 0xFFFFFFF0u;   // past both compressed arrays: such a load reads zeros
+constexpr int kStages24 = kXStages * kXB + kVStages * kVB24;      // 136 KB
+constexpr int kSmem24 = kWideRows * kOutPitch > kStages24 ? kWideRows * kOutPitch : kStages24;
+static_assert(kSmem24 <= 160 * 1024, "LDS of one work-group");
+
+struct WideArgs24 {
+    const uint16_t *act;
+    int in_ld, M;
+    const uint16_t *Vc;
+    uint32_t vc_bytes;
+    const uint16_t *meta;
+    uint32_t meta_bytes;
+    const uint16_t *bias;
+    uint16_t *out;
+    int out_ld;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t *__restrict__ sub_ptr,
+                                             const int32_t *__restrict__ gout, const int32_t *__restrict__ rec, int g,
+                                             int mt0, unsigned char *smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    const int rows = min(kWideRows, a.M - mt0 * kWideRows);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (int64_t)mt0 * kWideRows * a.in_ld, (uint32_t)rows * a.in_ld * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.Vc, a.vc_bytes);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta, a.meta_bytes);
+    const uint32_t sbase = lds_addr(smem);
+    const uint32_t vbase = sbase + kXStages * kXB;
+
+    auto load_rec = [&](int s) __attribute__((always_inline)) {
+        const int32_t *e = rec + (size_t)s * kWideRecInts;
+        WideRec x;
+        x.panel = __builtin_amdgcn_readfirstlane(e[0]);
+        x.mask = DENSE ? (1 << kWideU) - 1 : __builtin_amdgcn_readfirstlane(e[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + wave + 4 * j]);
+        x.segA = __builtin_amdgcn_readfirstlane(e[18]) * 64;
+        x.segB = __builtin_amdgcn_readfirstlane(e[19]) * 64;
+        return x;
+    };
+    // activation load i = wave + 4 j (j < 8): as the wide GEMM
+    auto issue_x = [&](int xs, const WideRec &x, int j) __attribute__((always_inline)) {
+        const int i = wave + 4 * j;
+        const int r = i * 8 + (lane >> 3);
+        const int q = (lane & 7) ^ swz8(r);
+        dma16(ra, sbase + (uint32_t)xs * kXB + (uint32_t)i * 1024u,
+              (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)(q < 4 ? x.segA : x.segB) + (uint32_t)((q & 3) << 4), 0);
+    };
+    // kept values of unit u = wave + 4 t (if kept): 1 KB to unit slot u
+    auto issue_v = [&](int vs, const WideRec &x, int t) __attribute__((always_inline)) {
+        const int u = wave + 4 * t;
+        if (DENSE || ((x.mask >> u) & 1))
+            dma16(rv, vbase + (uint32_t)vs * kVB24 + (uint32_t)u * 1024u, (uint32_t)lane * 16u, (uint32_t)x.blk[t] * 1024u);
+    };
+    // index words of this wave's units wave + 4 t: lanes 8 t .. 8 t + 7 load unit t's 128 bytes to
+    // this wave's 1 KB (t * 128 ..); lanes 32 .. 63 and absent units read zeros
+    auto issue_m = [&](int vs, const WideRec &x) __attribute__((always_inline)) {
+        const int t = (lane >> 3) & 3;
+        const int blk = t == 0 ? x.blk[0] : t == 1 ? x.blk[1] : t == 2 ? x.blk[2] : x.blk[3];
+        const uint32_t voff = lane < 32 && blk >= 0 ? (uint32_t)blk * 128u + (uint32_t)(lane & 7) * 16u : kPastEnd24;
+        dma16(rm, vbase + (uint32_t)vs * kVB24 + kWideU * 1024u + (uint32_t)wave * 1024u, voff, 0);
+    };
+
+    f32x16 acc[4][4];   // [row tile][member of the wave]
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.f;
+
+    auto xfrag = [&](const unsigned char *xt, int rt, int c) __attribute__((always_inline)) {
+        const int r = wr * 128 + rt * 32 + l32;
+        return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
+    };
+    // fragments of block h of the panel: the activation fragments of its chunks 2 h, 2 h + 1, and the
+    // kept values and index bits of each member t's unit 2 (4 wm + t) + h (present or not: a read of
+    // an unused slot is harmless)
+    bf16x16 xf[2][4];
+    bf16x8 af[2][4];
+    int ai[2][4];
+    auto read_frags = [&](int set, int xs, int vs, int h) __attribute__((always_inline)) {
+        const unsigned char *xt = smem + xs * kXB;
+        const unsigned char *vt = smem + kXStages * kXB + vs * kVB24;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            xf[set][rt].lo = xfrag(xt, rt, 2 * h);
+            xf[set][rt].hi = xfrag(xt, rt, 2 * h + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int u = 2 * (4 * wm + t) + h;
+            af[set][t] = *reinterpret_cast<const bf16x8 *>(vt + u * 1024 + l32 * 32 + lh * 16);
+            ai[set][t] = *reinterpret_cast<const uint16_t *>(vt + kWideU * 1024 + (u & 3) * 1024 + (u >> 2) * 128 + l32 * 4 +
+                                                             lh * 2);
+        }
+    };
+    auto products = [&](int set, int h, int m8, auto &&after) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (DENSE || ((m8 >> (2 * t + h)) & 1)) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    acc[rt][t] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[set][t], xf[set][rt], acc[rt][t],
+                                                                           ai[set][t], 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            after(t);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
+    if (s0 < s1) {
+        WideRec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
+        WideRec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_x(0, r0, j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) issue_v(0, r0, t);
+        issue_m(0, r0);
+        if (s0 + 1 < s1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) issue_x(1, r1, j);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) issue_v(1, r1, t);
+            issue_m(1, r1);
+        }
+        wait_vm<0, 0>(0);
+        __syncthreads();
+        read_frags(0, 0, 0, 0);
+        int xs = 0, vs = 0;
+        for (int s = s0; s < s1; ++s) {
+            const int m8 = (r0.mask >> (8 * wm)) & 0xFF;
+            const bool more2 = s + 2 < s1;
+            const int x2 = xs == 0 ? 2 : xs - 1;   // activation stage of s + 2 (that of s - 1)
+            read_frags(1, xs, vs, 1);
+            // block 0's products with 6 of the 8 activation loads of s + 2 (2, 2, 1, 1 per member group)
+            products(0, 0, m8, [&](int t) __attribute__((always_inline)) {
+                if (more2) {
+                    issue_x(x2, r2, t < 2 ? 2 * t : t + 2);
+                    if (t < 2) issue_x(x2, r2, 2 * t + 1);
+                }
+            });
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const WideRec r4 = load_rec(min(s + 4, s1 - 1));
+            // this wave's loads of s + 1 have landed; the 6 activation loads of s + 2 may be in flight
+            if (more2) wait_vm<6, 6>(6);
+            else wait_vm<0, 0>(0);
+            __syncthreads();
+            const int xn = xs == 2 ? 0 : xs + 1, vn = vs ^ 1;
+            read_frags(0, xn, vn, 0);   // block 0 of s + 1 (harmless past the last sub-step)
+            // block 1's products with the last 2 activation loads of s + 2 (its stage is that of
+            // s - 1) and the value loads of s + 2 (into the stage of s, free since the barrier)
+            products(1, 1, m8, [&](int t) __attribute__((always_inline)) {
+                if (more2) {
+                    if (t < 2) issue_x(x2, r2, 6 + t);
+                    issue_v(vs, r2, t);
+                    if (t == 3) issue_m(vs, r2);
+                }
+            });
+            r0 = r1;
+            r1 = r2;
+            r2 = r3;
+            r3 = r4;
+            xs = xn;
+            vs = vn;
+        }
+    }
+    __syncthreads();   // the stages are free for the output tile
+
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tg = wm * 4 + t;
+        const int o = gout[g * kWideG + tg];
+        if (o < 0) continue;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tg * 32 + q * 8 + lh * 4;
+                const int row = wr * 128 + rt * 32 + l32;
+                f32x4 v = quad(acc[rt][t], q);
+                if (a.bias) v = add_bias4(v, a.bias + o * 32 + q * 8 + lh * 4);
+                store4_bf16(reinterpret_cast<uint16_t *>(smem + row * kOutPitch + c * 2), v[0], v[1], v[2], v[3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    const int m0 = mt0 * kWideRows + wave * 64;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+        const int seg = i * 64 + lane, row = seg >> 5, cs = seg & 31;
+        const int t = cs >> 2, within = (cs & 3) * 8;
+        const int o = gout[g * kWideG + t];
+        if (o < 0 || m0 + row >= a.M) continue;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 64 + row) * kOutPitch + cs * 16);
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(a.out + (int64_t)(m0 + row) * a.out_ld + o * 32 + within));
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void k_wide_gemm_24(WideArgs24 a, const int32_t *__restrict__ order,
+                                                         const int32_t *__restrict__ flags,
+                                                         const int32_t *__restrict__ sub_ptr,
+                                                         const int32_t *__restrict__ gout,
+                                                         const int32_t *__restrict__ rec, int ngroups, int nmtiles,
+                                                         int tpc) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem24];
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = L / (tpc * ngroups), r4 = L % (tpc * ngroups);
+    const int mc = min(tpc, nmtiles - tpc * chunk);
+    const int g = order[r4 / mc];
+    const int mt0 = tpc * chunk + r4 % mc;
+    if (flags[g]) wide_tile_24<true>(a, sub_ptr, gout, rec, g, mt0, smem);
+    else wide_tile_24<false>(a, sub_ptr, gout, rec, g, mt0, smem);
+}
+
+// ------------------------------------------------------------------------------------------
 // Wide weight gradient (b = 32): for the kept blocks of a tile of 4 block rows x 16 block columns
 // (any rows, any columns),
 //   dV[i][p][q] = sum_m dY[m][r*32 + p] * X[m][c*32 + q]     (the block-masked SDDMM)
@@ -674,6 +910,28 @@ int32_t launch_wide_dw(const bsr_pattern &p, const DwArgs &a, const WideDwPlan &
         e = hipGetLastError();
         if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide weight-gradient reduce: ") + hipGetErrorString(e));
     }
+    return BSR_OK;
+}
+
+int32_t launch_wide_gemm_24(const bsr_pattern &p, const FwdArgs &a, const uint16_t *Vc, const uint16_t *meta,
+                            void *stream) {
+    const hipStream_t st = (hipStream_t)stream;
+    const WideSchedule &s = p.wide_fwd;
+    const DevSchedule &d = p.dev.wide_fwd;
+    const int nmtiles = (int)((a.M + kWideRows - 1) / kWideRows);
+    const int64_t nwg = (int64_t)s.ngroups * nmtiles;
+    if (nwg > (int64_t)INT32_MAX) return fail(BSR_ERR_INVALID_ARG, "problem too large for one launch");
+    if ((size_t)p.nnzb * 1024 >= (size_t)kPastEnd24) return fail(BSR_ERR_INVALID_ARG, "compressed values above 4 GiB");
+    if ((int64_t)kWideRows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
+        return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
+    if (nwg == 0) return BSR_OK;
+    const int tpc = wide_tiles_per_chunk(nmtiles);
+    const WideArgs24 wa{a.act, a.in_ld, (int)a.M, Vc, (uint32_t)((size_t)p.nnzb * 1024), meta,
+                        (uint32_t)((size_t)p.nnzb * 128), a.bias, a.out, a.out_ld};
+    hipLaunchKernelGGL(k_wide_gemm_24, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr, d.out,
+                       d.rec, s.ngroups, nmtiles, tpc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide 2:4 gemm launch: ") + hipGetErrorString(e));
     return BSR_OK;
 }
 

@@ -205,6 +205,8 @@ def test_op_kernels_names_the_dispatch():
     assert binding.op_kernels(p, "fwd", 8) == ["k_small_m_lines"]
     assert binding.op_kernels(p, "fwd", 0) == []
     assert binding.op_kernels(p, "dw", 0) == ["k_fill_zero"]
+    assert binding.op_kernels(p, "fwd_24", w.M) == ["k_wide_gemm_24"]
+    assert binding.op_kernels(p, "fwd_24", 8) == ["k_fwd_24"]
     w2 = synth.WORKLOADS[2]
     p2 = Pattern.from_mask(synth.block_mask(w2, 0), w2.N, w2.K, w2.b, upload=False)
     assert binding.op_kernels(p2, "fwd", w2.M)[0] in ("k_panel_gemm", "k_wide_gemm")
@@ -212,7 +214,7 @@ def test_op_kernels_names_the_dispatch():
     L = _lib.load()
     buf = ctypes.create_string_buffer(4)
     assert L.bsr_op_kernels(p.handle, 0, w.M, buf, 4) == 1   # too small
-    assert L.bsr_op_kernels(p.handle, 3, w.M, buf, 4) == 1
+    assert L.bsr_op_kernels(p.handle, 4, w.M, buf, 4) == 1
     assert L.bsr_op_kernels(p.handle, 0, -1, buf, 4) == 1
     assert L.bsr_op_kernels(None, 0, 1, buf, 4) == 1
 

@@ -305,3 +305,96 @@ def test_fwd_fp8_24_decode_workload_full():
     res = oracle.tolerance_check(Y.cpu(), ref, S)
     assert res["violations"] == 0, res
     p.close()
+
+
+# ---- the wide tile on the compressed blocks (b = 32, many rows, dense groups) ----
+
+def _mixed_mask(R, C, nfull, seed, density=0.15):
+    g = np.random.default_rng(seed)
+    mask = (g.random((R, C)) < density).astype(np.uint8)
+    mask[g.choice(R, size=nfull, replace=False)] = 1
+    mask[R - 1] = 0
+    return mask
+
+
+@pytest.mark.parametrize("M,R,C,nfull,seed,force", [
+    (700, 20, 15, 10, 70, False),    # 3 groups (8, 8, 4 members), a last half panel, ragged row tile
+    (256, 8, 16, 8, 71, False),      # one group, every sub-step dense
+    (513, 33, 8, 20, 72, True),      # the last group with one member, a one-row last tile
+    (300, 24, 40, 3, 73, True),      # mostly sparse rows: sub-steps with absent units
+])
+def test_fwd_24_wide_matches_oracle_and_image(monkeypatch, M, R, C, nfull, seed, force):
+    """bsr_linear_fwd_24 through the wide tile against the oracle's forward on the decompressed
+    blocks, and bit for bit against the image forward (same per-output order of sparse products)."""
+    b = 32
+    N, K = R * b, C * b
+    mask = _mixed_mask(R, C, nfull, seed)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    if force:
+        monkeypatch.setenv("BSR_GEMM_VARIANT", "4")
+    assert binding.op_kernels(p, "fwd_24", M) == ["k_wide_gemm_24"]
+    say(f"case 2:4 wide fwd M={M} R={R} C={C} full={nfull} nnzb={p.nnzb}")
+    V = _values(p.nnzb, b, seed)
+    X = synth.activations(M, K, seed)
+    bb = synth.bias_vector(N, seed)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_24(p, X.to(dev()), Vc, mt, bb.to(dev()), out=Y)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("BSR_GEMM_VARIANT", raising=False)
+    img = binding.values_pack_24(p, Vc, mt)
+    Yi = binding.linear_fwd_24_image(p, X.to(dev()), img, bb.to(dev()))
+    torch.cuda.synchronize()
+    assert torch.equal(Y.cpu().view(torch.int16), Yi.cpu().view(torch.int16))
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, S = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, N, b, bias=bb)
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    2:4 wide fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+def test_fwd_24_wide_integer_inputs_bit_exact():
+    """Integer activations and blocks: the wide 2:4 forward equals the oracle bit for bit."""
+    M, R, C, b = 300, 16, 8, 32
+    mask = _mixed_mask(R, C, 12, 74)
+    g = np.random.default_rng(74)
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, R * b, C * b, b)
+    assert binding.op_kernels(p, "fwd_24", M) == ["k_wide_gemm_24"]
+    X = torch.from_numpy(g.integers(-2, 3, size=(M, C * b)).astype(np.float32)).to(torch.bfloat16)
+    V = torch.from_numpy(g.integers(-1, 2, size=(p.nnzb, b, b)).astype(np.float32)).to(torch.bfloat16)
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Y = binding.linear_fwd_24(p, X.to(dev()), Vc, mt)
+    torch.cuda.synchronize()
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, _ = oracle.fwd(X, md["row_ptr"], md["col_idx"], D, R * b, b, want_s=False)
+    assert np.array_equal(Y.cpu().double().numpy(), ref)
+    p.close()
+
+
+def test_fwd_24_wide_zipf_workload():
+    """The Zipf 16384 x 4096 -> 11008 layer with its blocks pruned to 2:4: the wide tile takes it;
+    sampled rows against the oracle, and every row bit for bit against the image forward."""
+    w = synth.WORKLOADS[5]
+    say(f"case 2:4 wide fwd {w.name}")
+    host = synth.make_inputs(w, 0, with_dy=False)
+    md = meta.scan(host["mask"])
+    p = Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    assert binding.op_kernels(p, "fwd_24", w.M) == ["k_wide_gemm_24"]
+    Xd = host["X"].to(dev())
+    Vc, mt = binding.values_compress_24(p, host["V"].to(dev()))
+    Y = binding.linear_fwd_24(p, Xd, Vc, mt)
+    Yi = binding.linear_fwd_24_image(p, Xd, binding.values_pack_24(p, Vc, mt))
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
+    g = np.random.default_rng([0, 79])
+    rows = np.unique(np.concatenate([[0, w.M - 1], g.choice(w.M, size=48, replace=False)]))
+    rows_t = torch.from_numpy(rows)
+    D = oracle.decompress_24(*oracle.compress_24(host["V"]))
+    ref, S = oracle.fwd(host["X"][rows_t], md["row_ptr"], md["col_idx"], D, w.N, w.b)
+    res = oracle.tolerance_check(Y.cpu()[rows_t], ref, S)
+    say(f"    2:4 wide fwd ({rows.size} rows): max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
