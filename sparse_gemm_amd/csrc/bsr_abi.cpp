@@ -479,6 +479,11 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
         const FwdArgs a{X, M, p->K, nullptr, bias, Y, p->N};
         return launch_wide_gemm_24(*p, a, Vc, meta, stream);
     }
+    // many rows otherwise: the panel GEMM staging the compressed blocks as they are
+    if (M > small_m_max(*p)) {
+        const FwdArgs a{X, M, p->K, Vc, bias, Y, p->N};
+        return launch_group_gemm(*p, false, a, stream, true, meta);
+    }
     if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
     if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     return launch_fwd_24(*p, X, M, Vc, meta, bias, Y, stream);

@@ -211,9 +211,10 @@ int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a
 // the wide forward with 2:4-compressed blocks (Vc [nnzb][32][16], meta [nnzb][32][2])
 int32_t launch_wide_gemm_24(const bsr_pattern &p, const FwdArgs &a, const uint16_t *Vc, const uint16_t *meta,
                             void *stream);
-// sparse24: forward only; a.V holds 2:4 block images (bsr_values_pack_24) instead of bf16 blocks.
+// sparse24: forward only; a.V holds 2:4 block images (bsr_values_pack_24) instead of bf16 blocks,
+// or with meta24 the kept values of the compressed form (meta24: its index words).
 int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream,
-                          bool sparse24 = false);
+                          bool sparse24 = false, const uint16_t *meta24 = nullptr);
 int32_t launch_small_m_fwd(const bsr_pattern &p, const FwdArgs &a, void *stream);
 
 struct DwArgs {

@@ -54,9 +54,14 @@ __device__ __forceinline__ u32x4 buf_load16u(__amdgpu_buffer_rsrc_t r, uint32_t 
 // bank conflicts.
 // ------------------------------------------------------------------------------------------
 
-template <int BS, int G, int S, int NW, int NL, int NST, int MS, bool TRANS, bool SP = false>
+// SP: the form of the value blocks (forward only): kDense bf16 blocks, kImage24 2:4 block images
+// (bsr_values_pack_24), kCompact24 the compressed 2:4 form as it is (kept values V [nnzb][BS][BS/2],
+// index words meta [nnzb][BS][BS/16]).
+constexpr int kDense = 0, kImage24 = 1, kCompact24 = 2;
+template <int BS, int G, int S, int NW, int NL, int NST, int MS, bool TRANS, int SP = kDense>
 __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const uint16_t *__restrict__ act, int in_ld, int M, const uint16_t *__restrict__ V, uint32_t v_bytes,
+    const uint16_t *__restrict__ meta, uint32_t m_bytes,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int out_ld, const int32_t *__restrict__ order,
     const int32_t *__restrict__ sub_ptr, const int32_t *__restrict__ gout, const int32_t *__restrict__ rec,
     int ngroups, int nmtiles, int tpc) {
@@ -77,6 +82,11 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     constexpr int D = NST - 1;              // sub-steps in flight ahead of the one computed
     static_assert(NST == 2 || NST == 3, "two or three stages");
     constexpr int CPS = WBB / 1024;         // 1 KB load chunks per block
+    // compressed 2:4 blocks in a slot of WBB bytes: the kept values (rows of BS bytes) in its first
+    // CB bytes (chunks 0 .. CB / 1024 - 1), the index words (rows of BS / 8 bytes) in the MB bytes
+    // after them (chunk CB / 1024, lanes below MB / 16); the slot's remaining chunks load nothing
+    constexpr int CB = BS * BS, MB = BS * BS / 8;
+    static_assert(SP != kCompact24 || (!TRANS && CB + 1024 <= WBB), "compressed slot layout");
     constexpr int XPL = BM / 8 / NL;        // activation loads (8 rows x 128 bytes) per loader wave
     constexpr int WPL = S * CPS / NL;       // value-block chunks per loader wave
     constexpr int MAXL = XPL + WPL + 1;     // loads per loader wave and sub-step, at most
@@ -107,6 +117,7 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
     const int rows = min(BM, M - mt0 * BM);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(act + (int64_t)mt0 * BM * in_ld, (uint32_t)rows * in_ld * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V, v_bytes);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta, m_bytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, (uint32_t)sub_ptr[ngroups] * kRecInts * 4);
     const uint32_t sbase = lds_addr(smem);
     // loader lw's activation load i stages tile rows 8 (lw + NL i) .. + 7: lane -> row + lane / 8,
@@ -159,9 +170,20 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
         for (int j = 0; j < WPL; ++j) {
             const int c = lw + NL * j;
             if (x.blk[j] >= 0) {
-                dma16(rv, base + XB + (uint32_t)(c / CPS) * WBB + (uint32_t)(c % CPS) * 1024u, woff(j),
-                      (uint32_t)x.blk[j] * WBB);
-                ++n;
+                const uint32_t dst = base + XB + (uint32_t)(c / CPS) * WBB + (uint32_t)(c % CPS) * 1024u;
+                if constexpr (SP == kCompact24) {
+                    const int q = c % CPS;
+                    if (q < CB / 1024) {
+                        dma16(rv, dst, (uint32_t)lane * 16u, (uint32_t)x.blk[j] * CB + (uint32_t)q * 1024u);
+                        ++n;
+                    } else if (q == CB / 1024) {
+                        dma16(rm, dst, lane < MB / 16 ? (uint32_t)lane * 16u : 0xFFFFFFF0u, (uint32_t)x.blk[j] * MB);
+                        ++n;
+                    }
+                } else {
+                    dma16(rv, dst, woff(j), (uint32_t)x.blk[j] * WBB);
+                    ++n;
+                }
             }
         }
         if (lw == 0 && rsidx >= 0) {
@@ -232,7 +254,28 @@ __global__ __launch_bounds__((NW + NL) * 64) void k_panel_gemm(
                 const int slot = slot_of((wm * GW + t) * PB + h, map0, map1);
                 if (slot == 15) continue;
                 const unsigned char *wb = wt + slot * WBB;
-                if constexpr (SP) {
+                if constexpr (SP == kCompact24) {
+                    // compressed block: lane (n, half lh) takes the 8 kept values of columns 32 kk +
+                    // 16 lh .. + 15 of row n and their index word (as with the image below)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int n = nt * 32 + l32;
+#pragma unroll
+                        for (int kk = 0; kk < KCB / 2; ++kk) {
+                            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(wb + n * BS + (2 * kk + lh) * 16);
+                            const int idx = (int)*reinterpret_cast<const uint16_t *>(wb + CB + n * (BS / 8) + (2 * kk + lh) * 2);
+#pragma unroll
+                            for (int rt = 0; rt < RW; ++rt) {
+                                const bf16x16 bx = __builtin_shufflevector(xf[rt][2 * kk], xf[rt][2 * kk + 1], 0, 1, 2, 3,
+                                                                           4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                                acc[rt][t][nt] =
+                                    __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, bx, acc[rt][t][nt], idx, 0, 0);
+                            }
+                        }
+                    }
+                    continue;
+                }
+                if constexpr (SP == kImage24) {
                     // 2:4 image of the block: row n holds the row's kept values in 16-byte chunks
                     // 0 .. BS/16 - 1 and its 16-bit index words at the start of chunk BS/16 (the
                     // loaders stage it like a bf16 block of the same size). One sparse MFMA per
@@ -994,12 +1037,14 @@ int tiles_per_chunk(int nmtiles) {
     return std::max(1, std::min(t, nmtiles));
 }
 
-template <int BS, int G, int S, int NW, bool TRANS, bool SP = false>
-void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st) {
+template <int BS, int G, int S, int NW, bool TRANS, int SP = kDense>
+void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &d, const FwdArgs &a, hipStream_t st,
+               const uint16_t *meta) {
     constexpr int BM = NW * 32;
     const int nmtiles = (int)((a.M + BM - 1) / BM);
     const dim3 grid((unsigned)((int64_t)s.ngroups * nmtiles));
-    const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * 2);
+    const uint32_t v_bytes = (uint32_t)((size_t)p.nnzb * BS * BS * (SP == kCompact24 ? 1 : 2));
+    const uint32_t m_bytes = SP == kCompact24 ? (uint32_t)((size_t)p.nnzb * BS * BS / 8) : 0u;
     constexpr int NL = panel_loader_waves(NW);
     // three LDS stages (two sub-steps of loads in flight); two for the 2-member groups, which then
     // fit three work-groups per CU
@@ -1009,30 +1054,32 @@ void launch_pg(const bsr_pattern &p, const GroupSchedule &s, const DevSchedule &
     // gain for the 128-row tiles)
     constexpr int MS = G == 4 && NW == 8 ? 2 : 1;
     hipLaunchKernelGGL((k_panel_gemm<BS, G, S, NW, NL, NST, MS, TRANS, SP>), grid, dim3((NW + NL) * 64), 0, st, a.act, a.in_ld,
-                       (int)a.M, a.V, v_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec, s.ngroups, nmtiles,
+                       (int)a.M, a.V, v_bytes, meta, m_bytes, a.bias, a.out, a.out_ld, d.order, d.sub_ptr, d.out, d.rec,
+                       s.ngroups, nmtiles,
                        tiles_per_chunk(nmtiles));
 }
 
 // Dispatch on the block size and the variant to the instantiated kernels.
-template <bool TRANS, bool SP = false>
-int32_t launch_pg_variant(const bsr_pattern &p, int k, const FwdArgs &a, hipStream_t st) {
+template <bool TRANS, int SP = kDense>
+int32_t launch_pg_variant(const bsr_pattern &p, int k, const FwdArgs &a, hipStream_t st, const uint16_t *meta = nullptr) {
     const GroupSchedule &s = (TRANS ? p.bwd : p.fwd)[k];
     const DevSchedule &d = (TRANS ? p.dev.bwd : p.dev.fwd)[k];
     if (p.b == 32) {
-        if (k == 0) launch_pg<32, 4, 8, 8, TRANS, SP>(p, s, d, a, st);
-        else if (k == 1) launch_pg<32, 4, 4, 4, TRANS, SP>(p, s, d, a, st);
-        else if (k == 2) launch_pg<32, 2, 4, 4, TRANS, SP>(p, s, d, a, st);
-        else launch_pg<32, 1, 2, 4, TRANS, SP>(p, s, d, a, st);
+        if (k == 0) launch_pg<32, 4, 8, 8, TRANS, SP>(p, s, d, a, st, meta);
+        else if (k == 1) launch_pg<32, 4, 4, 4, TRANS, SP>(p, s, d, a, st, meta);
+        else if (k == 2) launch_pg<32, 2, 4, 4, TRANS, SP>(p, s, d, a, st, meta);
+        else launch_pg<32, 1, 2, 4, TRANS, SP>(p, s, d, a, st, meta);
     } else {
-        if (k == 0) launch_pg<64, 1, 1, 8, TRANS, SP>(p, s, d, a, st);
-        else launch_pg<64, 1, 1, 4, TRANS, SP>(p, s, d, a, st);
+        if (k == 0) launch_pg<64, 1, 1, 8, TRANS, SP>(p, s, d, a, st, meta);
+        else launch_pg<64, 1, 1, 4, TRANS, SP>(p, s, d, a, st, meta);
     }
     return BSR_OK;
 }
 
 }  // namespace
 
-int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream, bool sparse24) {
+int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a, void *stream, bool sparse24,
+                          const uint16_t *meta24) {
     if (!sparse24 && use_wide(p, transposed, a.M)) return launch_wide_gemm(p, transposed, a, stream);
     const hipStream_t st = (hipStream_t)stream;
     const int k = choose_variant(p, transposed, a.M);
@@ -1045,9 +1092,10 @@ int32_t launch_group_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &
         return fail(BSR_ERR_INVALID_ARG, "block values above 4 GiB");
     if ((int64_t)rows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
-    const int32_t rc = transposed ? launch_pg_variant<true>(p, k, a, st)
-                       : sparse24 ? launch_pg_variant<false, true>(p, k, a, st)
-                                  : launch_pg_variant<false>(p, k, a, st);
+    const int32_t rc = transposed            ? launch_pg_variant<true>(p, k, a, st)
+                       : sparse24 && meta24 ? launch_pg_variant<false, kCompact24>(p, k, a, st, meta24)
+                       : sparse24           ? launch_pg_variant<false, kImage24>(p, k, a, st)
+                                            : launch_pg_variant<false>(p, k, a, st);
     if (rc != BSR_OK) return rc;
     return launched(transposed ? "bwd_input launch" : "fwd launch");
 }
@@ -1162,7 +1210,7 @@ size_t dw_workspace_bytes(const bsr_pattern &p, int64_t M) { return M > 0 ? plan
 
 std::string kernels_of(const bsr_pattern &p, int op, int64_t M, int64_t small_max) {
     if (M <= 0) return op == 2 ? "k_fill_zero" : "";
-    if (op == 3) return use_wide(p, false, M) ? "k_wide_gemm_24" : "k_fwd_24";
+    if (op == 3) return use_wide(p, false, M) ? "k_wide_gemm_24" : M > small_max ? "k_panel_gemm" : "k_fwd_24";
     if (p.device_built) small_max = std::min<int64_t>(small_max, kSmallM);
     if (op == 0 && M <= small_max) {
         int cfg = -1;

@@ -211,6 +211,7 @@ def test_op_kernels_names_the_dispatch():
     p2 = Pattern.from_mask(synth.block_mask(w2, 0), w2.N, w2.K, w2.b, upload=False)
     assert binding.op_kernels(p2, "fwd", w2.M)[0] in ("k_panel_gemm", "k_wide_gemm")
     assert binding.op_kernels(p2, "dw", w2.M) == ["k_dw_panel", "k_dw_reduce"]
+    assert binding.op_kernels(p2, "fwd_24", w2.M) == ["k_panel_gemm"]
     L = _lib.load()
     buf = ctypes.create_string_buffer(4)
     assert L.bsr_op_kernels(p.handle, 0, w.M, buf, 4) == 1   # too small

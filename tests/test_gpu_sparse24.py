@@ -398,3 +398,63 @@ def test_fwd_24_wide_zipf_workload():
     say(f"    2:4 wide fwd ({rows.size} rows): max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
     assert res["violations"] == 0, res
     p.close()
+
+
+# ---- the panel GEMM staging the compressed blocks (many rows, other patterns) ----
+
+@pytest.mark.parametrize("variant", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("M,N,K,b,d,seed", [(300, 512, 480, 32, 0.4, 80), (300, 512, 448, 64, 0.4, 81),
+                                            (260, 768, 256, 32, 0.8, 82), (513, 1024, 512, 32, 0.15, 83),
+                                            (129, 640, 384, 64, 0.3, 84)])
+def test_fwd_24_compact_panel_every_variant(monkeypatch, variant, M, N, K, b, d, seed):
+    """bsr_linear_fwd_24 above the few-row sizes on patterns the wide tile does not take: every
+    panel-GEMM variant staging the compressed blocks, bit for bit against the image forward of the
+    same variant and within the tolerance of the oracle; ragged row tails, half panels, bias."""
+    monkeypatch.setenv("BSR_GEMM_VARIANT", variant)
+    mask = synth.uniform_mask(N // b, K // b, d, synth.rng(seed, synth.STREAM_PATTERN))
+    md = meta.scan(mask)
+    p = Pattern.from_mask(mask, N, K, b)
+    assert binding.op_kernels(p, "fwd_24", M) == ["k_panel_gemm"]
+    say(f"case 2:4 compact panel fwd variant={variant} M={M} N={N} K={K} b={b} d={d}")
+    V = _values(p.nnzb, b, seed)
+    X = synth.activations(M, K, seed).to(dev())
+    bb = synth.bias_vector(N, seed).to(dev())
+    Vc, mt = binding.values_compress_24(p, V.to(dev()))
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev())
+    binding.linear_fwd_24(p, X, Vc, mt, bb, out=Y)
+    Yi = binding.linear_fwd_24_image(p, X, binding.values_pack_24(p, Vc, mt), bb)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
+    D = oracle.decompress_24(*oracle.compress_24(V))
+    ref, S = oracle.fwd(X.cpu(), md["row_ptr"], md["col_idx"], D, N, b, bias=bb.cpu())
+    res = oracle.tolerance_check(Y.cpu(), ref, S)
+    say(f"    2:4 compact panel fwd: max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_fwd_24_compact_panel_workloads(k):
+    """The BERT-base FFN-up and square layers with their blocks pruned to 2:4 through
+    bsr_linear_fwd_24: bit for bit against the image forward, sampled rows against the oracle."""
+    w = synth.WORKLOADS[k]
+    say(f"case 2:4 compact fwd {w.name}")
+    host = synth.make_inputs(w, 0, with_dy=False)
+    md = meta.scan(host["mask"])
+    p = Pattern.from_mask(host["mask"], w.N, w.K, w.b)
+    assert binding.op_kernels(p, "fwd_24", w.M) == ["k_panel_gemm"]
+    Xd = host["X"].to(dev())
+    Vc, mt = binding.values_compress_24(p, host["V"].to(dev()))
+    Y = binding.linear_fwd_24(p, Xd, Vc, mt)
+    Yi = binding.linear_fwd_24_image(p, Xd, binding.values_pack_24(p, Vc, mt))
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Yi.view(torch.int16))
+    g = np.random.default_rng([0, 85])
+    rows = np.unique(np.concatenate([[0, w.M - 1], g.choice(w.M, size=48, replace=False)]))
+    rows_t = torch.from_numpy(rows)
+    D = oracle.decompress_24(*oracle.compress_24(host["V"]))
+    ref, S = oracle.fwd(host["X"][rows_t], md["row_ptr"], md["col_idx"], D, w.N, w.b)
+    res = oracle.tolerance_check(Y.cpu()[rows_t], ref, S)
+    say(f"    2:4 compact fwd ({rows.size} rows): max |g-ref|/S = {res['max_ratio']:.3e}, violations {res['violations']}")
+    assert res["violations"] == 0, res
+    p.close()
