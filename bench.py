@@ -72,12 +72,14 @@ def op_of_kernel(name: str):
         return None
     if "k_panel_gemm" in name:
         # template arguments <BS, G, S, NW, NL, NST, MS, TRANS, SP>: TRANS marks the input gradient,
-        # SP the 2:4 forward (not part of the step)
+        # SP other than 0 the 2:4 forward (not part of the step)
         m = re.search(r"k_panel_gemm<([^>]*)>", name)
         args = [a.strip() for a in m.group(1).split(",")] if m else []
-        if len(args) >= 9 and args[8] == "true":
+        if len(args) >= 9 and args[8] not in ("0", "false"):
             return None
         return "dx" if len(args) >= 8 and args[7] == "true" else "fwd"
+    if "k_wide_gemm_24" in name:
+        return None   # the 2:4 forward, not part of the step
     if "k_wide_gemm" in name:
         # template argument <TRANS>: the input gradient when true
         return "dx" if "k_wide_gemm<true>" in name else "fwd"
@@ -766,10 +768,11 @@ SPARSE24_LARGE_WORKLOAD = 5   # the matrix-core-bound Zipf layer
 
 
 def sparse24_large_leg(dev, reps: int) -> dict:
-    """The large-M forward with 2:4 block images on the sparse matrix cores (bsr_linear_fwd_24_image)
-    beside the bf16 forward on the same pattern (the Zipf workload, its blocks pruned to 2:4; one
-    buffer set, which already touches ~0.5 GB per launch). Useful FLOPs of the 2:4 forward count the
-    kept half of every block."""
+    """The large-M forward with 2:4 blocks on the sparse matrix cores, from the compressed form
+    (bsr_linear_fwd_24: the wide tile staging 1 KB of kept values and 128 B of index words per block)
+    and from block images (bsr_linear_fwd_24_image), beside the bf16 forward on the same pattern (the
+    Zipf workload, its blocks pruned to 2:4; one buffer set, which already touches ~0.5 GB per
+    launch). Useful FLOPs of the 2:4 forward count the kept half of every block."""
     import torch
     from sparse_gemm_amd import binding, synth
     w = synth.WORKLOADS[SPARSE24_LARGE_WORKLOAD]
@@ -780,11 +783,14 @@ def sparse24_large_leg(dev, reps: int) -> dict:
     Vc, mt = binding.values_compress_24(p, V)
     img = binding.values_pack_24(p, Vc, mt)
     ms16 = time_launches(lambda k: binding.linear_fwd(p, X, V, out=Y), 1, reps)
+    msc = time_launches(lambda k: binding.linear_fwd_24(p, X, Vc, mt, out=Y), 1, reps)
     ms24 = time_launches(lambda k: binding.linear_fwd_24_image(p, X, img, out=Y), 1, reps)
     F = 2.0 * w.M * w.b * w.b * p.nnzb
-    out = {"workload": w.name + " (blocks pruned to 2:4)", "fwd_24_image_us": ms24 * 1e3, "fwd_bf16_us": ms16 * 1e3,
-           "tflops_on_kept_values": F / 2 / (ms24 * 1e-3) / 1e12,
-           "bf16_tflops": F / (ms16 * 1e-3) / 1e12, "speedup_vs_bf16": ms16 / ms24}
+    out = {"workload": w.name + " (blocks pruned to 2:4)", "kernel": binding.op_kernels(p, "fwd_24", w.M),
+           "fwd_24_us": msc * 1e3, "fwd_24_image_us": ms24 * 1e3, "fwd_bf16_us": ms16 * 1e3,
+           "tflops_on_kept_values": F / 2 / (msc * 1e-3) / 1e12,
+           "bf16_tflops": F / (ms16 * 1e-3) / 1e12, "speedup_vs_bf16": ms16 / msc,
+           "image_speedup_vs_bf16": ms16 / ms24}
     del X, V, Y, Vc, mt, img
     p.close()
     return out

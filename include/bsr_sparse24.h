@@ -50,8 +50,9 @@ int32_t bsr_values_decompress_24(const bsr_pattern *p, const bsr_bf16 *Vc, const
  * takes its wide tile) runs that tile on the compressed blocks as they are (1 KB of kept values
  * plus 128 bytes of indices per block, one v_smfmac_f32_32x32x32_bf16 per block and 32 rows; the
  * same accumulation order as bsr_linear_fwd_24_image, so the same result bit for bit). Every other
- * call runs the kernel for few rows (16 rows per pass; M below 2^20 there). Every element of Y is
- * written. Limits: the compressed values below 4 GiB; Y must not overlap the inputs. */
+ * call runs the kernel for few rows (16 rows per pass). Every element of Y is written. Limits: M
+ * below 2^20 (BSR_ERR_INVALID_ARG otherwise), the compressed values below 4 GiB; Y must not overlap
+ * the inputs. */
 int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, const bsr_bf16 *Vc,
                           const uint16_t *meta, const bsr_bf16 *bias, bsr_bf16 *Y, void *stream);
 

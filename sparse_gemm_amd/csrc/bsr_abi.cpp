@@ -471,6 +471,7 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
     BSR_CHECK(check_ptr(meta, "meta", p->nnzb == 0));
     BSR_CHECK(check_ptr(bias, "bias", true));
     BSR_CHECK(check_ptr(Y, "Y", M == 0));
+    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
     if ((size_t)p->nnzb * p->b * p->b >= (size_t)0xFFFFFFF0u)
         return fail(BSR_ERR_INVALID_ARG, "compressed block values above 4 GiB");
     if (M == 0) return BSR_OK;
@@ -484,7 +485,6 @@ int32_t bsr_linear_fwd_24(const bsr_pattern *p, const bsr_bf16 *X, int64_t M, co
         const FwdArgs a{X, M, p->K, Vc, bias, Y, p->N};
         return launch_group_gemm(*p, false, a, stream, true, meta);
     }
-    if (M >= (int64_t)1 << 20) return fail(BSR_ERR_INVALID_ARG, "the 2:4 forward takes M below 2^20");
     if ((int64_t)16 * p->K * 2 > (int64_t)UINT32_MAX) return fail(BSR_ERR_INVALID_ARG, "rows of X too long");
     return launch_fwd_24(*p, X, M, Vc, meta, bias, Y, stream);
     BSR_TRY_END

@@ -15,6 +15,13 @@ def test_op_of_kernel():
     assert bench.op_of_kernel(pg.format(g=2, s=4, t="false", sp="false")) == "fwd"
     assert bench.op_of_kernel(pg.format(g=1, s=2, t="true", sp="false")) == "dx"
     assert bench.op_of_kernel(pg.format(g=2, s=4, t="false", sp="true")) is None   # 2:4 forward
+    assert bench.op_of_kernel(pg.format(g=2, s=4, t="false", sp=0)) == "fwd"
+    assert bench.op_of_kernel(pg.format(g=2, s=4, t="true", sp=0)) == "dx"
+    assert bench.op_of_kernel(pg.format(g=2, s=4, t="false", sp=1)) is None        # 2:4 images
+    assert bench.op_of_kernel(pg.format(g=2, s=4, t="false", sp=2)) is None        # compressed 2:4
+    assert bench.op_of_kernel(PREFIX + "k_wide_gemm<false>(bsr::WideArgs)") == "fwd"
+    assert bench.op_of_kernel(PREFIX + "k_wide_gemm<true>(bsr::WideArgs)") == "dx"
+    assert bench.op_of_kernel(PREFIX + "k_wide_gemm_24(bsr::WideArgs24)") is None
     assert bench.op_of_kernel(PREFIX + "k_small_m<64, 8, 1, 2, true, false, true>(unsigned short const*)") == "fwd"
     assert bench.op_of_kernel(PREFIX + "k_dw_panel<32, 2>(unsigned short const*)") == "dw"
     assert bench.op_of_kernel(PREFIX + "k_dw_reduce(float const*, int, unsigned long, unsigned short*)") == "dw"
