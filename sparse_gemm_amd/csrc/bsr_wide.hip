@@ -3,19 +3,21 @@
 //
 // Every kept block is a dense contraction on the matrix cores, zero blocks are skipped
 // (pytorch_block_sparse summary page, "Technical Foundation"). What changes against the panel GEMM
-// of bsr_kernels.hip is the register tile. A work-group is 4 waves, one per SIMD, and owns 256
-// activation rows x kWideG = 8 output blocks (256 output columns). Wave w owns rows
-// [128 (w & 1), +128) (4 row tiles of 32) and members [4 (w >> 1), +4): a 4 x 4 grid of 32 x 32 fp32
-// accumulators (256 accumulation registers). Per 16-deep chunk of a panel the wave reads 4
-// activation fragments and up to 4 value fragments (1 KB each) from LDS for up to 16 products,
-// 0.5 KB of LDS reads per product instead of 1 KB with the panel GEMM's 2 x 2 grids, whose
-// compute phase the LDS read rate bounds.
+// of bsr_kernels.hip is the register tile. A work-group owns 256 activation rows x kWideG = 8 output
+// blocks (256 output columns) and runs 8 waves, two per SIMD: wave w owns rows [128 (w & 1), +128)
+// (4 row tiles of 32) and members 2 (w >> 1), 2 (w >> 1) + 1, a 4 x 2 grid of 32 x 32 fp32
+// accumulators (128 registers). While one wave of a SIMD waits (on the issue of a direct-to-LDS load,
+// an LDS read or the barrier) the other issues matrix products. Per 16-deep chunk of a panel a wave
+// reads 4 activation fragments and up to 2 value fragments (1 KB each) from LDS for up to 8
+// products, 0.75 KB of LDS reads per product (the panel GEMM's 2 x 2 grids: 1 KB). Measured against
+// one wave per SIMD with 4 x 4 grids (Zipf 16384 x 4096 -> 11008, warm): forward 534 -> 479 us,
+// input gradient 551 -> 498; at density 1.0 1.27 PFLOP/s against 1.16.
 //
 // Sub-step = one panel of 64 input columns: the activation panel (256 rows x 128 bytes, whole cache
 // lines) and the kept value blocks of its 16 units (unit u = member u / 2, block u % 2 of the panel;
 // 2 KB each, staged at slot u) go to LDS by direct-to-LDS loads that every wave issues for its
 // share. The 160 KB of LDS hold 3 activation stages and 2 value stages: during sub-step s the
-// activation panel of s + 2 is loaded (issued during the first three 16-deep chunks of s) and the
+// activation panel of s + 2 is loaded (issued during the first two 16-deep chunks of s) and the
 // value blocks of s + 2 (during the last chunk, once the barrier has freed their stage). At the
 // end of s every wave waits for its loads of s + 1 and a barrier publishes them.
 // Groups whose every sub-step keeps all 16 units (e.g. block rows kept in full) run a body
@@ -49,11 +51,6 @@ constexpr int kOutPitch = kWideG * 32 * 2 + 16;        // staged output row (byt
 constexpr int kSmem = kWideRows * kOutPitch > kStagesBytes ? kWideRows * kOutPitch : kStagesBytes;
 static_assert(kSmem <= 160 * 1024, "LDS of one work-group");
 
-struct WideRec {
-    int panel, mask, blk[4];   // blk: this wave's units wave + 4 j
-    int segA, segB;            // byte offsets in an activation row of the panel's two input blocks
-};
-
 struct WideArgs {
     const uint16_t *act;
     int in_ld, M;
@@ -67,11 +64,11 @@ struct WideArgs {
 // One work-group's tile: group g, activation tile mt0. DENSE: every sub-step keeps all 16 units.
 template <bool TRANS, bool DENSE>
 __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__restrict__ sub_ptr,
-                                          const int32_t *__restrict__ gout, const int32_t *__restrict__ rec, int g,
-                                          int mt0, unsigned char *smem) {
+                                           const int32_t *__restrict__ gout, const int32_t *__restrict__ rec, int g,
+                                           int mt0, unsigned char *smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wr = wave & 1, wm = wave >> 1;
+    const int wr = wave & 1, wm = wave >> 1;   // rows 128 wr .., members 2 wm, 2 wm + 1
     const int l32 = lane & 31, lh = lane >> 5;
 
     const int rows = min(kWideRows, a.M - mt0 * kWideRows);
@@ -82,47 +79,47 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
     // Sub-step records come through scalar loads whose index is clamped into the group (no
     // select on the loaded values): a record is loaded three sub-steps ahead and first read at the
     // end of the sub-step that loaded it, when the wait for it costs nothing.
+    struct Rec {
+        int mask, blk[4];   // blk: value block of unit (wave + 8 j) / 2 (-1 = none)
+        int segA, segB;     // byte offsets in an activation row of the panel's two input blocks
+    };
     auto load_rec = [&](int s) __attribute__((always_inline)) {
         const int32_t *e = rec + (size_t)s * kWideRecInts;
-        WideRec x;
-        x.panel = __builtin_amdgcn_readfirstlane(e[0]);
+        Rec x;
         x.mask = DENSE ? (1 << kWideU) - 1 : __builtin_amdgcn_readfirstlane(e[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + wave + 4 * j]);
+        for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + ((wave + 8 * j) >> 1)]);
         x.segA = __builtin_amdgcn_readfirstlane(e[18]) * 64;
         x.segB = __builtin_amdgcn_readfirstlane(e[19]) * 64;
         return x;
     };
-    // activation load i = wave + 4 j (j < 8) of the panel into activation stage xs: rows 8 i .. 8 i
+    // activation load i = wave + 8 j (j < 4) of the panel into activation stage xs: rows 8 i .. 8 i
     // + 7 (lane -> row 8 i + lane / 8, LDS chunk lane % 8 holding source chunk q = (lane % 8) ^
     // swz8(row): 16 bytes q % 4 of input block segA (q < 4) or segB). Rows past M read as zeros
     // through the range-checked voffset; a last half panel's missing block is never used.
-    auto issue_x = [&](int xs, const WideRec &x, int j) __attribute__((always_inline)) {
-        const int i = wave + 4 * j;
+    auto issue_x = [&](int xs, const Rec &x, int j) __attribute__((always_inline)) {
+        const int i = wave + 8 * j;
         const int r = i * 8 + (lane >> 3);
         const int q = (lane & 7) ^ swz8(r);
         dma16(ra, sbase + (uint32_t)xs * kXB + (uint32_t)i * 1024u,
               (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)(q < 4 ? x.segA : x.segB) + (uint32_t)((q & 3) << 4), 0);
     };
-    // value block of unit u = wave + 4 t (if kept) into value stage vs: two 1 KB halves (lane ->
-    // block row 16 q + lane / 4, chunk (lane % 4) ^ swz4(row))
-    auto issue_v = [&](int vs, const WideRec &x, int t) __attribute__((always_inline)) {
-        const int u = wave + 4 * t;
+    // value load k = wave + 8 j (j < 4): half q = k % 2 of the block of unit u = k / 2 (if kept) into
+    // value stage vs, 1 KB (lane -> block row 16 q + lane / 4, chunk (lane % 4) ^ swz4(row))
+    auto issue_v = [&](int vs, const Rec &x, int j) __attribute__((always_inline)) {
+        const int k = wave + 8 * j, u = k >> 1, q = k & 1;
         if (DENSE || ((x.mask >> u) & 1)) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int n = 16 * q + (lane >> 2);
-                dma16(rv, sbase + kXStages * kXB + (uint32_t)vs * kVB + (uint32_t)u * kWBB + (uint32_t)q * 1024u,
-                      (uint32_t)(n * 64 + (((lane & 3) ^ swz4(n)) << 4)), (uint32_t)x.blk[t] * kWBB);
-            }
+            const int n = 16 * q + (lane >> 2);
+            dma16(rv, sbase + kXStages * kXB + (uint32_t)vs * kVB + (uint32_t)u * kWBB + (uint32_t)q * 1024u,
+                  (uint32_t)(n * 64 + (((lane & 3) ^ swz4(n)) << 4)), (uint32_t)x.blk[j] * kWBB);
         }
     };
 
-    f32x16 acc[4][4];   // [row tile][member of the wave]
+    f32x16 acc[4][2];   // [row tile][member of the wave]
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.f;
 
@@ -149,29 +146,27 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
         const int r = wr * 128 + rt * 32 + l32;
         return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
     };
-
     // Products of one staged sub-step, chunk by chunk (c = 16-deep chunk of the panel, block c / 2),
-    // member by member: fragment set c & 1 holds chunk c. m8 = presence of this wave's 8 units (bit
-    // 2 t + h: member 4 wm + t, block h of the panel). Absent units' products are skipped, never run
+    // member by member: fragment set c & 1 holds chunk c. m4 = presence of this wave's 4 units (bit
+    // 2 t + h: member 2 wm + t, block h of the panel). Absent units' products are skipped, never run
     // on zero blocks (zero times a non-finite activation is not zero). Fragments are read one chunk
     // ahead into the other register set (for every unit, present or not: a read of an unused slot
     // is harmless), so the LDS latency hides behind the matrix cores.
-    bf16x8 xf[2][4], wf[2][4];
+    bf16x8 xf[2][4], wf[2][2];
     auto read_frags = [&](int set, int xs, int vs, int c) __attribute__((always_inline)) {
         const unsigned char *xt = smem + xs * kXB;
-        const unsigned char *wt = smem + kXStages * kXB + vs * kVB + wm * 8 * kWBB;
+        const unsigned char *wt = smem + kXStages * kXB + vs * kVB + wm * 4 * kWBB;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) xf[set][rt] = xfrag(xt, rt, c);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) wf[set][t] = wfrag(wt + (2 * t + (c >> 1)) * kWBB, c & 1);
+        for (int t = 0; t < 2; ++t) wf[set][t] = wfrag(wt + (2 * t + (c >> 1)) * kWBB, c & 1);
     };
-    // the products of chunk c; after(t) runs after those of member t (scheduling barriers keep it
-    // there, so load issues go out between products)
-    auto products = [&](int c, int m8, auto &&after) __attribute__((always_inline)) {
+    // the products of chunk c (presence bit 2 t + c / 2 of m4); after(t) runs after member t's
+    auto products = [&](int c, int m4, auto &&after) __attribute__((always_inline)) {
         const int cur = c & 1, h = c >> 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (DENSE || ((m8 >> (2 * t + h)) & 1)) {
+        for (int t = 0; t < 2; ++t) {
+            if (DENSE || ((m4 >> (2 * t + h)) & 1)) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) acc[rt][t] = mfma32(wf[cur][t], xf[cur][rt], acc[rt][t]);
             }
@@ -183,43 +178,41 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
 
     // Sub-step pipeline. Before sub-step s: activation stages hold s, s + 1 (landed or in flight),
     // value stages s, s + 1; fragment set 0 holds chunk 0 of s. Sub-step s: chunks 0 .. 2 (each
-    // reading the next chunk's fragments), with the activation panel of s + 2 issued between their
-    // products into the third activation stage (free since the last barrier); then every wave waits
-    // for its LDS reads of s (all in registers now) and for its loads of s + 1, and a barrier
-    // publishes s + 1 and frees the stages of s; then the value blocks of s + 2 are issued into
-    // their stage between the products of chunk 3, after the reads of chunk 0 of s + 1. The issue
-    // of a direct-to-LDS load holds the wave while the compute unit's load path is busy, so the
-    // loads go out one or two at a time between groups of 4 products. The barrier never waits on an
-    // LDS read, the next sub-step starts with its first fragments in registers, and loads have about
-    // one sub-step to land.
+    // reading the next chunk's fragments), with the activation panel of s + 2 issued between the
+    // products of chunks 0 and 1 into the third activation stage (free since the last barrier);
+    // then every wave waits for its LDS reads of s (all in registers now) and for its loads of
+    // s + 1, and a barrier publishes s + 1 and frees the stages of s; then the value blocks of s + 2
+    // are issued into their stage between the products of chunk 3, after the reads of chunk 0 of
+    // s + 1. The barrier never waits on an LDS read, the next sub-step starts with its first
+    // fragments in registers, and loads have about one sub-step to land.
     const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
     if (s0 < s1) {
-        WideRec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
-        WideRec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
+        Rec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
+        Rec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) issue_x(0, r0, j);
+        for (int j = 0; j < 4; ++j) issue_x(0, r0, j);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) issue_v(0, r0, t);
+        for (int j = 0; j < 4; ++j) issue_v(0, r0, j);
         if (s0 + 1 < s1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) issue_x(1, r1, j);
+            for (int j = 0; j < 4; ++j) issue_x(1, r1, j);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) issue_v(1, r1, t);
+            for (int j = 0; j < 4; ++j) issue_v(1, r1, j);
         }
         wait_vm<0, 0>(0);
         __syncthreads();
         read_frags(0, 0, 0, 0);
         int xs = 0, vs = 0;
         for (int s = s0; s < s1; ++s) {
-            const int m8 = (r0.mask >> (8 * wm)) & 0xFF;
+            const int m4 = (r0.mask >> (4 * wm)) & 0xF;
             const bool more2 = s + 2 < s1;
             const int x2 = xs == 0 ? 2 : xs - 1;   // activation stage of s + 2 (that of s - 1)
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
                 read_frags((c + 1) & 1, xs, vs, c + 1);
-                // the 8 activation loads of s + 2 over the first 3 product groups of chunks 0 .. 2
-                products(c, m8, [&](int t) __attribute__((always_inline)) {
-                    if (more2 && t < 3 && 3 * c + t < 8) issue_x(x2, r2, 3 * c + t);
+                // the 4 activation loads of s + 2 after the member groups of chunks 0 and 1
+                products(c, m4, [&](int t) __attribute__((always_inline)) {
+                    if (more2 && c < 2) issue_x(x2, r2, 2 * c + t);
                 });
             }
             // every LDS read of sub-step s has landed in registers (chunk 3's included)
@@ -227,17 +220,19 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
             // the record of s + 4 is loaded now, with no LDS read outstanding: scalar loads share
             // the LDS wait counter and return out of order, so one in flight would turn the partial
             // LDS waits into full ones
-            const WideRec r4 = load_rec(min(s + 4, s1 - 1));
-            // this wave's loads of s + 1 have landed; the activation loads of s + 2, issued after
-            // them during chunks 0 .. 2, may still be in flight
-            if (more2) wait_vm<8, 8>(8);
+            const Rec r4 = load_rec(min(s + 4, s1 - 1));
+            // this wave's loads of s + 1 have landed; its 4 activation loads of s + 2 may not have
+            if (more2) wait_vm<4, 4>(4);
             else wait_vm<0, 0>(0);
-            __syncthreads();   // everyone's have; nobody reads the stages of s any more
+            __syncthreads();
             const int xn = xs == 2 ? 0 : xs + 1, vn = vs ^ 1;
-            read_frags(0, xn, vn, 0);   // chunk 0 of s + 1 (harmless past the last sub-step)
-            // value loads of s + 2: 2 per product group
-            products(3, m8, [&](int t) __attribute__((always_inline)) {
-                if (more2) issue_v(vs, r2, t);
+            read_frags(0, xn, vn, 0);
+            // the 4 value loads of s + 2, 2 per member group
+            products(3, m4, [&](int t) __attribute__((always_inline)) {
+                if (more2) {
+                    issue_v(vs, r2, 2 * t);
+                    issue_v(vs, r2, 2 * t + 1);
+                }
             });
             r0 = r1;
             r1 = r2;
@@ -250,11 +245,11 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
     __syncthreads();   // the stages are free for the output tile
 
     // Epilogue through LDS: item v of lane l of acc[rt][t] is output column 8 (v / 4) + 4 (l / 32) +
-    // v % 4 of member 4 wm + t, activation row 128 wr + 32 rt + l % 32. Bias in fp32, one bf16
-    // rounding; then every wave stores 64 staged rows as 16-byte pieces of whole 64-byte block rows.
+    // v % 4 of member 2 wm + t, activation row 128 wr + 32 rt + l % 32. Bias in fp32, one bf16
+    // rounding; then every wave stores 32 staged rows as 16-byte pieces of whole 64-byte block rows.
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int tg = wm * 4 + t;
+    for (int t = 0; t < 2; ++t) {
+        const int tg = wm * 2 + t;
         const int o = gout[g * kWideG + tg];
         if (o < 0) continue;
 #pragma unroll
@@ -267,31 +262,28 @@ __device__ __forceinline__ void wide_tile(const WideArgs &a, const int32_t *__re
                 if (a.bias) v = add_bias4(v, a.bias + o * 32 + q * 8 + lh * 4);
                 store4_bf16(reinterpret_cast<uint16_t *>(smem + row * kOutPitch + c * 2), v[0], v[1], v[2], v[3]);
             }
-            // one accumulator tile at a time: keeps the reads of the accumulation registers from
-            // being hoisted all at once (which spills)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
-    const int m0 = mt0 * kWideRows + wave * 64;
+    const int m0 = mt0 * kWideRows + wave * 32;
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
         const int seg = i * 64 + lane, row = seg >> 5, cs = seg & 31;   // 32 pieces per row
         const int t = cs >> 2, within = (cs & 3) * 8;
         const int o = gout[g * kWideG + t];
         if (o < 0 || m0 + row >= a.M) continue;
-        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 64 + row) * kOutPitch + cs * 16);
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 32 + row) * kOutPitch + cs * 16);
         __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(a.out + (int64_t)(m0 + row) * a.out_ld + o * 32 + within));
     }
 }
 
 template <bool TRANS>
-__global__ __launch_bounds__(256, 1) void k_wide_gemm(WideArgs a, const int32_t *__restrict__ order,
-                                                      const int32_t *__restrict__ flags,
-                                                      const int32_t *__restrict__ sub_ptr,
-                                                      const int32_t *__restrict__ gout,
-                                                      const int32_t *__restrict__ rec, int ngroups, int nmtiles,
-                                                      int tpc) {
+__global__ __launch_bounds__(512, 1) void k_wide_gemm(WideArgs a, const int32_t *__restrict__ order,
+                                                  const int32_t *__restrict__ flags,
+                                                  const int32_t *__restrict__ sub_ptr,
+                                                  const int32_t *__restrict__ gout,
+                                                  const int32_t *__restrict__ rec, int ngroups, int nmtiles, int tpc) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
     // Work-group -> (group, activation tile), as in the panel GEMM: each XCD takes a contiguous run
     // of chunks of tpc activation tiles x all groups (heaviest groups first), so the work-groups
@@ -306,21 +298,22 @@ __global__ __launch_bounds__(256, 1) void k_wide_gemm(WideArgs a, const int32_t 
 }
 
 // ------------------------------------------------------------------------------------------
-// 2:4 wide-tile forward (b = 32): the wide GEMM's tile, schedule and pipeline with every kept block
-// in the compressed 2:4 form (torchao sparsity README, Table 4.1: half the values plus 2-bit
+// 2:4 wide-tile forward (b = 32): the wide GEMM's tile, schedule, waves and pipeline with every kept
+// block in the compressed 2:4 form (torchao sparsity README, Table 4.1: half the values plus 2-bit
 // indices): Vc holds a block's 32 rows x 16 kept values (1 KB), meta its 32 rows x two 16-bit
-// index words (128 bytes). Both are staged as they are (1 KB of values per unit, identity lane map;
-// each wave's 4 units' index words by one load whose lanes 32 .. 63 read zeros), so a sub-step
-// stages 20 KB of values instead of 32. Per block and row tile one v_smfmac_f32_32x32x32_bf16: lane
+// index words (128 bytes). Both are staged as they are: 1 KB of values per unit (identity lane map)
+// and, per wave, the index words of its 2 units (u = wave + 8 t) by one load into its own 1 KB (lanes
+// 8 t .. 8 t + 7 fetch unit u's 128 bytes, the others read zeros), so a sub-step stages 24 KB of
+// values and indices instead of 32. Per block and row tile one v_smfmac_f32_32x32x32_bf16: lane
 // (row n = l % 32, half h = l / 32) takes 8 kept values of columns 16 h .. 16 h + 15 of block row n
 // and their 16 index bits; the activation operand is the two 16-deep fragments of the block's 32
-// columns, concatenated. Sub-step s: the block-0 products (with 6 activation loads of s + 2 among
-// them), the wait and the barrier, then the block-1 products (with the other 2 and the value loads
-// of s + 2): 6 and 7 loads per half, as the compute unit's load path takes them.
+// columns, read as one 16-element vector. Sub-step s: the block-0 products with the 4 activation
+// loads of s + 2 among them, the wait and the barrier, then the block-1 products with the value and
+// index loads of s + 2.
 // ------------------------------------------------------------------------------------------
-constexpr int kVB24 = kWideU * 1024 + 4 * 1024;                   // staged values + index words
+constexpr int kVB24 = kWideU * 1024 + 8 * 1024;                   // staged values + index words
 constexpr uint32_t kPastEnd24 = 0xFFFFFFF0u;   // past both compressed arrays: such a load reads zeros
-constexpr int kStages24 = kXStages * kXB + kVStages * kVB24;      // 136 KB
+constexpr int kStages24 = kXStages * kXB + kVStages * kVB24;      // 144 KB
 constexpr int kSmem24 = kWideRows * kOutPitch > kStages24 ? kWideRows * kOutPitch : kStages24;
 static_assert(kSmem24 <= 160 * 1024, "LDS of one work-group");
 
@@ -342,7 +335,7 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
                                              int mt0, unsigned char *smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wr = wave & 1, wm = wave >> 1;
+    const int wr = wave & 1, wm = wave >> 1;   // rows 128 wr .., members 2 wm, 2 wm + 1
     const int l32 = lane & 31, lh = lane >> 5;
 
     const int rows = min(kWideRows, a.M - mt0 * kWideRows);
@@ -352,45 +345,48 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
     const uint32_t sbase = lds_addr(smem);
     const uint32_t vbase = sbase + kXStages * kXB;
 
+    struct Rec {
+        int mask, blk[2];   // blk: value block of unit wave + 8 t (-1 = none)
+        int segA, segB;
+    };
     auto load_rec = [&](int s) __attribute__((always_inline)) {
         const int32_t *e = rec + (size_t)s * kWideRecInts;
-        WideRec x;
-        x.panel = __builtin_amdgcn_readfirstlane(e[0]);
+        Rec x;
         x.mask = DENSE ? (1 << kWideU) - 1 : __builtin_amdgcn_readfirstlane(e[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x.blk[j] = __builtin_amdgcn_readfirstlane(e[2 + wave + 4 * j]);
+        for (int t = 0; t < 2; ++t) x.blk[t] = __builtin_amdgcn_readfirstlane(e[2 + wave + 8 * t]);
         x.segA = __builtin_amdgcn_readfirstlane(e[18]) * 64;
         x.segB = __builtin_amdgcn_readfirstlane(e[19]) * 64;
         return x;
     };
-    // activation load i = wave + 4 j (j < 8): as the wide GEMM
-    auto issue_x = [&](int xs, const WideRec &x, int j) __attribute__((always_inline)) {
-        const int i = wave + 4 * j;
+    // activation load i = wave + 8 j (j < 4): as the wide GEMM
+    auto issue_x = [&](int xs, const Rec &x, int j) __attribute__((always_inline)) {
+        const int i = wave + 8 * j;
         const int r = i * 8 + (lane >> 3);
         const int q = (lane & 7) ^ swz8(r);
         dma16(ra, sbase + (uint32_t)xs * kXB + (uint32_t)i * 1024u,
               (uint32_t)r * (uint32_t)a.in_ld * 2u + (uint32_t)(q < 4 ? x.segA : x.segB) + (uint32_t)((q & 3) << 4), 0);
     };
-    // kept values of unit u = wave + 4 t (if kept): 1 KB to unit slot u
-    auto issue_v = [&](int vs, const WideRec &x, int t) __attribute__((always_inline)) {
-        const int u = wave + 4 * t;
+    // kept values of unit u = wave + 8 t (if kept): 1 KB to unit slot u
+    auto issue_v = [&](int vs, const Rec &x, int t) __attribute__((always_inline)) {
+        const int u = wave + 8 * t;
         if (DENSE || ((x.mask >> u) & 1))
             dma16(rv, vbase + (uint32_t)vs * kVB24 + (uint32_t)u * 1024u, (uint32_t)lane * 16u, (uint32_t)x.blk[t] * 1024u);
     };
-    // index words of this wave's units wave + 4 t: lanes 8 t .. 8 t + 7 load unit t's 128 bytes to
-    // this wave's 1 KB (t * 128 ..); lanes 32 .. 63 and absent units read zeros
-    auto issue_m = [&](int vs, const WideRec &x) __attribute__((always_inline)) {
-        const int t = (lane >> 3) & 3;
-        const int blk = t == 0 ? x.blk[0] : t == 1 ? x.blk[1] : t == 2 ? x.blk[2] : x.blk[3];
-        const uint32_t voff = lane < 32 && blk >= 0 ? (uint32_t)blk * 128u + (uint32_t)(lane & 7) * 16u : kPastEnd24;
+    // index words of this wave's units wave + 8 t: lanes 8 t .. 8 t + 7 load unit t's 128 bytes to
+    // this wave's 1 KB (t * 128 ..); the other lanes and absent units read zeros
+    auto issue_m = [&](int vs, const Rec &x) __attribute__((always_inline)) {
+        const int t = (lane >> 3) & 1;
+        const int blk = t == 0 ? x.blk[0] : x.blk[1];
+        const uint32_t voff = lane < 16 && blk >= 0 ? (uint32_t)blk * 128u + (uint32_t)(lane & 7) * 16u : kPastEnd24;
         dma16(rm, vbase + (uint32_t)vs * kVB24 + kWideU * 1024u + (uint32_t)wave * 1024u, voff, 0);
     };
 
-    f32x16 acc[4][4];   // [row tile][member of the wave]
+    f32x16 acc[4][2];   // [row tile][member of the wave]
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.f;
 
@@ -399,11 +395,12 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
         return *reinterpret_cast<const bf16x8 *>(xt + r * 128 + (((2 * c + lh) ^ swz8(r)) << 4));
     };
     // fragments of block h of the panel: the activation fragments of its chunks 2 h, 2 h + 1, and the
-    // kept values and index bits of each member t's unit 2 (4 wm + t) + h (present or not: a read of
-    // an unused slot is harmless)
+    // kept values and index bits of each member t's unit u = 2 (2 wm + t) + h (present or not: a read
+    // of an unused slot is harmless); unit u's index words sit in the region of wave u % 8, at
+    // 128 (u / 8)
     bf16x16 xf[2][4];
-    bf16x8 af[2][4];
-    int ai[2][4];
+    bf16x8 af[2][2];
+    int ai[2][2];
     auto read_frags = [&](int set, int xs, int vs, int h) __attribute__((always_inline)) {
         const unsigned char *xt = smem + xs * kXB;
         const unsigned char *vt = smem + kXStages * kXB + vs * kVB24;
@@ -413,17 +410,17 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
             xf[set][rt].hi = xfrag(xt, rt, 2 * h + 1);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int u = 2 * (4 * wm + t) + h;
+        for (int t = 0; t < 2; ++t) {
+            const int u = 2 * (2 * wm + t) + h;
             af[set][t] = *reinterpret_cast<const bf16x8 *>(vt + u * 1024 + l32 * 32 + lh * 16);
-            ai[set][t] = *reinterpret_cast<const uint16_t *>(vt + kWideU * 1024 + (u & 3) * 1024 + (u >> 2) * 128 + l32 * 4 +
+            ai[set][t] = *reinterpret_cast<const uint16_t *>(vt + kWideU * 1024 + (u & 7) * 1024 + (u >> 3) * 128 + l32 * 4 +
                                                              lh * 2);
         }
     };
-    auto products = [&](int set, int h, int m8, auto &&after) __attribute__((always_inline)) {
+    auto products = [&](int set, int h, int m4, auto &&after) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (DENSE || ((m8 >> (2 * t + h)) & 1)) {
+        for (int t = 0; t < 2; ++t) {
+            if (DENSE || ((m4 >> (2 * t + h)) & 1)) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
                     acc[rt][t] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[set][t], xf[set][rt], acc[rt][t],
@@ -437,18 +434,18 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
 
     const int s0 = sub_ptr[g], s1 = sub_ptr[g + 1];
     if (s0 < s1) {
-        WideRec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
-        WideRec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
+        Rec r0 = load_rec(s0), r1 = load_rec(min(s0 + 1, s1 - 1));
+        Rec r2 = load_rec(min(s0 + 2, s1 - 1)), r3 = load_rec(min(s0 + 3, s1 - 1));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) issue_x(0, r0, j);
+        for (int j = 0; j < 4; ++j) issue_x(0, r0, j);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) issue_v(0, r0, t);
+        for (int t = 0; t < 2; ++t) issue_v(0, r0, t);
         issue_m(0, r0);
         if (s0 + 1 < s1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) issue_x(1, r1, j);
+            for (int j = 0; j < 4; ++j) issue_x(1, r1, j);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) issue_v(1, r1, t);
+            for (int t = 0; t < 2; ++t) issue_v(1, r1, t);
             issue_m(1, r1);
         }
         wait_vm<0, 0>(0);
@@ -456,32 +453,31 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
         read_frags(0, 0, 0, 0);
         int xs = 0, vs = 0;
         for (int s = s0; s < s1; ++s) {
-            const int m8 = (r0.mask >> (8 * wm)) & 0xFF;
+            const int m4 = (r0.mask >> (4 * wm)) & 0xF;
             const bool more2 = s + 2 < s1;
             const int x2 = xs == 0 ? 2 : xs - 1;   // activation stage of s + 2 (that of s - 1)
             read_frags(1, xs, vs, 1);
-            // block 0's products with 6 of the 8 activation loads of s + 2 (2, 2, 1, 1 per member group)
-            products(0, 0, m8, [&](int t) __attribute__((always_inline)) {
+            // block 0's products with the 4 activation loads of s + 2 (2 per member group)
+            products(0, 0, m4, [&](int t) __attribute__((always_inline)) {
                 if (more2) {
-                    issue_x(x2, r2, t < 2 ? 2 * t : t + 2);
-                    if (t < 2) issue_x(x2, r2, 2 * t + 1);
+                    issue_x(x2, r2, 2 * t);
+                    issue_x(x2, r2, 2 * t + 1);
                 }
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const WideRec r4 = load_rec(min(s + 4, s1 - 1));
-            // this wave's loads of s + 1 have landed; the 6 activation loads of s + 2 may be in flight
-            if (more2) wait_vm<6, 6>(6);
+            const Rec r4 = load_rec(min(s + 4, s1 - 1));
+            // this wave's loads of s + 1 have landed; the 4 activation loads of s + 2 may be in flight
+            if (more2) wait_vm<4, 4>(4);
             else wait_vm<0, 0>(0);
             __syncthreads();
             const int xn = xs == 2 ? 0 : xs + 1, vn = vs ^ 1;
             read_frags(0, xn, vn, 0);   // block 0 of s + 1 (harmless past the last sub-step)
-            // block 1's products with the last 2 activation loads of s + 2 (its stage is that of
-            // s - 1) and the value loads of s + 2 (into the stage of s, free since the barrier)
-            products(1, 1, m8, [&](int t) __attribute__((always_inline)) {
+            // block 1's products with the value and index loads of s + 2 (into the stage of s, free
+            // since the barrier)
+            products(1, 1, m4, [&](int t) __attribute__((always_inline)) {
                 if (more2) {
-                    if (t < 2) issue_x(x2, r2, 6 + t);
                     issue_v(vs, r2, t);
-                    if (t == 3) issue_m(vs, r2);
+                    if (t == 1) issue_m(vs, r2);
                 }
             });
             r0 = r1;
@@ -495,8 +491,8 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
     __syncthreads();   // the stages are free for the output tile
 
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int tg = wm * 4 + t;
+    for (int t = 0; t < 2; ++t) {
+        const int tg = wm * 2 + t;
         const int o = gout[g * kWideG + tg];
         if (o < 0) continue;
 #pragma unroll
@@ -513,19 +509,19 @@ __device__ __forceinline__ void wide_tile_24(const WideArgs24 &a, const int32_t 
         }
     }
     __syncthreads();
-    const int m0 = mt0 * kWideRows + wave * 64;
+    const int m0 = mt0 * kWideRows + wave * 32;
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
         const int seg = i * 64 + lane, row = seg >> 5, cs = seg & 31;
         const int t = cs >> 2, within = (cs & 3) * 8;
         const int o = gout[g * kWideG + t];
         if (o < 0 || m0 + row >= a.M) continue;
-        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 64 + row) * kOutPitch + cs * 16);
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(smem + (wave * 32 + row) * kOutPitch + cs * 16);
         __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(a.out + (int64_t)(m0 + row) * a.out_ld + o * 32 + within));
     }
 }
 
-__global__ __launch_bounds__(256, 1) void k_wide_gemm_24(WideArgs24 a, const int32_t *__restrict__ order,
+__global__ __launch_bounds__(512, 1) void k_wide_gemm_24(WideArgs24 a, const int32_t *__restrict__ order,
                                                          const int32_t *__restrict__ flags,
                                                          const int32_t *__restrict__ sub_ptr,
                                                          const int32_t *__restrict__ gout,
@@ -928,7 +924,7 @@ int32_t launch_wide_gemm_24(const bsr_pattern &p, const FwdArgs &a, const uint16
     const int tpc = wide_tiles_per_chunk(nmtiles);
     const WideArgs24 wa{a.act, a.in_ld, (int)a.M, Vc, (uint32_t)((size_t)p.nnzb * 1024), meta,
                         (uint32_t)((size_t)p.nnzb * 128), a.bias, a.out, a.out_ld};
-    hipLaunchKernelGGL(k_wide_gemm_24, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr, d.out,
+    hipLaunchKernelGGL(k_wide_gemm_24, dim3((unsigned)nwg), dim3(512), 0, st, wa, d.order, d.flags, d.sub_ptr, d.out,
                        d.rec, s.ngroups, nmtiles, tpc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide 2:4 gemm launch: ") + hipGetErrorString(e));
@@ -949,10 +945,10 @@ int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a
     const int tpc = wide_tiles_per_chunk(nmtiles);
     const WideArgs wa{a.act, a.in_ld, (int)a.M, a.V, (uint32_t)((size_t)p.nnzb * 32 * 32 * 2), a.bias, a.out, a.out_ld};
     if (transposed)
-        hipLaunchKernelGGL(k_wide_gemm<true>, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr,
+        hipLaunchKernelGGL(k_wide_gemm<true>, dim3((unsigned)nwg), dim3(512), 0, st, wa, d.order, d.flags, d.sub_ptr,
                            d.out, d.rec, s.ngroups, nmtiles, tpc);
     else
-        hipLaunchKernelGGL(k_wide_gemm<false>, dim3((unsigned)nwg), dim3(256), 0, st, wa, d.order, d.flags, d.sub_ptr,
+        hipLaunchKernelGGL(k_wide_gemm<false>, dim3((unsigned)nwg), dim3(512), 0, st, wa, d.order, d.flags, d.sub_ptr,
                            d.out, d.rec, s.ngroups, nmtiles, tpc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide gemm launch: ") + hipGetErrorString(e));
