@@ -541,8 +541,8 @@ __global__ __launch_bounds__(512, 1) void k_wide_gemm_24(WideArgs24 a, const int
 // Wide weight gradient (b = 32): for the kept blocks of a tile of 4 block rows x 16 block columns
 // (any rows, any columns),
 //   dV[i][p][q] = sum_m dY[m][r*32 + p] * X[m][c*32 + q]     (the block-masked SDDMM)
-// over one chunk of activation rows. 4 waves, one per SIMD; wave w owns tile columns [4 w, 4 w + 4)
-// of all 4 rows: 4 x 4 accumulators of 32 x 32 (products D[q][p] += X^T . dY with A = X fragments
+// over one chunk of activation rows. 8 waves, two per SIMD; wave w owns tile columns 2 w, 2 w + 1
+// of all 4 rows: 4 x 2 accumulators of 32 x 32 (products D[q][p] += X^T . dY with A = X fragments
 // and B = dY fragments, so each lane ends with 4 consecutive q of one p). Every one of the 64
 // products is computed, absent blocks included, and only kept blocks are written: one code path,
 // no per-block branches around the matrix-core chain. Per 32-row step, the 4 rows' dY segments
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void k_wide_gemm_24(WideArgs24 a, const int
 // of a tile read row or column 0: they only feed products that are dropped. Fragments come from
 // transposing LDS reads; the 16-byte chunks of each staged row are XOR swizzled by 4 (row % 4),
 // which keeps the reads of 4 consecutive rows per 16 lanes on distinct banks. Per 16-deep chunk a
-// wave reads 4 + 4 fragments for 16 products.
+// wave reads 2 + 4 fragments for 8 products.
 // With one chunk of rows the sums are rounded to bf16 directly (staged through LDS, stored as
 // 16-byte pieces of whole block rows); otherwise fp32 partials go to the workspace at the blocks'
 // compact indices.
@@ -566,7 +566,9 @@ constexpr int kDwXB = kDwStep * kWdwCols * 64;     // staged X: 32 KB
 constexpr int kDwStage = kDwDYB + kDwXB;           // 40 KB
 constexpr int kDwStages = 4;
 static_assert(kDwStages * kDwStage <= 160 * 1024, "LDS of one work-group");
-constexpr int kDwLoads = (kDwDYB + kDwXB) / 1024 / 4;   // direct-to-LDS loads per wave and step (10)
+constexpr int kDwWaves8 = 8;                        // waves of a work-group, two per SIMD
+constexpr int kDwLoads = (kDwDYB + kDwXB) / 1024 / kDwWaves8;   // direct-to-LDS loads per wave and step (5)
+constexpr int kDwDYLoads = kDwDYB / 1024 / kDwWaves8;           // of which dY loads (1)
 
 struct WdwOut {
     uint16_t *dV;       // bf16 blocks (one chunk of rows)
@@ -585,24 +587,24 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
     const uint32_t sbase = lds_addr(smem);
     const int nsteps = (rows + kDwStep - 1) / kDwStep;
 
-    // Loads of step `step` into stage st, 10 per wave. dY loads d = wave, wave + 4 (1 KB each: 4
-    // activation rows x 4 block rows x 64 bytes): lane -> activation row 4 d + lane / 16, staged
-    // chunk lane % 16 of that row, which holds source chunk (lane % 16) ^ 4 (lane / 16) (block row
-    // of the tile = source chunk / 4, 16-byte piece = source chunk % 4). X loads x = wave + 4 k,
-    // k < 8 (one activation row of 1 KB each): staged chunk lane holds source chunk lane ^ 4 wave
-    // (x % 4 = wave; tile column = source chunk / 4).
+    // Loads of step `step` into stage st, 5 per wave (8 waves). dY load d = wave (1 KB: 4 activation
+    // rows x 4 block rows x 64 bytes): lane -> activation row 4 d + lane / 16, staged chunk lane % 16
+    // of that row, which holds source chunk (lane % 16) ^ 4 (lane / 16) (block row of the tile =
+    // source chunk / 4, 16-byte piece = source chunk % 4). X loads x = wave + 8 k, k < 4 (one
+    // activation row of 1 KB each): staged chunk lane holds source chunk lane ^ 4 (x % 4), x % 4 =
+    // wave % 4 (tile column = source chunk / 4).
     const int dsrc = (lane & 15) ^ ((lane >> 4) << 2);
     const uint32_t dlane = (uint32_t)(lane >> 4) * (uint32_t)N * 2u + (uint32_t)max(it[dsrc >> 2], 0) * 64u +
                            (uint32_t)(dsrc & 3) * 16u;
-    const int xsrc = lane ^ (wave << 2);
+    const int xsrc = lane ^ ((wave & 3) << 2);
     const uint32_t xlane = (uint32_t)max(it[4 + (xsrc >> 2)], 0) * 64u + (uint32_t)(xsrc & 3) * 16u;
     auto issue = [&](int st, int step, int k) __attribute__((always_inline)) {
         const uint32_t base = sbase + (uint32_t)st * kDwStage;
-        if (k < 2) {
-            const int d = wave + 4 * k;
+        if (k < kDwDYLoads) {
+            const int d = wave + kDwWaves8 * k;
             dma16(rd, base + (uint32_t)d * 1024u, dlane + (uint32_t)(step * kDwStep + 4 * d) * (uint32_t)N * 2u, 0);
         } else {
-            const int x = wave + 4 * (k - 2);
+            const int x = wave + kDwWaves8 * (k - kDwDYLoads);
             dma16(rx, base + kDwDYB + (uint32_t)x * 1024u, xlane + (uint32_t)(step * kDwStep + x) * (uint32_t)K * 2u, 0);
         }
     };
@@ -623,19 +625,21 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
         return __builtin_bit_cast(bf16x8, v);
     };
 
-    f32x16 acc[kWdwRows][4];   // [block row t][column jj of the wave]
+    // wave w holds the blocks of all 4 rows x columns 2 w, 2 w + 1 of the tile (128 registers), two
+    // waves per SIMD, so that one issues products while the other waits
+    f32x16 acc[kWdwRows][2];   // [block row t][column jj of the wave]
 #pragma unroll
     for (int t = 0; t < kWdwRows; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[t][jj][v] = 0.f;
 
-    bf16x8 fa[2][4], fb[2][4];   // [set][jj]: X fragments (A); [set][t]: dY fragments (B)
+    bf16x8 fa[2][2], fb[2][4];   // [set][jj]: X fragments (A); [set][t]: dY fragments (B)
     auto read_frags = [&](int set, int st, int kc) __attribute__((always_inline)) {
         const unsigned char *dt = smem + st * kDwStage, *xt = dt + kDwDYB;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) fa[set][jj] = frag(xt, kWdwCols * 64, kc * 16, (4 * wave + jj) * 32);
+        for (int jj = 0; jj < 2; ++jj) fa[set][jj] = frag(xt, kWdwCols * 64, kc * 16, (2 * wave + jj) * 32);
 #pragma unroll
         for (int t = 0; t < kWdwRows; ++t) fb[set][t] = frag(dt, kWdwRows * 64, kc * 16, t * 32);
     };
@@ -643,7 +647,7 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
 #pragma unroll
         for (int t = 0; t < kWdwRows; ++t) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) acc[t][jj] = mfma32(fa[set][jj], fb[set][t], acc[t][jj]);
+            for (int jj = 0; jj < 2; ++jj) acc[t][jj] = mfma32(fa[set][jj], fb[set][t], acc[t][jj]);
             __builtin_amdgcn_sched_barrier(0);
             after(t);
             __builtin_amdgcn_sched_barrier(0);
@@ -660,14 +664,12 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
     // while the compute unit's load path is busy (about 64 bytes a clock), so the loads go out one or
     // two at a time between groups of 4 products. Steps past the chunk load zeros, so the loop has
     // no tail cases.
-    constexpr int kHalf = kDwLoads / 2;
-    static_assert(kDwLoads == 10 && kHalf == 5, "the product groups below issue 5 loads per half step");
-    auto spread = [&](int stage, int step, int k0) __attribute__((always_inline)) {
-        // 5 loads over the 4 product groups: 2, 1, 1, 1
+    // a step's 5 loads go out in two parts, 3 (the first 3 product groups of one half step) and 2
+    constexpr int kHalf = 3;
+    static_assert(kDwLoads == 5, "the product groups below issue 3 + 2 loads per step");
+    auto spread = [&](int stage, int step, int k0, int nk) __attribute__((always_inline)) {
         return [=, &issue](int t) __attribute__((always_inline)) {
-            const int a = t == 0 ? 0 : t + 1, b = t + 2;
-#pragma unroll
-            for (int k = a; k < b; ++k) issue(stage, step, k0 + k);
+            if (t < nk) issue(stage, step, k0 + t);
         };
     };
 #pragma unroll
@@ -683,12 +685,12 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
     for (int s = 0; s < nsteps; ++s) {
         const int st = s % kDwStages;
         read_frags(1, st, 1);
-        products(0, spread((s + kDwStages - 1) % kDwStages, s + kDwStages - 1, kHalf));
+        products(0, spread((s + kDwStages - 1) % kDwStages, s + kDwStages - 1, kHalf, kDwLoads - kHalf));
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wait_vm<(kDwStages - 2) * kDwLoads, (kDwStages - 2) * kDwLoads>(0);
         __syncthreads();
         read_frags(0, (s + 1) % kDwStages, 0);
-        products(1, spread(st, s + kDwStages, 0));
+        products(1, spread(st, s + kDwStages, 0, kHalf));
     }
     wait_vm<0, 0>(0);
     __syncthreads();   // the stages are free for the output staging
@@ -699,8 +701,8 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
 #pragma unroll
         for (int t = 0; t < kWdwRows; ++t)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int c = it[kWdwCompactAt + 16 * t + 4 * wave + jj];
+            for (int jj = 0; jj < 2; ++jj) {
+                const int c = it[kWdwCompactAt + 16 * t + 2 * wave + jj];
                 if (c < 0) continue;
                 float *dst = o.partial + ((size_t)o.ch * o.P2 + (c - o.cbase)) * 1024 + l32 * 32 + 4 * lh;
 #pragma unroll
@@ -709,17 +711,18 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
             }
         return;
     }
-    // bf16: wave's 16 blocks staged as [slot][32 rows][64 + 16 bytes], then 16-byte stores
+    // bf16: wave's 8 blocks staged as [slot 2 t + jj][32 rows][64 + 16 bytes], then 16-byte stores
     constexpr int BP = 80;                          // staged block row pitch (bytes)
-    unsigned char *wst = smem + wave * 16 * 32 * BP;
+    static_assert(kDwWaves8 * 8 * 32 * BP <= kDwStages * kDwStage, "output staging fits in the stages");
+    unsigned char *wst = smem + wave * 8 * 32 * BP;
 #pragma unroll
     for (int t = 0; t < kWdwRows; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 v = quad(acc[t][jj], q4);
-                store4_bf16(reinterpret_cast<uint16_t *>(wst + (4 * t + jj) * 32 * BP + l32 * BP + (8 * q4 + 4 * lh) * 2),
+                store4_bf16(reinterpret_cast<uint16_t *>(wst + (2 * t + jj) * 32 * BP + l32 * BP + (8 * q4 + 4 * lh) * 2),
                             v[0], v[1], v[2], v[3]);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -727,9 +730,9 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
     // (each wave reads back only what it wrote: no barrier needed beyond the wave's own LDS ordering)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
         const int seg = i * 64 + lane, slot = seg >> 7, rowp = (seg >> 2) & 31, piece = seg & 3;
-        const int e = it[kWdwBlockAt + 16 * (slot >> 2) + 4 * wave + (slot & 3)];
+        const int e = it[kWdwBlockAt + 16 * (slot >> 1) + 2 * wave + (slot & 1)];
         if (e < 0) continue;
         const u32x4 val = *reinterpret_cast<const u32x4 *>(wst + slot * 32 * BP + rowp * BP + piece * 16);
         *reinterpret_cast<u32x4 *>(o.dV + (size_t)e * 1024 + rowp * 32 + piece * 8) = val;
@@ -740,7 +743,7 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
 // share of both kinds of work in its first round: XCD x runs, in order, its contiguous run of the
 // first n1 items (whole rows range each), then its contiguous run of the n2 x c2 (chunk, item) pairs
 // of the other items (items fastest). Work-groups past an XCD's share exit at once.
-__global__ __launch_bounds__(256, 1) void k_wide_dw(const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X,
+__global__ __launch_bounds__(512, 1) void k_wide_dw(const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X,
                                                     int K, int M, const int32_t *__restrict__ items, int n1, int n2,
                                                     int c2, int mchunk, int cbase, int P2,
                                                     float *__restrict__ partial, uint16_t *__restrict__ dV) {
@@ -896,7 +899,7 @@ int32_t launch_wide_dw(const bsr_pattern &p, const DwArgs &a, const WideDwPlan &
         most = (int)std::max<int64_t>(most, share);
     }
     if (most == 0) return BSR_OK;
-    hipLaunchKernelGGL(k_wide_dw, dim3((unsigned)(most * kXCDs)), dim3(256), 0, st, a.dY, p.N, a.X, p.K, (int)a.M,
+    hipLaunchKernelGGL(k_wide_dw, dim3((unsigned)(most * kXCDs)), dim3(kDwWaves8 * 64), 0, st, a.dY, p.N, a.X, p.K, (int)a.M,
                        p.dev.wdw_items, w.n1, w.n2, w.c2, w.mchunk, w.cbase, w.P2, partial, a.dV);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(BSR_ERR_HIP, std::string("wide weight-gradient launch: ") + hipGetErrorString(e));
