@@ -60,7 +60,7 @@ struct GroupSchedule {
 };
 
 // Wide-tile panel GEMM (b = 32; the matrix-core-bound regime of dense groups): a work-group owns
-// kWideG = 8 output blocks (256 output columns) and 256 activation rows, held by 4 waves as 4 x 4
+// kWideG = 8 output blocks (256 output columns) and 256 activation rows, held by 8 waves as 4 x 2
 // grids of 32 x 32 accumulators. One sub-step per 64-column panel in which any member keeps a
 // block; the value block of unit u (member u / 2, block u % 2 of the panel) is staged at slot u.
 // Record, kWideRecInts ints: [0] panel, [1] presence mask (bit u = unit u has a block),
