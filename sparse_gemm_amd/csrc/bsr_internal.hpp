@@ -4,6 +4,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <mutex>
 #include <vector>
 
 #include "bsr_linear.h"
@@ -98,22 +99,29 @@ struct DwSchedule {
     std::vector<int32_t> items;   // [n * kDwItemInts], by super-tiles of 8 x 4 tiles
 };
 
-// Wide weight-gradient items (b = 32): a tile of kWdwRows block rows (any rows) by kWdwCols block
-// columns (any columns), run by 4 waves that each hold 4 x 4 block accumulators; the products of
-// absent blocks are computed and dropped. Two kinds, in this order: dense items (4 rows whose 16
+// Wide weight-gradient items (b = 32). Tile items: kWdwRows block rows (any rows) by kWdwCols block
+// columns (any columns), run by 8 waves that each hold 4 x 2 block accumulators; the products of
+// absent blocks are computed and dropped. Three kinds, in this order: dense items (4 rows whose 16
 // consecutive columns are all kept, rows taken in order of decreasing kept-block count, so that
-// full rows share tiles), then gathered items that take every remaining block, a seed row (most
-// remaining blocks) with the 3 rows that share most of its columns, and the 16 columns most of the
-// 4 rows keep (see make_wide_dw). Item layout, kWdwItemInts ints: [t] block row t (t < 4; -1 =
-// unused), [4 + j] block column j (j < 16; -1 = unused), [kWdwBlockAt + 16 t + j] CSR index of block
-// (t, j) or -1, [kWdwCompactAt + 16 t + j] its compact index (blocks numbered in item order, row-
-// major inside an item) or -1.
+// full rows share tiles); gathered items (a seed row, most remaining blocks, with the 3 rows that
+// share most of its columns, and the 16 columns most of the 4 rows keep) that keep at least
+// kWdwThinBelow blocks; then thin items, the blocks of the sparser gathered tiles in order of
+// (column, row), kWdwThinBlocks at a time, one wave each (see make_wide_dw). Tile item layout,
+// kWdwItemInts ints: [t] block row t (t < 4; -1 = unused), [4 + j] block column j (j < 16; -1 =
+// unused), [kWdwKindAt] -1, [kWdwBlockAt + 16 t + j] CSR index of block (t, j) or -1,
+// [kWdwCompactAt + 16 t + j] its compact index (blocks numbered in item order, row-major inside an
+// item) or -1. Thin item: [kWdwKindAt] 1, block k (k < kWdwThinBlocks) in column [4 + k] and row
+// [12 + k], CSR index [kWdwBlockAt + k] (-1 = none), compact index [kWdwCompactAt + k]; every other
+// entry -1.
 constexpr int kWdwRows = 4;
 constexpr int kWdwCols = 16;
+constexpr int kWdwKindAt = 20;
 constexpr int kWdwBlockAt = 24;
 constexpr int kWdwCompactAt = 88;
 constexpr int kWdwItemInts = 152;
-constexpr int kWdwWindow = 32;   // candidate rows per gathered item (next by remaining count)
+constexpr int kWdwWindow = 32;      // candidate rows per gathered item (next by remaining count)
+constexpr int kWdwThinBlocks = 8;   // blocks of a thin item
+constexpr int kWdwThinBelow = 16;   // gathered tiles keeping fewer blocks become thin items
 struct WideDwSchedule {
     int n = 0;        // items
     int ndense = 0;   // the first ndense items are dense
@@ -170,6 +178,11 @@ struct bsr_pattern {
     // only, rebuilt there from a device mask; nnzb is the capacity (the most kept blocks it holds),
     // dw.n the capacity of weight-gradient items, and no host-side list is filled.
     bool device_built = false;
+    // The wide weight-gradient split of the last M planned (the plan depends on the pattern and M
+    // only; a call plans it twice, for the workspace size and for the launch).
+    mutable std::mutex wdw_plan_mu;
+    mutable int64_t wdw_plan_M = -1;
+    mutable bsr::WideDwPlan wdw_plan;
 };
 
 namespace bsr {

@@ -5,6 +5,7 @@
 // and the data. Blocks are canonical: ascending column inside a row, ascending row inside a
 // column. The transposed form is what the input-gradient kernel walks, so it needs no atomics.
 #include <algorithm>
+#include <array>
 #include <cstdlib>
 #include <string>
 #include <numeric>
@@ -271,7 +272,8 @@ DwSchedule make_dw_items(const bsr_pattern &p, const std::vector<char> &taken) {
 // most remaining blocks; with it go the 3 rows, among the next kWdwWindow by remaining count, that
 // share most of its remaining columns (ties: more remaining blocks, then the order of the count
 // list); the item takes the 16 columns that most of its rows keep (ties: lower column), in
-// ascending column order. Returns an empty schedule (every block left to the tile items) for b = 64
+// ascending column order; the blocks of gathered tiles that keep fewer than kWdwThinBelow go to thin
+// items instead. Returns an empty schedule (every block left to the tile items) for b = 64
 // and for patterns without a dense tile (measured: on BERT-base FFN-up and the square 10% layer the
 // tile items take 25 and 83 us, the gathered wide items 31 and 94 us).
 WideDwSchedule make_wide_dw(const bsr_pattern &p, std::vector<char> &taken) {
@@ -381,11 +383,40 @@ WideDwSchedule make_wide_dw(const bsr_pattern &p, std::vector<char> &taken) {
         taken.assign(p.nnzb, 0);
         return s;
     }
+    // gathered tiles keeping fewer than kWdwThinBelow blocks give them to thin items, by (column,
+    // row): a 4 x 16 tile computes 64 products and stages 20 segments per step for its few blocks,
+    // a thin item 1 product and 2 segments per block (Zipf layer: 52 of the 89 gathered tiles held
+    // only rows with one block, 4 useful products of 64)
+    std::vector<std::array<int32_t, 3>> pool;   // (column, row, CSR index)
+    std::vector<std::vector<int32_t>> kept, thin;
+    for (auto &it : gathered) {
+        int cnt = 0;
+        for (int k = 0; k < kWdwRows * kWdwCols; ++k) cnt += it[kWdwBlockAt + k] >= 0;
+        if (cnt >= kWdwThinBelow) {
+            kept.push_back(std::move(it));
+            continue;
+        }
+        for (int t = 0; t < kWdwRows; ++t)
+            for (int j = 0; j < kWdwCols; ++j)
+                if (it[kWdwBlockAt + 16 * t + j] >= 0) pool.push_back({it[4 + j], it[t], it[kWdwBlockAt + 16 * t + j]});
+    }
+    gathered = std::move(kept);
+    std::sort(pool.begin(), pool.end());
+    for (size_t f = 0; f < pool.size(); f += kWdwThinBlocks) {
+        std::vector<int32_t> it(kWdwItemInts, -1);
+        it[kWdwKindAt] = 1;
+        for (size_t k = 0; k < (size_t)kWdwThinBlocks && f + k < pool.size(); ++k) {
+            it[4 + k] = pool[f + k][0];
+            it[12 + k] = pool[f + k][1];
+            it[kWdwBlockAt + k] = pool[f + k][2];
+        }
+        thin.push_back(std::move(it));
+    }
     s.ndense = (int)dense.size();
-    s.n = (int)(dense.size() + gathered.size());
+    s.n = (int)(dense.size() + gathered.size() + thin.size());
     s.compact.assign(p.nnzb, -1);
     int32_t next = 0;
-    for (auto *list : {&dense, &gathered})
+    for (auto *list : {&dense, &gathered, &thin})
         for (auto &it : *list) {
             s.first.push_back(next);
             for (int k = 0; k < kWdwRows * kWdwCols; ++k)

@@ -739,6 +739,86 @@ __device__ __forceinline__ void wide_dw_tile(const uint16_t *__restrict__ dY, in
     }
 }
 
+// Thin weight-gradient item: up to 8 blocks anywhere, wave w computes block w over one chunk of
+// activation rows, dV[i][p][q] = sum_m dY[m][r*32 + p] * X[m][c*32 + q] (the block-masked SDDMM),
+// with no reuse between the blocks and no exchange between the waves (no barrier). Per 32-row step a
+// wave stages its block's dY segment and X segment (32 rows x 64 bytes each, 4 direct-to-LDS loads
+// of 16 rows: lane -> row lane / 4, 16-byte piece lane % 4) in its own 4 KB of a stage; 5 stages, so
+// that the loads of a step are issued 4 steps ahead (these blocks' segments mostly miss L2, and one
+// block's products do not cover a miss). Rows past the chunk read zeros, as in the tile items; the
+// wave drains its loads before it ends, so that none lands in the LDS of a later work-group.
+constexpr int kThinStages = 5;
+constexpr int kThinWaveBytes = 2 * kDwStep * 64;                 // dY and X segments of one step: 4 KB
+constexpr int kThinStage = kDwWaves8 * kThinWaveBytes;          // 32 KB
+static_assert(kWdwThinBlocks == kDwWaves8, "one wave per block of a thin item");
+static_assert(kThinStages * kThinStage <= kDwStages * kDwStage, "thin stages fit the tile items' LDS");
+
+__device__ __forceinline__ void wide_dw_thin(const uint16_t *__restrict__ dY, int N, const uint16_t *__restrict__ X,
+                                             int K, const int32_t *__restrict__ it, int m_begin, int rows,
+                                             const WdwOut &o, unsigned char *smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int e = it[kWdwBlockAt + wave];
+    if (e < 0) return;   // wave-uniform; the thin path has no barrier
+    const int r = it[12 + wave], c = it[4 + wave];
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dY + (size_t)m_begin * N, (uint32_t)((size_t)rows * N * 2));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)m_begin * K, (uint32_t)((size_t)rows * K * 2));
+    const uint32_t sbase = lds_addr(smem) + (uint32_t)wave * kThinWaveBytes;
+    unsigned char *const mine = smem + wave * kThinWaveBytes;
+    const int nsteps = (rows + kDwStep - 1) / kDwStep;
+    const uint32_t dlane = (uint32_t)(lane >> 2) * (uint32_t)N * 2u + (uint32_t)r * 64u + (uint32_t)(lane & 3) * 16u;
+    const uint32_t xlane = (uint32_t)(lane >> 2) * (uint32_t)K * 2u + (uint32_t)c * 64u + (uint32_t)(lane & 3) * 16u;
+    auto issue = [&](int st, int step) __attribute__((always_inline)) {
+        const uint32_t base = sbase + (uint32_t)st * kThinStage;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t row = (uint32_t)(step * kDwStep + 16 * h);
+            dma16(rd, base + (uint32_t)h * 1024u, dlane + row * (uint32_t)N * 2u, 0);
+            dma16(rx, base + 2048u + (uint32_t)h * 1024u, xlane + row * (uint32_t)K * 2u, 0);
+        }
+    };
+    // T[k0 + 8 (l / 32) .. + 7][l % 32] of a staged 32 x 64-byte segment for lane l: two transposing
+    // reads of 4 rows (lane s of a 16-lane group points at row R + s / 4, columns C .. C + 3)
+    auto frag = [&](const unsigned char *seg, int k0) __attribute__((always_inline)) {
+        const int gq = lane >> 4, s16 = lane & 15;
+        const int R = k0 + (gq >> 1) * 8 + (s16 >> 2);
+        const int C = (gq & 1) * 16 + 4 * (s16 & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(seg + R * 64 + C * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(seg + (R + 4) * 64 + C * 2));
+        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kThinStages - 1; ++q) issue(q, q);
+    for (int s = 0; s < nsteps; ++s) {
+        // into the stage of s - 1, once every LDS read of s - 1 has returned
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue((s + kThinStages - 1) % kThinStages, s + kThinStages - 1);
+        wait_vm<4 * (kThinStages - 1), 4 * (kThinStages - 1)>(0);   // this wave's loads of s have landed
+        const unsigned char *seg = mine + (s % kThinStages) * kThinStage;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) acc = mfma32(frag(seg + 2048, kc * 16), frag(seg, kc * 16), acc);
+    }
+    wait_vm<0, 0>(0);
+    // item v of lane l: D[q][p], q = 8 (v / 4) + 4 (l / 32) + v % 4 (block column), p = l % 32
+    if (o.partial) {
+        float *dst = o.partial + ((size_t)o.ch * o.P2 + (it[kWdwCompactAt + wave] - o.cbase)) * 1024 + l32 * 32 + 4 * lh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<f32x4 *>(dst + 8 * q4) = quad(acc, q4);
+    } else {
+        uint16_t *dst = o.dV + (size_t)e * 1024 + l32 * 32 + 4 * lh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = quad(acc, q4);
+            store4_bf16(dst + 8 * q4, v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
 // Work-groups go to the XCDs round robin (XCD = blockIdx % 8), so that each XCD gets an equal
 // share of both kinds of work in its first round: XCD x runs, in order, its contiguous run of the
 // first n1 items (whole rows range each), then its contiguous run of the n2 x c2 (chunk, item) pairs
@@ -766,7 +846,9 @@ __global__ __launch_bounds__(512, 1) void k_wide_dw(const uint16_t *__restrict__
         rows = min(M - m_begin, mchunk);
         if (c2 > 1) o.partial = partial;
     }
-    wide_dw_tile(dY, N, X, K, items + (size_t)item * kWdwItemInts, m_begin, rows, o, smem);
+    const int32_t *it = items + (size_t)item * kWdwItemInts;
+    if (it[kWdwKindAt] == 1) wide_dw_thin(dY, N, X, K, it, m_begin, rows, o, smem);
+    else wide_dw_tile(dY, N, X, K, it, m_begin, rows, o, smem);
 }
 
 // dV of the blocks of the split items: the fixed-order sum of their fp32 partials over the chunks.
@@ -805,39 +887,54 @@ bool use_wide(const bsr_pattern &p, bool transposed, int64_t M) {
 
 // Splits of the wide weight-gradient items for M activation rows. A model of one XCD (32 compute
 // units, one work-group each, work-groups placed in order on the unit that frees first) gives the
-// finishing time, in 32-row steps, of its share of the first n1 items (whole: ceil(M / 32) steps
-// each) and of the (chunk, item) pairs of the rest (mchunk / 32 steps each), plus a few steps per
-// work-group for its prologue and epilogue; the partials of split items cost their bytes (written
-// once, read once) at about 2 MB per step, plus a reduction launch. The candidates keep the dense
-// items whole, or split every item, into 1 .. 16 chunks of at least 256 rows; the cheapest wins
-// (ties: fewer chunks).
-WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M) {
+// finishing time, in 32-row steps of a dense item, of its share of the first n1 items (whole:
+// ceil(M / 32) steps each) and of the (chunk, item) pairs of the rest (mchunk / 32 steps each, items
+// fastest), plus a few steps per work-group for its prologue and epilogue. A step of a gathered item
+// costs 1.3 dense steps, one of a thin item 0.8 (Zipf layer, 4 chunks: 769 ns per dense step, 1179
+// per gathered, 628 per thin). Partials of split items: written during the products, read once by
+// the reduction (counted as 1.5 times their bytes at ~4 MB per step), plus its launch. The
+// candidates keep the dense items whole, or split every item, into 1 .. 16 chunks of at least 256
+// rows; the cheapest wins (ties: fewer chunks). The plan is cached per pattern for the last M.
+static WideDwPlan plan_wide_dw_model(const bsr_pattern &p, int64_t M) {
     const WideDwSchedule &s = p.wdw;
     WideDwPlan best;
     if (s.n == 0 || M <= 0) return best;
     constexpr int64_t kExtra = 6;   // prologue and epilogue of a work-group, in steps
     constexpr int kUnits = kCUs / kXCDs;
     const int64_t steps = (M + 31) / 32;
-    auto xcd_time = [&](int64_t a, int64_t la, int64_t b, int64_t lb) {
-        std::vector<std::pair<int64_t, int64_t>> free_at = {{0, kUnits}};   // (time, units)
-        auto place = [&](int64_t jobs, int64_t len) {
-            while (jobs > 0) {
-                size_t k = 0;
-                for (size_t q = 1; q < free_at.size(); ++q)
-                    if (free_at[q].first < free_at[k].first) k = q;
-                const int64_t t = free_at[k].first, c = free_at[k].second, use = std::min(jobs, c);
-                if (use == c) free_at.erase(free_at.begin() + (long)k);
-                else free_at[k].second -= use;
-                bool merged = false;
-                for (auto &f : free_at)
-                    if (f.first == t + len) f.second += use, merged = true;
-                if (!merged) free_at.push_back({t + len, use});
-                jobs -= use;
-            }
-        };
-        place(a, la);
-        place(b, lb);
-        int64_t last = 0;
+    // step cost of each item relative to a dense one
+    std::vector<double> cost(s.n, 1.0);
+    for (int k = s.ndense; k < s.n; ++k) cost[k] = s.items[(size_t)k * kWdwItemInts + kWdwKindAt] == 1 ? 0.8 : 1.3;
+    std::vector<std::pair<double, int64_t>> free_at;   // (time, units), at most kUnits entries
+    auto place = [&](int64_t jobs, double len) {      // on the units that free first, in order
+        while (jobs > 0) {
+            size_t k = 0;
+            for (size_t q = 1; q < free_at.size(); ++q)
+                if (free_at[q].first < free_at[k].first) k = q;
+            const double t = free_at[k].first;
+            const int64_t use = std::min(jobs, free_at[k].second);
+            if (use == free_at[k].second) free_at.erase(free_at.begin() + (long)k);
+            else free_at[k].second -= use;
+            bool merged = false;
+            for (auto &f : free_at)
+                if (f.first == t + len) f.second += use, merged = true;
+            if (!merged) free_at.push_back({t + len, use});
+            jobs -= use;
+        }
+    };
+    // the XCD's a whole items, then its (chunk, item) pairs b0 .. b0 + b - 1 (item n1 + pair % n2), in
+    // runs of equal cost
+    auto xcd_time = [&](int64_t a, int n1, int64_t b0, int64_t b, int n2, int64_t csteps) {
+        free_at.assign(1, {0.0, (int64_t)kUnits});
+        place(a, (double)(steps + kExtra));
+        for (int64_t g = b0; g < b0 + b;) {
+            const double c = cost[n1 + (int)(g % n2)];
+            int64_t e = g + 1;
+            while (e < b0 + b && cost[n1 + (int)(e % n2)] == c) ++e;
+            place(e - g, (double)csteps * c + (double)kExtra);
+            g = e;
+        }
+        double last = 0;
         for (auto &f : free_at) last = std::max(last, f.first);
         return last;
     };
@@ -851,15 +948,15 @@ WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M) {
             const int c2e = (int)((M + mchunk - 1) / mchunk);
             if (c2 > 1 && c2e != c2) continue;
             const int n2 = s.n - n1;
-            int64_t t = 0;
+            double t = 0;
             for (int x = 0; x < kXCDs; ++x) {
-                const int64_t a = (int64_t)n1 * (x + 1) / kXCDs - (int64_t)n1 * x / kXCDs;
+                const int64_t a0 = (int64_t)n1 * x / kXCDs, a = (int64_t)n1 * (x + 1) / kXCDs - a0;
                 const int64_t n2c = (int64_t)n2 * c2e;
-                const int64_t b = n2c * (x + 1) / kXCDs - n2c * x / kXCDs;
-                t = std::max(t, xcd_time(a, steps + kExtra, b, mchunk / 32 + kExtra));
+                const int64_t b0 = n2c * x / kXCDs, b = n2c * (x + 1) / kXCDs - b0;
+                t = std::max(t, xcd_time(a, n1, b0, b, n2 > 0 ? n2 : 1, mchunk / 32));
             }
             const int64_t P2 = s.first[s.n] - s.first[n1];
-            const double cost = (double)t + (c2e > 1 ? (double)P2 * c2e * 8192.0 / 2.0e6 + 8.0 : 0.0);
+            const double cost = (double)t + (c2e > 1 ? (double)P2 * c2e * 6144.0 / 4.0e6 + 8.0 : 0.0);
             if (!have || cost < best_cost) {
                 have = true;
                 best_cost = cost;
@@ -872,6 +969,23 @@ WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M) {
             }
             if (n2 == 0) break;
         }
+    }
+    return best;
+}
+
+WideDwPlan plan_wide_dw(const bsr_pattern &p, int64_t M) {
+    const WideDwSchedule &s = p.wdw;
+    WideDwPlan best;
+    bool cached = false;
+    {
+        std::lock_guard<std::mutex> lock(p.wdw_plan_mu);
+        if (p.wdw_plan_M == M) best = p.wdw_plan, cached = true;
+    }
+    if (!cached) {
+        best = plan_wide_dw_model(p, M);
+        std::lock_guard<std::mutex> lock(p.wdw_plan_mu);
+        p.wdw_plan_M = M;
+        p.wdw_plan = best;
     }
     if (const char *f = std::getenv("BSR_WDW_SPLIT")) {   // tuning knob: "n1,c2"
         int n1 = 0, c2 = 1;

@@ -191,9 +191,39 @@ static void check_pattern(const bsr_pattern &p) {
     }
     std::fill(hit.begin(), hit.end(), 0);
     int32_t next = 0;
+    bool seen_thin = false;
     for (int it = 0; it < p.wdw.n; ++it) {
         const int32_t *x = &p.wdw.items[(size_t)it * kWdwItemInts];
         REQUIRE(p.wdw.first[it] == next);
+        // thin items (after every tile item): block k in column [4 + k], row [12 + k]; nothing else set
+        REQUIRE(x[kWdwKindAt] == -1 || x[kWdwKindAt] == 1);
+        if (x[kWdwKindAt] == 1) {
+            seen_thin = true;
+            REQUIRE(it >= p.wdw.ndense);
+            int cnt = 0;
+            for (int k = 0; k < kWdwItemInts; ++k) {
+                const bool used = k == kWdwKindAt || (k >= 4 && k < 4 + kWdwThinBlocks) ||
+                                  (k >= 12 && k < 12 + kWdwThinBlocks) ||
+                                  (k >= kWdwBlockAt && k < kWdwBlockAt + kWdwThinBlocks) ||
+                                  (k >= kWdwCompactAt && k < kWdwCompactAt + kWdwThinBlocks);
+                if (!used) REQUIRE(x[k] == -1);
+            }
+            for (int k = 0; k < kWdwThinBlocks; ++k) {
+                const int32_t e = x[kWdwBlockAt + k], c = x[kWdwCompactAt + k], col = x[4 + k], r = x[12 + k];
+                REQUIRE((e >= 0) == (c >= 0) && (e >= 0) == (col >= 0) && (e >= 0) == (r >= 0));
+                if (e < 0) continue;
+                ++cnt;
+                REQUIRE(e < n && r < R && col < C);
+                if (e >= n || r >= R) continue;
+                hit[e]++;
+                REQUIRE(p.col_idx[e] == col && e >= p.row_ptr[r] && e < p.row_ptr[r + 1]);
+                REQUIRE(c == next && p.wdw.compact[c] == e);
+                ++next;
+            }
+            REQUIRE(cnt > 0);
+            continue;
+        }
+        REQUIRE(!seen_thin);
         for (int t = 0; t < kWdwRows; ++t) {
             REQUIRE(x[t] >= -1 && x[t] < R);
             for (int u = 0; u < t; ++u) REQUIRE(x[t] < 0 || x[t] != x[u]);
