@@ -867,8 +867,12 @@ __global__ __launch_bounds__(256) void k_wide_dw_reduce(const float *__restrict_
     store4_bf16(dV + (size_t)compact[cbase + c] * 1024 + v, s[0], s[1], s[2], s[3]);
 }
 
-int wide_tiles_per_chunk(int nmtiles) {
-    int t = 4;
+// Activation tiles per XCD chunk: 4 for the forward, 2 for the input gradient, whose 16 groups on
+// the Zipf layer (16384 x 4096 -> 11008) walk the same panels, so that a chunk's work-groups all run
+// together on one XCD (warm, two runs: 4 tiles 489 / 493 us, 2 tiles 482 / 479; forward 479 / 474
+// against 490 / 494).
+int wide_tiles_per_chunk(int nmtiles, bool transposed) {
+    int t = transposed ? 2 : 4;
     if (const char *f = std::getenv("BSR_WIDE_TPC")) t = std::atoi(f);   // tuning knob
     return std::max(1, std::min(t, nmtiles));
 }
@@ -1038,7 +1042,7 @@ int32_t launch_wide_gemm_24(const bsr_pattern &p, const FwdArgs &a, const uint16
     if ((int64_t)kWideRows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
     if (nwg == 0) return BSR_OK;
-    const int tpc = wide_tiles_per_chunk(nmtiles);
+    const int tpc = wide_tiles_per_chunk(nmtiles, false);
     const WideArgs24 wa{a.act, a.in_ld, (int)a.M, Vc, (uint32_t)((size_t)p.nnzb * 1024), meta,
                         (uint32_t)((size_t)p.nnzb * 128), a.bias, a.out, a.out_ld};
     hipLaunchKernelGGL(k_wide_gemm_24, dim3((unsigned)nwg), dim3(512), 0, st, wa, d.order, d.flags, d.sub_ptr, d.out,
@@ -1059,7 +1063,7 @@ int32_t launch_wide_gemm(const bsr_pattern &p, bool transposed, const FwdArgs &a
     if ((int64_t)kWideRows * a.in_ld * 2 + 256 > (int64_t)UINT32_MAX)
         return fail(BSR_ERR_INVALID_ARG, "activation rows too long for 32-bit buffer offsets");
     if (nwg == 0) return BSR_OK;
-    const int tpc = wide_tiles_per_chunk(nmtiles);
+    const int tpc = wide_tiles_per_chunk(nmtiles, transposed);
     const WideArgs wa{a.act, a.in_ld, (int)a.M, a.V, (uint32_t)((size_t)p.nnzb * 32 * 32 * 2), a.bias, a.out, a.out_ld};
     if (transposed)
         hipLaunchKernelGGL(k_wide_gemm<true>, dim3((unsigned)nwg), dim3(512), 0, st, wa, d.order, d.flags, d.sub_ptr,
