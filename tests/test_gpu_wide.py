@@ -107,7 +107,10 @@ def test_wide_is_deterministic(monkeypatch):
 
 
 # ---- the wide weight gradient (dense tiles of 4 full block rows x 16 consecutive block columns,
-# then gathered tiles of any 4 rows x any 16 columns taking every other block) ----
+# then gathered tiles of any 4 rows x any 16 columns taking every other block, whose sparser tiles
+# give their blocks to thin items of 8 single blocks, one wave each: every case below but the two
+# all-dense ones has thin items, some with fewer than 8 blocks, and M = 1000 splits them over row
+# chunks) ----
 
 @pytest.mark.parametrize("M,R,C,nfull,seed", [
     (300, 21, 40, 9, 7),      # 21 rows: 2 dense row groups, 8 leftover columns, gathered rows
