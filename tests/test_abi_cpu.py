@@ -220,6 +220,25 @@ def test_op_kernels_names_the_dispatch():
     assert L.bsr_op_kernels(None, 0, 1, buf, 4) == 1
 
 
+def test_weight_gradient_plan_follows_m():
+    """The wide weight-gradient split is cached per pattern for the last M planned: calls with
+    changing M on one pattern plan (workspace bytes, kernels) exactly as fresh patterns do."""
+    from sparse_gemm_amd import binding
+    w = synth.WORKLOADS[5]
+    mask = synth.block_mask(w, 0)
+    p = Pattern.from_mask(mask, w.N, w.K, w.b, upload=False)
+    seq = [w.M, 4096, w.M, 300, 4096, 1, w.M]
+    got = [(binding.bwd_weight_workspace_bytes(p, m), binding.op_kernels(p, "dw", m)) for m in seq]
+    for m, g in zip(seq, got):
+        q = Pattern.from_mask(mask, w.N, w.K, w.b, upload=False)
+        assert g == (binding.bwd_weight_workspace_bytes(q, m), binding.op_kernels(q, "dw", m)), m
+        q.close()
+    # the split depends on M: 16384 rows split the sparse items over row chunks (fp32 partials and a
+    # reduction), 4096 rows do not
+    assert got[0][1] == ["k_wide_dw", "k_wide_dw_reduce"] and got[1][1] == ["k_wide_dw"]
+    p.close()
+
+
 def test_device_pattern_argument_errors():
     """bsr_pattern_create_device rejects bad shapes and capacities before touching a GPU."""
     L = _lib.load()
